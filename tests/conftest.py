@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long CPU-side oracle runs")
+
+
+@pytest.fixture(scope="session")
+def weights():
+    from encoder_transformer_amd import synth
+    return synth.make_weights()
+
+
+@pytest.fixture(scope="session")
+def oracle_weights(weights):
+    from oracle import julia_oracle as jo
+    return jo.OracleWeights(weights)
