@@ -1,0 +1,180 @@
+"""Benchmark of the Julia-1 forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = jl_forward + jl_probs over one packed batch already resident in
+HBM (weights loaded, token ids on the device). The headline workload is the
+throughput case: 16 sequences of 1,024 tokens, question types cycling
+choice/score/noul, 2-20 options of 1-48 tokens, bf16. Extra fields report
+the batch-1 latency case (1 x 1,024), the long-context case (16 x 8,192) and
+the ragged serving mix (256 sequences of 64-2,048 tokens).
+
+`roofline` covers the kernel class with the most device time in the timed
+region, measured with HIP events bracketing each of its launches on the
+launch stream; `cpu_baseline` times the CPU oracle on two of the 1,024-token
+sequences. Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_FP32_TFLOPS = 157.3
+HBM_GBPS = 8000.0
+D, FFN_HEAD = 384, 1536
+
+
+def band_pairs(L, w=64):
+    p = np.arange(L)
+    return int(np.sum(np.minimum(L - 1, p + w) - np.maximum(0, p - w) + 1))
+
+
+def class_flops(batch):
+    """Algorithmic FLOPs per step of each kernel class (masked work not counted)."""
+    lens = np.diff(batch.seq_offsets).astype(np.int64)
+    T, M = int(lens.sum()), batch.n_markers
+    glob = int(np.sum(lens * lens))
+    band = sum(band_pairs(int(L)) for L in lens)
+    f = {
+        "qkv": 22 * 2 * T * D * 3 * D,
+        "outproj": 22 * 2 * T * D * D,
+        "mlp_in": 22 * 2 * T * D * 2304,
+        "mlp_out": 22 * 2 * T * 1152 * D,
+        "attn_global": 8 * 1536 * glob,
+        "attn_local": 14 * 1536 * band,
+        # head layer 1 on every token, layer 2 keys/values on every token and
+        # the rest on marker rows, attention of marker queries over their sequence
+        "head_gemm": 2 * T * D * (3 * D + D + 2 * FFN_HEAD) + 2 * T * D * 2 * D
+                     + 2 * M * D * (D + D + 2 * FFN_HEAD),
+        "head_attn": 1536 * glob + 1536 * int(sum(len(batch.sequence(b)[1]) * lens[b]
+                                                  for b in range(batch.n_seqs))),
+        "misc": 2 * M * D * D + 2 * M * D,
+    }
+    launches = {"qkv": 22, "outproj": 22, "mlp_in": 22, "mlp_out": 22, "attn_global": 8, "attn_local": 14}
+    return f, launches
+
+
+def time_workload(model, batch, steps, warmup, profile_class=None):
+    import torch
+    from encoder_transformer_amd import lib
+    ids = torch.from_numpy(np.ascontiguousarray(batch.ids)).to("cuda:0")
+    so, mp, qt = batch.seq_offsets, batch.mask_positions, batch.qtype
+    logits = torch.empty(batch.n_markers, dtype=torch.float32, device="cuda:0")
+
+    def step():
+        model.forward(ids, so, mp, qt, out=logits)
+        model.probs(logits, so, mp, qt)
+
+    # warm-up with every class timed, to find where the device time goes
+    model.profile(True, 0x3FF)
+    for _ in range(max(1, warmup)):
+        step()
+    torch.cuda.synchronize()
+    per_class = {lib.KERNEL_CLASS_NAMES[c]: model.profile_read(c) for c in range(10)}
+    dominant = max(per_class, key=lambda k: per_class[k][0]) if profile_class is None else profile_class
+    cls_id = lib.KERNEL_CLASS_NAMES.index(dominant)
+    model.profile(True, 1 << cls_id)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t = time.perf_counter() - t0
+    dom_ms, dom_n = model.profile_read(cls_id)
+    model.profile(False, 0)
+    return t, dominant, dom_ms, dom_n, per_class
+
+
+def cpu_baseline():
+    """The oracle on two 1,024-token sequences of the throughput batch."""
+    from threadpoolctl import threadpool_info
+    from encoder_transformer_amd import synth
+    from oracle import julia_oracle as jo
+    W = jo.OracleWeights(synth.make_weights())
+    batch = synth.make_batch(2)
+    seqs = [0, 1]
+    t0 = time.perf_counter()
+    jo.forward(W, batch, seqs)
+    t = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(len(seqs) / t, 4), "unit": "decisions/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"2 of the 16 x 1,024-token sequences (2,048 tokens), float64 NumPy, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the forward pass shards by "
+              "sequence with no cross-GPU traffic, and this build measures one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from encoder_transformer_amd import lib, synth
+    assert torch.cuda.is_available(), "no GPU visible"
+    path = synth.cached_weight_file()
+    model = lib.Model(path, lib.BF16, max_tokens=300_000, max_markers=4096, device=0)
+
+    b2 = synth.make_batch(2)
+    t, dom, dom_ms, dom_n, per_class = time_workload(model, b2, args.steps, args.warmup)
+    ms_step = 1e3 * t / args.steps
+    flops, launches = class_flops(b2)
+    total_flops = sum(flops.values())
+    dom_flops_step = flops[dom]
+    achieved = dom_flops_step * args.steps / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": dom, "launches": dom_n, "avg_launch_us": round(1e3 * dom_ms / max(1, dom_n), 2)}
+
+    result = {
+        "metric": "decisions/s + tokens/s at 16×1024 bf16 (MFMA % peak); ms/call at 1×1024",
+        "value": round(b2.n_seqs * args.steps / t, 2),
+        "unit": "decisions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "16 x 1,024-token questions (choice/score/noul cycling, 2-20 options of "
+                               "1-48 tokens), packed unpadded; random-init Julia-1 weights (std 0.02)",
+                   "global_batch": b2.n_seqs, "seq_len": 1024, "parallelism": "single GPU"},
+        "tokens_per_s": round(b2.n_tokens * args.steps / t, 1),
+        "step_tflops": round(total_flops / (ms_step * 1e-3) / 1e12, 2),
+        "step_mfma_frac": round(total_flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "device_ms_per_step_by_class": {k: round(v[0] / max(1, args.warmup), 4) for k, v in per_class.items()},
+        "roofline": roofline,
+    }
+    if not args.no_extra:
+        extra = {}
+        b1 = synth.make_batch(1)
+        t1, *_ = time_workload(model, b1, max(args.steps, 20), args.warmup)
+        extra["1x1024_ms_per_call"] = round(1e3 * t1 / max(args.steps, 20), 4)
+        for name, cfg, st in [("16x8192", 3, 5), ("ragged256", 4, 5)]:
+            b = synth.make_batch(cfg)
+            tt, d, dms, dn, _ = time_workload(model, b, st, 2)
+            fl = sum(class_flops(b)[0].values())
+            extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2),
+                           "tokens_per_s": round(b.n_tokens * st / tt, 1),
+                           "step_mfma_frac": round(fl / (tt / st) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "dominant_kernel": d}
+        result["extra"] = extra
+    result["ms_per_call_1x1024"] = result.get("extra", {}).get("1x1024_ms_per_call")
+    model.close()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,819 @@
+// Host side of libjl: weight loading, workspace, per-call planning and the C ABI.
+//
+// One call of jl_forward validates the packed batch on the host, uploads a few
+// KB of metadata (offsets, marker lists, attention work items) through a
+// pinned staging buffer, and enqueues about 120 kernels on the caller's
+// stream.  No allocation happens per call.
+#include "jl.h"
+#include "jl_internal.h"
+
+#include <fcntl.h>
+#include <sys/mman.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+using namespace jl;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg) {
+  g_err = msg;
+  return code;
+}
+
+#define JL_HIP(expr)                                                                      \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) return fail(JL_ERR_DEVICE, std::string(#expr ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+uint16_t f32_to_bf16(float f) {  // round to nearest even; NaN stays NaN
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct LayerW {
+  const float *attn_norm = nullptr;
+  const void *Wqkv = nullptr, *Wo = nullptr, *Wi = nullptr, *Wout = nullptr;
+  const float *mlp_norm = nullptr;
+};
+struct HeadW {
+  const void *in_w = nullptr, *out_w = nullptr, *l1_w = nullptr, *l2_w = nullptr;
+  const float *in_b = nullptr, *out_b = nullptr, *l1_b = nullptr, *l2_b = nullptr;
+  const float *n1_w = nullptr, *n1_b = nullptr, *n2_w = nullptr, *n2_b = nullptr;
+};
+
+struct ProfRec {
+  int cls;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct jl_model {
+  int device = 0;
+  int precision = JL_BF16;
+  bool bf16 = true;
+  size_t esize = 2;
+  int64_t max_tokens = 0, max_markers = 0, max_seqs = 0;
+
+  char *warena = nullptr;
+  size_t wbytes = 0;
+  char *ws = nullptr;
+  size_t wsbytes = 0;
+
+  // weights
+  const float *emb = nullptr, *emb_norm = nullptr, *final_norm = nullptr, *type_rows = nullptr;
+  LayerW L[kLayers];
+  HeadW H[2];
+  const float *sc_nw = nullptr, *sc_nb = nullptr, *sc_w1 = nullptr, *sc_b1 = nullptr, *sc_w2 = nullptr,
+              *sc_b2 = nullptr;
+  const float *rope_cos[2] = {nullptr, nullptr}, *rope_sin[2] = {nullptr, nullptr};  // [0] local, [1] global
+
+  // workspace
+  float *x = nullptr, *z = nullptr, *sh = nullptr;
+  char *qkv = nullptr, *o = nullptr, *act = nullptr, *qm = nullptr, *om = nullptr, *actm = nullptr;
+  int *pos = nullptr, *tok_seq = nullptr;
+  int *meta = nullptr;
+  size_t meta_ints = 0;
+  int *host_meta = nullptr;  // pinned staging
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+
+  // per-kernel timer
+  bool prof = false;
+  uint32_t prof_mask = 0;
+  std::vector<ProfRec> prof_rec;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+};
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// weight file
+// ---------------------------------------------------------------------------
+
+struct TensorEntry {
+  std::vector<uint32_t> shape;
+  uint64_t offset = 0, checksum = 0;
+};
+
+struct MappedFile {
+  void *base = MAP_FAILED;
+  size_t size = 0;
+  ~MappedFile() {
+    if (base != MAP_FAILED) munmap(base, size);
+  }
+};
+
+int parse_weight_file(const char *path, MappedFile &mf, std::map<std::string, TensorEntry> &tab) {
+  const int fd = open(path, O_RDONLY);
+  if (fd < 0) return fail(JL_ERR_FILE, std::string("cannot open weight file ") + path);
+  struct stat st;
+  if (fstat(fd, &st) != 0) {
+    close(fd);
+    return fail(JL_ERR_FILE, "cannot stat weight file");
+  }
+  mf.size = (size_t)st.st_size;
+  if (mf.size < 16) {
+    close(fd);
+    return fail(JL_ERR_FILE, "weight file truncated (no header)");
+  }
+  mf.base = mmap(nullptr, mf.size, PROT_READ, MAP_PRIVATE, fd, 0);
+  close(fd);
+  if (mf.base == MAP_FAILED) return fail(JL_ERR_FILE, "cannot map weight file");
+  const unsigned char *p = (const unsigned char *)mf.base;
+  if (std::memcmp(p, "JLW1", 4) != 0) return fail(JL_ERR_FILE, "bad weight-file magic");
+  uint32_t version, n, hdr;
+  std::memcpy(&version, p + 4, 4);
+  std::memcpy(&n, p + 8, 4);
+  std::memcpy(&hdr, p + 12, 4);
+  if (version != 1) return fail(JL_ERR_FILE, "unsupported weight-file version");
+  if (hdr > mf.size) return fail(JL_ERR_FILE, "weight file truncated (header)");
+  size_t off = 16;
+  for (uint32_t i = 0; i < n; ++i) {
+    if (off + 2 > hdr) return fail(JL_ERR_FILE, "corrupt weight-file header");
+    uint16_t nl;
+    std::memcpy(&nl, p + off, 2);
+    off += 2;
+    if (off + nl + 1 > hdr) return fail(JL_ERR_FILE, "corrupt weight-file header");
+    std::string name((const char *)p + off, nl);
+    off += nl;
+    const uint8_t nd = p[off++];
+    if (nd > 4 || off + 4 * nd + 16 > hdr) return fail(JL_ERR_FILE, "corrupt weight-file header");
+    TensorEntry e;
+    uint64_t count = 1;
+    for (int d = 0; d < nd; ++d) {
+      uint32_t v;
+      std::memcpy(&v, p + off, 4);
+      off += 4;
+      e.shape.push_back(v);
+      count *= v;
+    }
+    std::memcpy(&e.offset, p + off, 8);
+    std::memcpy(&e.checksum, p + off + 8, 8);
+    off += 16;
+    if (e.offset % 4 != 0 || e.offset + count * 4 > mf.size)
+      return fail(JL_ERR_FILE, "weight file truncated (tensor " + name + ")");
+    tab[name] = e;
+  }
+  return JL_OK;
+}
+
+uint64_t checksum_words(const uint32_t *w, size_t n) {
+  uint64_t s = 0;
+  for (size_t i = 0; i < n; ++i) s += w[i];
+  return s;
+}
+
+// Host staging of the converted weights (everything but the embedding table).
+struct Arena {
+  std::vector<char> buf;
+  size_t add(size_t bytes) {
+    const size_t off = (buf.size() + 255) & ~size_t(255);
+    buf.resize(off + bytes);
+    return off;
+  }
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" const char *jl_last_error(void) { return g_err.c_str(); }
+
+extern "C" int jl_validate(const int32_t *seq_offsets, int32_t n_seqs, const int32_t *mask_positions,
+                           int32_t n_markers, const int32_t *qtype, int64_t max_tokens,
+                           int64_t max_markers) {
+  if (n_seqs < 0 || n_markers < 0) return fail(JL_ERR_ARG, "negative sequence or marker count");
+  if (!seq_offsets) return fail(JL_ERR_ARG, "seq_offsets is NULL");
+  if (n_seqs > 0 && !qtype) return fail(JL_ERR_ARG, "qtype is NULL");
+  if (n_markers > 0 && !mask_positions) return fail(JL_ERR_ARG, "mask_positions is NULL");
+  if (seq_offsets[0] != 0) return fail(JL_ERR_LENGTH, "seq_offsets[0] must be 0");
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t len = (int64_t)seq_offsets[b + 1] - seq_offsets[b];
+    if (len < 1 || len > JL_MAX_SEQ_LEN)
+      return fail(JL_ERR_LENGTH, "sequence " + std::to_string(b) + " has length " + std::to_string(len) +
+                                     " (must be 1.." + std::to_string(JL_MAX_SEQ_LEN) + ")");
+    if (qtype[b] < 0 || qtype[b] > 2)
+      return fail(JL_ERR_QTYPE, "sequence " + std::to_string(b) + " has question type " + std::to_string(qtype[b]));
+  }
+  const int64_t T = seq_offsets[n_seqs];
+  if (T > max_tokens)
+    return fail(JL_ERR_CAPACITY, std::to_string(T) + " tokens exceed the handle's " + std::to_string(max_tokens));
+  if (n_markers > max_markers)
+    return fail(JL_ERR_CAPACITY,
+                std::to_string(n_markers) + " markers exceed the handle's " + std::to_string(max_markers));
+  for (int32_t k = 0; k < n_markers; ++k) {
+    if (mask_positions[k] < 0 || mask_positions[k] >= T)
+      return fail(JL_ERR_OPTIONS, "marker " + std::to_string(k) + " lies outside every sequence");
+    if (k > 0 && mask_positions[k] <= mask_positions[k - 1])
+      return fail(JL_ERR_OPTIONS, "marker positions must be strictly increasing");
+  }
+  int32_t k = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    int32_t c = 0;
+    while (k < n_markers && mask_positions[k] < seq_offsets[b + 1]) {
+      ++k;
+      ++c;
+    }
+    if (c < JL_MIN_OPTIONS || c > JL_MAX_OPTIONS)
+      return fail(JL_ERR_OPTIONS, "sequence " + std::to_string(b) + " has " + std::to_string(c) +
+                                      " options (must be 2..20)");
+    if (qtype[b] == JL_NOUL && c != 2)
+      return fail(JL_ERR_OPTIONS, "noul sequence " + std::to_string(b) + " must have exactly 2 options");
+  }
+  return JL_OK;
+}
+
+extern "C" void jl_free(jl_model *m) {
+  if (!m) return;
+  DeviceGuard dg(m->device);
+  if (m->upload_done) {
+    (void)hipEventSynchronize(m->upload_done);
+    (void)hipEventDestroy(m->upload_done);
+  }
+  for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
+  if (m->host_meta) (void)hipHostFree(m->host_meta);
+  if (m->ws) (void)hipFree(m->ws);
+  if (m->warena) (void)hipFree(m->warena);
+  delete m;
+}
+
+extern "C" int jl_load_weights(const char *path, int precision, int64_t max_tokens, int64_t max_markers,
+                               int device, jl_model **out) {
+  if (!path || !out) return fail(JL_ERR_ARG, "path and out must not be NULL");
+  *out = nullptr;
+  if (precision != JL_FP32 && precision != JL_BF16) return fail(JL_ERR_ARG, "precision must be JL_FP32 or JL_BF16");
+  if (max_tokens < 1 || max_tokens > (int64_t)1 << 26) return fail(JL_ERR_ARG, "max_tokens must be in 1..2^26");
+  if (max_markers < 2 || max_markers > max_tokens) return fail(JL_ERR_ARG, "max_markers must be in 2..max_tokens");
+  if (device < 0) return fail(JL_ERR_ARG, "device must be >= 0");
+
+  // Parse, verify and convert on the host first: file errors never need a GPU.
+  MappedFile mf;
+  std::map<std::string, TensorEntry> tab;
+  if (int rc = parse_weight_file(path, mf, tab)) return rc;
+
+  const bool bf = precision == JL_BF16;
+  const size_t es = bf ? 2 : 4;
+  const char *base = (const char *)mf.base;
+  auto get = [&](const std::string &name, std::vector<uint32_t> shape, const float **data) -> int {
+    auto it = tab.find(name);
+    if (it == tab.end()) return fail(JL_ERR_FILE, "weight file lacks tensor " + name);
+    if (it->second.shape != shape) return fail(JL_ERR_FILE, "tensor " + name + " has the wrong shape");
+    size_t n = 1;
+    for (uint32_t d : shape) n *= d;
+    const uint32_t *w = (const uint32_t *)(base + it->second.offset);
+    if (checksum_words(w, n) != it->second.checksum) return fail(JL_ERR_FILE, "checksum mismatch in tensor " + name);
+    *data = (const float *)w;
+    return JL_OK;
+  };
+
+  Arena ar;
+  // Offsets are resolved to device pointers after the upload.
+  struct Pending {
+    const void **dst;
+    size_t off;
+  };
+  std::vector<Pending> pend;
+  auto put_f32 = [&](const float *src, size_t n, const float **dst) {
+    const size_t off = ar.add(n * 4);
+    std::memcpy(ar.buf.data() + off, src, n * 4);
+    pend.push_back({(const void **)dst, off});
+  };
+  // element matrix [rows, cols]; `row_of` maps destination row -> source row
+  auto put_elem = [&](const float *src, size_t rows, size_t cols, const void **dst, const std::vector<int> *row_of) {
+    const size_t off = ar.add(rows * cols * es);
+    char *d = ar.buf.data() + off;
+    for (size_t r = 0; r < rows; ++r) {
+      const float *s = src + (size_t)(row_of ? (*row_of)[r] : (int)r) * cols;
+      if (bf) {
+        uint16_t *o = (uint16_t *)d + r * cols;
+        for (size_t c = 0; c < cols; ++c) o[c] = f32_to_bf16(s[c]);
+      } else {
+        std::memcpy((float *)d + r * cols, s, cols * 4);
+      }
+    }
+    pend.push_back({dst, off});
+  };
+
+  jl_model *m = new jl_model();
+  m->device = device;
+  m->precision = precision;
+  m->bf16 = bf;
+  m->esize = es;
+  m->max_tokens = max_tokens;
+  m->max_markers = max_markers;
+  m->max_seqs = std::min<int64_t>(max_tokens, max_markers / 2);
+
+  const uint32_t D = kWidth;
+  const float *t = nullptr;
+  int rc = JL_OK;
+#define GET(name, ...)                                   \
+  if ((rc = get(name, {__VA_ARGS__}, &t)) != JL_OK) {    \
+    delete m;                                            \
+    return rc;                                           \
+  }
+  const float *emb_host = nullptr;
+  GET("embeddings.tok_embeddings.weight", (uint32_t)kVocab, D);
+  emb_host = t;
+  GET("embeddings.norm.weight", D);
+  put_f32(t, D, &m->emb_norm);
+  // GEGLU rows interleaved by 16: [a0..a15, g0..g15, a16..a31, g16..g31, ...]
+  std::vector<int> geglu_rows(2 * kGeglu);
+  for (int o = 0; o < kGeglu; ++o) {
+    geglu_rows[32 * (o / 16) + (o % 16)] = o;
+    geglu_rows[32 * (o / 16) + 16 + (o % 16)] = kGeglu + o;
+  }
+  for (int l = 0; l < kLayers; ++l) {
+    const std::string p = "layers." + std::to_string(l) + ".";
+    if (l != 0) {
+      GET(p + "attn_norm.weight", D);
+      put_f32(t, D, &m->L[l].attn_norm);
+    }
+    GET(p + "attn.Wqkv.weight", 3 * D, D);
+    put_elem(t, 3 * D, D, &m->L[l].Wqkv, nullptr);
+    GET(p + "attn.Wo.weight", D, D);
+    put_elem(t, D, D, &m->L[l].Wo, nullptr);
+    GET(p + "mlp_norm.weight", D);
+    put_f32(t, D, &m->L[l].mlp_norm);
+    GET(p + "mlp.Wi.weight", 2 * kGeglu, D);
+    put_elem(t, 2 * kGeglu, D, &m->L[l].Wi, &geglu_rows);
+    GET(p + "mlp.Wo.weight", D, kGeglu);
+    put_elem(t, D, kGeglu, &m->L[l].Wout, nullptr);
+  }
+  GET("final_norm.weight", D);
+  put_f32(t, D, &m->final_norm);
+  GET("head.type_embedding.weight", 3, D);
+  put_f32(t, 3 * D, &m->type_rows);
+  for (int j = 0; j < 2; ++j) {
+    const std::string p = "head.layers." + std::to_string(j) + ".";
+    HeadW &h = m->H[j];
+    GET(p + "self_attn.in_proj_weight", 3 * D, D);
+    put_elem(t, 3 * D, D, &h.in_w, nullptr);
+    GET(p + "self_attn.in_proj_bias", 3 * D);
+    put_f32(t, 3 * D, &h.in_b);
+    GET(p + "self_attn.out_proj.weight", D, D);
+    put_elem(t, D, D, &h.out_w, nullptr);
+    GET(p + "self_attn.out_proj.bias", D);
+    put_f32(t, D, &h.out_b);
+    GET(p + "linear1.weight", (uint32_t)kHeadFfn, D);
+    put_elem(t, kHeadFfn, D, &h.l1_w, nullptr);
+    GET(p + "linear1.bias", (uint32_t)kHeadFfn);
+    put_f32(t, kHeadFfn, &h.l1_b);
+    GET(p + "linear2.weight", D, (uint32_t)kHeadFfn);
+    put_elem(t, D, kHeadFfn, &h.l2_w, nullptr);
+    GET(p + "linear2.bias", D);
+    put_f32(t, D, &h.l2_b);
+    GET(p + "norm1.weight", D);
+    put_f32(t, D, &h.n1_w);
+    GET(p + "norm1.bias", D);
+    put_f32(t, D, &h.n1_b);
+    GET(p + "norm2.weight", D);
+    put_f32(t, D, &h.n2_w);
+    GET(p + "norm2.bias", D);
+    put_f32(t, D, &h.n2_b);
+  }
+  GET("head.scorer.norm.weight", D);
+  put_f32(t, D, &m->sc_nw);
+  GET("head.scorer.norm.bias", D);
+  put_f32(t, D, &m->sc_nb);
+  GET("head.scorer.fc1.weight", D, D);
+  put_f32(t, (size_t)D * D, &m->sc_w1);
+  GET("head.scorer.fc1.bias", D);
+  put_f32(t, D, &m->sc_b1);
+  GET("head.scorer.fc2.weight", 1, D);
+  put_f32(t, D, &m->sc_w2);
+  GET("head.scorer.fc2.bias", 1);
+  put_f32(t, 1, &m->sc_b2);
+#undef GET
+  // RoPE tables: angle p * theta^(-2j/64) in double, cos/sin rounded to FP32
+  for (int gl = 0; gl < 2; ++gl) {
+    const double theta = gl ? kThetaGlobal : kThetaLocal;
+    std::vector<float> c((size_t)kMaxSeq * 32), s((size_t)kMaxSeq * 32);
+    for (int j = 0; j < 32; ++j) {
+      const double omega = std::pow(theta, -2.0 * j / kHeadDim);
+      for (int p = 0; p < kMaxSeq; ++p) {
+        const double a = (double)p * omega;
+        c[(size_t)p * 32 + j] = (float)std::cos(a);
+        s[(size_t)p * 32 + j] = (float)std::sin(a);
+      }
+    }
+    put_f32(c.data(), c.size(), &m->rope_cos[gl]);
+    put_f32(s.data(), s.size(), &m->rope_sin[gl]);
+  }
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device >= ndev) {
+    delete m;
+    return fail(JL_ERR_DEVICE, "no HIP device " + std::to_string(device));
+  }
+  DeviceGuard dg(device);
+  const size_t emb_bytes = (size_t)kVocab * D * 4;
+  const size_t rest = (ar.buf.size() + 255) & ~size_t(255);
+  m->wbytes = emb_bytes + rest;
+  if (hipMalloc((void **)&m->warena, m->wbytes) != hipSuccess) {
+    delete m;
+    return fail(JL_ERR_OOM, "cannot allocate device memory for the weights");
+  }
+  auto bail = [&](int code, const std::string &msg) {
+    jl_free(m);
+    return fail(code, msg);
+  };
+  if (hipMemcpy(m->warena, emb_host, emb_bytes, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(m->warena + emb_bytes, ar.buf.data(), ar.buf.size(), hipMemcpyHostToDevice) != hipSuccess)
+    return bail(JL_ERR_DEVICE, "weight upload failed");
+  m->emb = (const float *)m->warena;
+  for (const Pending &pd : pend) *pd.dst = m->warena + emb_bytes + pd.off;
+
+  // workspace
+  const size_t T = (size_t)max_tokens, Mm = (size_t)max_markers, Bm = (size_t)m->max_seqs;
+  m->meta_ints = 2 * (Bm + 1) + Bm + Mm + 8 * (T / 64 + Bm + 1) + 8 * Bm + 64;
+  size_t off = 0;
+  std::vector<std::pair<void **, size_t>> slots;
+  auto reserve = [&](void **holder, size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    slots.push_back({holder, off});
+    off += bytes;
+  };
+  reserve((void **)&m->x, T * D * 4);
+  reserve((void **)&m->qkv, T * 3 * D * es);
+  reserve((void **)&m->o, T * D * es);
+  reserve((void **)&m->act, T * kHeadFfn * es);
+  reserve((void **)&m->pos, T * 4);
+  reserve((void **)&m->tok_seq, T * 4);
+  reserve((void **)&m->z, Mm * D * 4);
+  reserve((void **)&m->qm, Mm * D * es);
+  reserve((void **)&m->om, Mm * D * es);
+  reserve((void **)&m->actm, Mm * kHeadFfn * es);
+  reserve((void **)&m->sh, Mm * D * 4);
+  reserve((void **)&m->meta, m->meta_ints * 4);
+  m->wsbytes = (off + 255) & ~size_t(255);
+  if (hipMalloc((void **)&m->ws, m->wsbytes) != hipSuccess)
+    return bail(JL_ERR_OOM, "cannot allocate the device workspace");
+  for (auto &sl : slots) *sl.first = m->ws + sl.second;
+  if (hipHostMalloc((void **)&m->host_meta, m->meta_ints * 4, hipHostMallocDefault) != hipSuccess)
+    return bail(JL_ERR_OOM, "cannot allocate pinned staging memory");
+  if (hipEventCreateWithFlags(&m->upload_done, hipEventDisableTiming) != hipSuccess)
+    return bail(JL_ERR_DEVICE, "cannot create an event");
+  *out = m;
+  return JL_OK;
+}
+
+extern "C" int jl_model_info(const jl_model *m, int64_t *info, int n) {
+  if (!m || !info) return fail(JL_ERR_ARG, "NULL argument");
+  const int64_t v[6] = {m->precision, m->max_tokens, m->max_markers, m->device, (int64_t)m->wbytes,
+                        (int64_t)m->wsbytes};
+  for (int i = 0; i < n && i < 6; ++i) info[i] = v[i];
+  return JL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// per-call planning and launch sequence
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct Plan {
+  int B = 0, M = 0, T = 0;
+  int n_work = 0;
+  const int *d_so = nullptr, *d_mo = nullptr, *d_qt = nullptr, *d_mp = nullptr;
+  const AttnWork *d_aw = nullptr, *d_mw = nullptr;
+};
+
+// Build the metadata in pinned memory and enqueue its upload.
+int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, int32_t M, const int32_t *qt,
+                hipStream_t s, Plan &pl) {
+  pl.B = B;
+  pl.M = M;
+  pl.T = so[B];
+  if (m->upload_pending) {
+    JL_HIP(hipEventSynchronize(m->upload_done));
+    m->upload_pending = false;
+  }
+  int *h = m->host_meta;
+  size_t o = 0;
+  const size_t o_so = o;
+  for (int b = 0; b <= B; ++b) h[o++] = so[b];
+  const size_t o_mo = o;
+  {
+    int k = 0;
+    for (int b = 0; b <= B; ++b) {
+      while (k < M && mp[k] < so[b]) ++k;
+      h[o++] = k;
+    }
+  }
+  const size_t o_qt = o;
+  for (int b = 0; b < B; ++b) h[o++] = qt[b];
+  const size_t o_mp = o;
+  for (int k = 0; k < M; ++k) h[o++] = mp[k];
+  o = (o + 7) & ~size_t(7);
+  // encoder / head-layer-1 work items, longest sequences first
+  std::vector<int> order(B);
+  for (int b = 0; b < B; ++b) order[b] = b;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return so[a + 1] - so[a] > so[b + 1] - so[b]; });
+  const size_t o_aw = o;
+  int nw = 0;
+  for (int b : order) {
+    const int start = so[b], len = so[b + 1] - so[b];
+    for (int q0 = 0; q0 < len; q0 += 64) {
+      AttnWork w{start + q0, std::min(64, len - q0), start, len, q0, 0, 0, 0};
+      std::memcpy(h + o, &w, sizeof(w));
+      o += 8;
+      ++nw;
+    }
+  }
+  const size_t o_mw = o;
+  for (int b = 0; b < B; ++b) {
+    const int first = h[o_mo + b], cnt = h[o_mo + b + 1] - first;
+    AttnWork w{first, cnt, so[b], so[b + 1] - so[b], 0, 0, 0, 0};
+    std::memcpy(h + o, &w, sizeof(w));
+    o += 8;
+  }
+  if (o > m->meta_ints) return fail(JL_ERR_CAPACITY, "batch metadata exceeds the staging buffer");
+  JL_HIP(hipMemcpyAsync(m->meta, h, o * 4, hipMemcpyHostToDevice, s));
+  JL_HIP(hipEventRecord(m->upload_done, s));
+  m->upload_pending = true;
+  pl.n_work = nw;
+  pl.d_so = m->meta + o_so;
+  pl.d_mo = m->meta + o_mo;
+  pl.d_qt = m->meta + o_qt;
+  pl.d_mp = m->meta + o_mp;
+  pl.d_aw = (const AttnWork *)(m->meta + o_aw);
+  pl.d_mw = (const AttnWork *)(m->meta + o_mw);
+  return JL_OK;
+}
+
+hipEvent_t prof_event(jl_model *m) {
+  if (m->ev_used == m->ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    m->ev_pool.push_back(e);
+  }
+  return m->ev_pool[m->ev_used++];
+}
+
+struct Launch {
+  jl_model *m;
+  hipStream_t s;
+  int cls;
+  hipEvent_t a = nullptr;
+  Launch(jl_model *m_, hipStream_t s_, int c) : m(m_), s(s_), cls(c) {
+    if (m->prof && (m->prof_mask >> c & 1u)) {
+      a = prof_event(m);
+      if (a) (void)hipEventRecord(a, s);
+    }
+  }
+  void done() {
+    if (a) {
+      hipEvent_t b = prof_event(m);
+      if (b) {
+        (void)hipEventRecord(b, s);
+        m->prof_rec.push_back({cls, a, b});
+      }
+    }
+  }
+};
+
+#define JL_LAUNCH(cls, call)                                                          \
+  do {                                                                                \
+    Launch L_(m, s, cls);                                                             \
+    hipError_t e_ = (call);                                                           \
+    L_.done();                                                                        \
+    if (e_ != hipSuccess) return fail(JL_ERR_DEVICE, std::string("kernel launch failed: ") + hipGetErrorString(e_)); \
+  } while (0)
+
+GemmArgs gemm(const void *A, int lda, const float *g, const float *b, const void *W, int ldw, const float *bias,
+              void *C, int ldc, int M, int N, int K) {
+  GemmArgs a{};
+  a.A = A;
+  a.lda = lda;
+  a.ln_g = g;
+  a.ln_b = b;
+  a.W = W;
+  a.ldw = ldw;
+  a.bias = bias;
+  a.C = C;
+  a.ldc = ldc;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return a;
+}
+
+// Enqueue the forward pass up to `stop` (see jl_debug_hidden; 26 = logits).
+int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float *out, hipStream_t s) {
+  const bool bf = m->bf16;
+  const size_t es = m->esize;
+  const int T = pl.T, M = pl.M, D = kWidth;
+  auto copy_out = [&](const float *src, size_t rows) -> int {
+    JL_HIP(hipMemcpyAsync(out, src, rows * D * 4, hipMemcpyDeviceToDevice, s));
+    return JL_OK;
+  };
+  JL_LAUNCH(JL_K_EMBED, launch_embed(ids, m->emb, m->emb_norm, T, pl.d_so, pl.B, m->x, m->pos, m->tok_seq, s));
+  if (stop == 0) return copy_out(m->x, T);
+
+  AttnArgs at{};
+  at.q = m->qkv;
+  at.q_stride = 3 * D;
+  at.k = m->qkv + D * es;
+  at.v = m->qkv + 2 * D * es;
+  at.kv_stride = 3 * D;
+  at.o = m->o;
+  at.o_stride = D;
+  at.work = pl.d_aw;
+  for (int l = 0; l < kLayers; ++l) {
+    const LayerW &W = m->L[l];
+    const bool glob = layer_is_global(l);
+    GemmArgs q = gemm(m->x, D, W.attn_norm, nullptr, W.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D);
+    q.rope_cos = m->rope_cos[glob];
+    q.rope_sin = m->rope_sin[glob];
+    q.pos = m->pos;
+    q.rope_cols = 2 * D;
+    JL_LAUNCH(JL_K_QKV, launch_gemm(bf, A_LN, E_STORE, q, s));
+    at.half_window = glob ? -1 : kHalfWindow;
+    JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, launch_attention(bf, at, pl.n_work, s));
+    JL_LAUNCH(JL_K_OUTPROJ,
+              launch_gemm(bf, A_ACT, E_RESID, gemm(m->o, D, nullptr, nullptr, W.Wo, D, nullptr, m->x, D, T, D, D), s));
+    JL_LAUNCH(JL_K_MLP_IN, launch_gemm(bf, A_LN, E_GEGLU,
+                                       gemm(m->x, D, W.mlp_norm, nullptr, W.Wi, D, nullptr, m->act, kGeglu, T,
+                                            2 * kGeglu, D),
+                                       s));
+    JL_LAUNCH(JL_K_MLP_OUT, launch_gemm(bf, A_ACT, E_RESID,
+                                        gemm(m->act, kGeglu, nullptr, nullptr, W.Wout, kGeglu, nullptr, m->x, D, T,
+                                             D, kGeglu),
+                                        s));
+    if (stop == l + 1) return copy_out(m->x, T);
+  }
+  // head input: final LayerNorm + type row (in place)
+  JL_LAUNCH(JL_K_MISC, launch_final_ln_type(m->x, m->final_norm, m->type_rows, pl.d_qt, m->tok_seq, T, m->x, s));
+  if (stop == 23) return copy_out(m->x, T);
+
+  // head layer 1 over every token
+  {
+    const HeadW &H = m->H[0];
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_STORE,
+                                          gemm(m->x, D, H.n1_w, H.n1_b, H.in_w, D, H.in_b, m->qkv, 3 * D, T, 3 * D, D),
+                                          s));
+    at.half_window = -1;
+    JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, at, pl.n_work, s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_ACT, E_RESID,
+                                          gemm(m->o, D, nullptr, nullptr, H.out_w, D, H.out_b, m->x, D, T, D, D), s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_RELU,
+                                          gemm(m->x, D, H.n2_w, H.n2_b, H.l1_w, D, H.l1_b, m->act, kHeadFfn, T,
+                                               kHeadFfn, D),
+                                          s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_ACT, E_RESID,
+                                          gemm(m->act, kHeadFfn, nullptr, nullptr, H.l2_w, kHeadFfn, H.l2_b, m->x, D,
+                                               T, D, kHeadFfn),
+                                          s));
+  }
+  if (stop == 24) return copy_out(m->x, T);
+
+  // head layer 2: keys and values for every token, the rest at marker rows only
+  {
+    const HeadW &H = m->H[1];
+    char *kv = m->qkv;  // [T, 768]: k then v
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_STORE,
+                                          gemm(m->x, D, H.n1_w, H.n1_b, (const char *)H.in_w + (size_t)D * D * es, D,
+                                               H.in_b + D, kv, 2 * D, T, 2 * D, D),
+                                          s));
+    JL_LAUNCH(JL_K_MISC, launch_gather_rows(m->x, pl.d_mp, M, m->z, s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_STORE,
+                                          gemm(m->z, D, H.n1_w, H.n1_b, H.in_w, D, H.in_b, m->qm, D, M, D, D), s));
+    AttnArgs mk{};
+    mk.q = m->qm;
+    mk.q_stride = D;
+    mk.k = kv;
+    mk.v = kv + D * es;
+    mk.kv_stride = 2 * D;
+    mk.o = m->om;
+    mk.o_stride = D;
+    mk.work = pl.d_mw;
+    mk.half_window = -1;
+    JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, mk, pl.B, s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_ACT, E_RESID,
+                                          gemm(m->om, D, nullptr, nullptr, H.out_w, D, H.out_b, m->z, D, M, D, D), s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_RELU,
+                                          gemm(m->z, D, H.n2_w, H.n2_b, H.l1_w, D, H.l1_b, m->actm, kHeadFfn, M,
+                                               kHeadFfn, D),
+                                          s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_ACT, E_RESID,
+                                          gemm(m->actm, kHeadFfn, nullptr, nullptr, H.l2_w, kHeadFfn, H.l2_b, m->z, D,
+                                               M, D, kHeadFfn),
+                                          s));
+  }
+  if (stop == 25) return copy_out(m->z, M);
+
+  // scorer (FP32 in both modes)
+  JL_LAUNCH(JL_K_MISC, launch_gemm(bf, A_LN, E_GELU_F32,
+                                   gemm(m->z, D, m->sc_nw, m->sc_nb, m->sc_w1, D, m->sc_b1, m->sh, D, M, D, D), s));
+  JL_LAUNCH(JL_K_MISC, launch_score_dot(m->sh, m->sc_w2, m->sc_b2, M, out, s));
+  return JL_OK;
+}
+
+}  // namespace
+
+extern "C" int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
+                          const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, float *logits_dev,
+                          void *stream) {
+  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, m->max_tokens, m->max_markers))
+    return rc;
+  if (n_seqs == 0) return JL_OK;
+  if (!ids_dev || !logits_dev) return fail(JL_ERR_ARG, "ids_dev and logits_dev must not be NULL");
+  DeviceGuard dg(m->device);
+  hipStream_t s = (hipStream_t)stream;
+  Plan pl;
+  if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl)) return rc;
+  return run_forward(m, ids_dev, pl, 26, logits_dev, s);
+}
+
+extern "C" int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
+                               const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, int32_t stage,
+                               float *out_dev, void *stream) {
+  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (stage < 0 || stage > 25) return fail(JL_ERR_ARG, "stage must be in 0..25");
+  if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, m->max_tokens, m->max_markers))
+    return rc;
+  if (n_seqs == 0) return JL_OK;
+  if (!ids_dev || !out_dev) return fail(JL_ERR_ARG, "ids_dev and out_dev must not be NULL");
+  DeviceGuard dg(m->device);
+  hipStream_t s = (hipStream_t)stream;
+  Plan pl;
+  if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl)) return rc;
+  return run_forward(m, ids_dev, pl, stage, out_dev, s);
+}
+
+extern "C" int jl_probs(jl_model *m, const float *logits_dev, const int32_t *seq_offsets, int32_t n_seqs,
+                        const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, float *probs_dev,
+                        float *answer_dev, int32_t *argmax_dev, float *maxprob_dev, void *stream) {
+  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, m->max_tokens, m->max_markers))
+    return rc;
+  if (n_seqs == 0) return JL_OK;
+  if (!logits_dev) return fail(JL_ERR_ARG, "logits_dev must not be NULL");
+  DeviceGuard dg(m->device);
+  hipStream_t s = (hipStream_t)stream;
+  Plan pl;
+  if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl)) return rc;
+  JL_LAUNCH(JL_K_MISC, launch_probs(logits_dev, pl.d_mo, pl.d_qt, n_seqs, probs_dev, answer_dev, argmax_dev,
+                                    maxprob_dev, s));
+  return JL_OK;
+}
+
+extern "C" int jl_profile(jl_model *m, int enable, uint32_t class_mask) {
+  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  m->prof = enable != 0;
+  m->prof_mask = class_mask;
+  m->prof_rec.clear();
+  m->ev_used = 0;
+  return JL_OK;
+}
+
+extern "C" int jl_profile_read(jl_model *m, int kernel_class, double *total_ms, int64_t *launches) {
+  if (!m || !total_ms || !launches) return fail(JL_ERR_ARG, "NULL argument");
+  if (kernel_class < 0 || kernel_class >= JL_K_NCLASS) return fail(JL_ERR_ARG, "bad kernel class");
+  DeviceGuard dg(m->device);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (const ProfRec &r : m->prof_rec) {
+    if (r.cls != kernel_class) continue;
+    JL_HIP(hipEventSynchronize(r.b));
+    float ms = 0.f;
+    JL_HIP(hipEventElapsedTime(&ms, r.a, r.b));
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return JL_OK;
+}

@@ -1,0 +1,82 @@
+// Internal declarations shared by the kernel and host translation units of
+// libjl.  Nothing here is part of the public C ABI (include/jl.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jl {
+
+// Model shape (mmBERT-small encoder + Julia-1 decision head).
+constexpr int kVocab = 256000;
+constexpr int kWidth = 384;
+constexpr int kHeads = 6;
+constexpr int kHeadDim = 64;
+constexpr int kLayers = 22;
+constexpr int kGeglu = 1152;        // GEGLU output width (projection is 2 x 1152)
+constexpr int kHeadFfn = 1536;
+constexpr int kHalfWindow = 64;     // local layers: |i - j| <= 64
+constexpr int kMaxSeq = 8192;
+constexpr double kThetaLocal = 10000.0;
+constexpr double kThetaGlobal = 160000.0;
+constexpr float kLnEps = 1e-5f;
+
+// A layer is global when its index is a multiple of 3 (layers 0, 3, ..., 21).
+inline bool layer_is_global(int l) { return l % 3 == 0; }
+
+enum AMode { A_ACT = 0, A_LN = 1 };                    // GEMM A-operand source
+enum EMode { E_STORE = 0, E_RESID = 1, E_GEGLU = 2, E_RELU = 3, E_GELU_F32 = 4 };
+
+// C[M, N] = A[M, K] . W[N, K]^T with a fused prologue (A_LN) and epilogue.
+struct GemmArgs {
+  const void *A;        // A_ACT: element matrix [M, lda]; A_LN: FP32 [M, lda], K == 384
+  int lda;
+  const float *ln_g;    // A_LN: LayerNorm gain (nullptr: no normalization)
+  const float *ln_b;    // A_LN: LayerNorm shift (nullptr: none)
+  const void *W;        // element matrix [N, ldw] (GEGLU: rows interleaved by 16)
+  int ldw;
+  const float *bias;    // [N] or nullptr
+  void *C;              // output (element type, or FP32 for E_RESID / E_GELU_F32)
+  int ldc;
+  int M, N, K;
+  const float *rope_cos;// E_STORE: [8192, 32] table or nullptr (no RoPE)
+  const float *rope_sin;
+  const int *pos;       // [M] position of each row inside its sequence (RoPE)
+  int rope_cols;        // columns [0, rope_cols) are rotated (q and k: 768)
+};
+
+// One attention work item: up to 64 queries of one sequence, one head per blockIdx.y.
+struct AttnWork {
+  int q_row0;   // first query row in the q buffer
+  int n_q;      // queries in this item (1..64)
+  int kv_row0;  // first key row of the sequence in the k/v buffers
+  int kv_len;   // sequence length
+  int q_pos0;   // position of the first query inside its sequence
+  int pad0, pad1, pad2;
+};
+
+struct AttnArgs {
+  const void *q; int q_stride;      // element strides between rows; head h at column 64h
+  const void *k; const void *v; int kv_stride;
+  void *o; int o_stride;
+  const AttnWork *work;
+  int half_window;                  // < 0: attend to the whole sequence
+};
+
+// Launchers (kernels.hip).  `bf16` selects the bf16 instantiation, else FP32.
+hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain, int T,
+                        const int *seq_offsets, int n_seqs, float *x, int *pos, int *tok_seq,
+                        hipStream_t s);
+hipError_t launch_gemm(bool bf16, int amode, int emode, const GemmArgs &a, hipStream_t s);
+hipError_t launch_attention(bool bf16, const AttnArgs &a, int n_work, hipStream_t s);
+hipError_t launch_final_ln_type(const float *x, const float *gain, const float *type_rows,
+                                const int *qtype, const int *tok_seq, int T, float *h,
+                                hipStream_t s);
+hipError_t launch_gather_rows(const float *src, const int *rows, int n, float *dst, hipStream_t s);
+hipError_t launch_score_dot(const float *hid, const float *w2, const float *b2, int n,
+                            float *logits, hipStream_t s);
+hipError_t launch_probs(const float *logits, const int *marker_offsets, const int *qtype,
+                        int n_seqs, float *probs, float *answer, int *argmax, float *maxprob,
+                        hipStream_t s);
+
+}  // namespace jl

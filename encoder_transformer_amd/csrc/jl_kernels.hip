@@ -1,0 +1,618 @@
+// HIP kernels of the Julia-1 forward pass for gfx950 (CDNA4, 64-wide waves).
+//
+// GEMMs and attention run on matrix cores: v_mfma_f32_16x16x32_bf16 in the
+// bf16 mode, v_mfma_f32_16x16x4_f32 in the FP32 mode, FP32 accumulation in
+// both.  Every operand fragment holds 8 consecutive K elements per lane (lane
+// group g = lane / 16 owns k = 8g .. 8g+7 of a 32-wide K step); the FP32 mode
+// feeds the same fragment to eight 16x16x4 steps, so one tiling serves both.
+// Row-wise work (LayerNorm, softmax over options, dot products) uses
+// wavefront reductions.
+#include "jl_internal.h"
+
+#include <math.h>
+
+namespace jl {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// fragments and matrix-core steps
+// ---------------------------------------------------------------------------
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+__device__ inline Frag<bf16> load_frag(const bf16 *p) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8 *>(p);
+  return f;
+}
+__device__ inline Frag<float> load_frag(const float *p) {
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4 *>(p);
+  f.hi = *reinterpret_cast<const f32x4 *>(p + 4);
+  return f;
+}
+__device__ inline void store_frag(bf16 *p, const Frag<bf16> &f) {
+  *reinterpret_cast<bf16x8 *>(p) = f.v;
+}
+__device__ inline void store_frag(float *p, const Frag<float> &f) {
+  *reinterpret_cast<f32x4 *>(p) = f.lo;
+  *reinterpret_cast<f32x4 *>(p + 4) = f.hi;
+}
+__device__ inline float frag_get(const Frag<bf16> &f, int e) { return (float)f.v[e]; }
+__device__ inline float frag_get(const Frag<float> &f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
+
+// Build a fragment from 8 FP32 values (bf16: round to nearest even).
+__device__ inline void frag_from(Frag<bf16> &f, const float *v) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)v[e];
+}
+__device__ inline void frag_from(Frag<float> &f, const float *v) {
+  f.lo = f32x4{v[0], v[1], v[2], v[3]};
+  f.hi = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// acc[16x16] += A(16 x 32) . B(32 x 16); lane (i + 16g) supplies A row i and
+// B column i at k = 8g .. 8g+7.
+__device__ inline void mfma(f32x4 &acc, const Frag<bf16> &a, const Frag<bf16> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ inline void mfma(f32x4 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], acc, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], acc, 0, 0, 0);
+}
+
+template <typename T> __device__ inline T to_elem(float v);
+template <> __device__ inline bf16 to_elem<bf16>(float v) { return (bf16)v; }
+template <> __device__ inline float to_elem<float>(float v) { return v; }
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ inline float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+
+// ---------------------------------------------------------------------------
+// embedding gather + LayerNorm (gain only); positions and sequence ids
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ ids,
+                                                    const float *__restrict__ emb,
+                                                    const float *__restrict__ gain, int T,
+                                                    const int *__restrict__ seq_offsets, int n_seqs,
+                                                    float *__restrict__ x, int *__restrict__ pos,
+                                                    int *__restrict__ tok_seq) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int id = ids[t];
+  const bool ok = id >= 0 && id < kVocab;
+  const float *e = emb + (size_t)(ok ? id : 0) * kWidth;
+  float v[6], s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) { v[i] = e[lane + 64 * i]; s += v[i]; }
+  const float mean = wave_sum(s) * (1.0f / kWidth);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) { const float d = v[i] - mean; q += d * d; }
+  const float rstd = rsqrtf(wave_sum(q) * (1.0f / kWidth) + kLnEps);
+  float *xr = x + (size_t)t * kWidth;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) xr[lane + 64 * i] = ok ? (v[i] - mean) * rstd * gain[lane + 64 * i] : NAN;
+  if (lane == 0) {
+    int lo = 0, hi = n_seqs - 1;  // last b with seq_offsets[b] <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seq_offsets[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    pos[t] = t - seq_offsets[lo];
+    tok_seq[t] = lo;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM: C = A . W^T, 256 threads as 2 x 2 waves, wave tile (BM/2) x 64
+// ---------------------------------------------------------------------------
+
+template <typename T> struct LdsStride;            // padded row strides: conflict-free
+template <> struct LdsStride<bf16> { static constexpr int v = 40; };   // 80 B rows
+template <> struct LdsStride<float> { static constexpr int v = 36; };  // 144 B rows
+
+template <typename T, int BM, int AM, int EM>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  constexpr int BN = 128, BK = 32, WN = 2;
+  constexpr int TM = BM / 2, TN = BN / WN;
+  constexpr int MT = TM / 16, NT = TN / 16;
+  constexpr int LS = LdsStride<T>::v;
+  constexpr int A_CH = BM * BK / 8 / 256;
+  constexpr int B_CH = BN * BK / 8 / 256;
+  static_assert(NT == 4, "epilogues assume 64 columns per wave");
+  __shared__ __attribute__((aligned(16))) T sA[2][BM * LS];
+  __shared__ __attribute__((aligned(16))) T sB[2][BN * LS];
+  __shared__ float sMean[BM], sRstd[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int M = g.M;
+
+  const bool do_ln = (AM == A_LN) && g.ln_g != nullptr;
+  if (do_ln) {
+    for (int r = wave; r < BM; r += 4) {
+      const int row = m0 + r;
+      float mean = 0.f, rstd = 0.f;
+      if (row < M) {
+        const float *xr = (const float *)g.A + (size_t)row * g.lda;
+        float v[6], s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) { v[i] = xr[lane + 64 * i]; s += v[i]; }
+        mean = wave_sum(s) * (1.0f / kWidth);
+        float q = 0.f;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) { const float d = v[i] - mean; q += d * d; }
+        rstd = rsqrtf(wave_sum(q) * (1.0f / kWidth) + kLnEps);
+      }
+      if (lane == 0) { sMean[r] = mean; sRstd[r] = rstd; }
+    }
+    __syncthreads();
+  }
+
+  Frag<T> ra[A_CH], rb[B_CH];
+  auto load_tiles = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int idx = tid + c * 256, r = idx >> 2, kc = (idx & 3) * 8;
+      const int row = min(m0 + r, M - 1);
+      if (AM == A_ACT) {
+        ra[c] = load_frag((const T *)g.A + (size_t)row * g.lda + k0 + kc);
+      } else {
+        const float *src = (const float *)g.A + (size_t)row * g.lda + k0 + kc;
+        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(src);
+        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(src + 4);
+        float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        if (do_ln) {
+          const float mu = sMean[r], rs = sRstd[r];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[e] = (v[e] - mu) * rs * g.ln_g[k0 + kc + e];
+            if (g.ln_b) v[e] += g.ln_b[k0 + kc + e];
+          }
+        }
+        frag_from(ra[c], v);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < B_CH; ++c) {
+      const int idx = tid + c * 256, r = idx >> 2, kc = (idx & 3) * 8;
+      rb[c] = load_frag((const T *)g.W + (size_t)(n0 + r) * g.ldw + k0 + kc);
+    }
+  };
+  auto store_tiles = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      const int idx = tid + c * 256, r = idx >> 2, kc = (idx & 3) * 8;
+      store_frag(&sA[buf][r * LS + kc], ra[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < B_CH; ++c) {
+      const int idx = tid + c * 256, r = idx >> 2, kc = (idx & 3) * 8;
+      store_frag(&sB[buf][r * LS + kc], rb[c]);
+    }
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = g.K / BK;
+  load_tiles(0);
+  store_tiles(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) load_tiles(kt + 1);
+    Frag<T> fa[MT], fb[NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      fa[i] = load_frag(&sA[cur][(wm * TM + i * 16 + (lane & 15)) * LS + (lane >> 4) * 8]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      fb[j] = load_frag(&sB[cur][(wn * TN + j * 16 + (lane & 15)) * LS + (lane >> 4) * 8]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) mfma(acc[i][j], fa[i], fb[j]);
+    if (kt + 1 < KT) store_tiles(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: acc[i][j][r] = C[row0 + 16i + r][col0 + 16j]
+  const int row0 = m0 + wm * TM + (lane >> 4) * 4;
+  const int wcol = n0 + wn * TN;            // first of this wave's 64 columns
+  const int col0 = wcol + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + i * 16 + r;
+      if (row >= M) continue;
+      float v[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) v[j] = acc[i][j][r];
+      if (EM == E_GEGLU) {
+        T *C = (T *)g.C + (size_t)row * g.ldc + wcol / 2 + (lane & 15);
+        C[0] = to_elem<T>(gelu_erf(v[0]) * v[1]);
+        C[16] = to_elem<T>(gelu_erf(v[2]) * v[3]);
+        continue;
+      }
+      if (g.bias) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) v[j] += g.bias[col0 + j * 16];
+      }
+      if (EM == E_STORE) {
+        if (g.rope_cos && wcol < g.rope_cols) {  // the wave's 64 columns are one head
+          const int p = g.pos[row];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int d = j * 16 + (lane & 15);
+            const float c = g.rope_cos[p * 32 + d], s = g.rope_sin[p * 32 + d];
+            const float lo = v[j], hi = v[j + 2];
+            v[j] = lo * c - hi * s;
+            v[j + 2] = hi * c + lo * s;
+          }
+        }
+        T *C = (T *)g.C + (size_t)row * g.ldc + col0;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) C[j * 16] = to_elem<T>(v[j]);
+      } else if (EM == E_RESID) {
+        float *C = (float *)g.C + (size_t)row * g.ldc + col0;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) C[j * 16] += v[j];
+      } else if (EM == E_RELU) {
+        T *C = (T *)g.C + (size_t)row * g.ldc + col0;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) C[j * 16] = to_elem<T>(fmaxf(v[j], 0.f));
+      } else if (EM == E_GELU_F32) {
+        float *C = (float *)g.C + (size_t)row * g.ldc + col0;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) C[j * 16] = gelu_erf(v[j]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention: one block = up to 64 queries of one sequence and one head.
+// S^T = K Q^T and O^T = V^T P^T keep each lane's 4 x 4 scores, its running
+// max / sum and its output column on the same query (lane % 16).
+// ---------------------------------------------------------------------------
+
+// Slot of key k (0..63) in the transposed V tile: the 8 keys that lane group
+// g feeds to one 32-key step, {4g..4g+3, 16+4g..16+4g+3}, become contiguous.
+__device__ inline int vt_slot(int k) {
+  const int w = k & 31;
+  return (k & 32) + ((w >> 2) & 3) * 8 + (w >> 4) * 4 + (w & 3);
+}
+
+template <typename T>
+__device__ inline void store_vt_pair(T *row, int slot, float a, float b);
+template <>
+__device__ inline void store_vt_pair<bf16>(bf16 *row, int slot, float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 p;
+  p[0] = (bf16)a;
+  p[1] = (bf16)b;
+  *reinterpret_cast<bf16x2 *>(row + slot) = p;
+}
+template <>
+__device__ inline void store_vt_pair<float>(float *row, int slot, float a, float b) {
+  *reinterpret_cast<float2 *>(row + slot) = make_float2(a, b);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  constexpr int KS = 72;  // LDS row stride (elements)
+  __shared__ __attribute__((aligned(16))) T sK[2][64 * KS];
+  __shared__ __attribute__((aligned(16))) T sV[2][64 * KS];  // [d][slot]
+  const AttnWork w = a.work[blockIdx.x];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 15, g = lane >> 4;
+  const int qi = wave * 16 + ql;
+  const int qpos = w.q_pos0 + qi;
+  const float scale = 0.125f * kLog2e;  // 1/sqrt(64), in the exp2 domain
+
+  const T *qp = (const T *)a.q + (size_t)(w.q_row0 + min(qi, w.n_q - 1)) * a.q_stride + h * kHeadDim;
+  const Frag<T> fq0 = load_frag(qp + g * 8);
+  const Frag<T> fq1 = load_frag(qp + 32 + g * 8);
+
+  int lo = 0, hi = w.kv_len;
+  if (a.half_window >= 0) {
+    lo = max(0, w.q_pos0 - a.half_window);
+    hi = min(w.kv_len, w.q_pos0 + w.n_q + a.half_window);
+  }
+  const int n_tiles = (hi - lo + 63) >> 6;
+
+  const T *kbase = (const T *)a.k + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
+  const T *vbase = (const T *)a.v + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
+  const int last = w.kv_len - 1;
+  Frag<T> rk0, rk1, rv0, rv1;
+  auto load_tile = [&](int t) {
+    const int base = lo + t * 64;
+    const int k0 = base + (tid >> 3);
+    const int v0 = base + 2 * (tid >> 3);
+    rk0 = load_frag(kbase + (size_t)min(k0, last) * a.kv_stride);
+    rk1 = load_frag(kbase + (size_t)min(k0 + 32, last) * a.kv_stride);
+    rv0 = load_frag(vbase + (size_t)min(v0, last) * a.kv_stride);
+    rv1 = load_frag(vbase + (size_t)min(v0 + 1, last) * a.kv_stride);
+  };
+  auto store_tile = [&](int buf) {
+    const int c = (tid & 7) * 8;
+    store_frag(&sK[buf][(tid >> 3) * KS + c], rk0);
+    store_frag(&sK[buf][((tid >> 3) + 32) * KS + c], rk1);
+    const int slot = vt_slot(2 * (tid >> 3));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) store_vt_pair<T>(&sV[buf][(c + e) * KS], slot, frag_get(rv0, e), frag_get(rv1, e));
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    f32x4 s[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      s[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const T *kr = &sK[cur][(ks * 16 + ql) * KS + g * 8];
+      mfma(s[ks], load_frag(kr), fq0);
+      mfma(s[ks], load_frag(kr + 32), fq1);
+    }
+    const int base = lo + t * 64;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = base + ks * 16 + 4 * g + r;
+        bool ok = key < hi;
+        if (a.half_window >= 0) ok = ok && abs(qpos - key) <= a.half_window;
+        const float v = ok ? s[ks][r] * scale : -INFINITY;
+        s[ks][r] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m - m_use);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= alpha;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(s[ks][r] - m_use);
+        s[ks][r] = p;
+        l += p;
+      }
+#pragma unroll
+    for (int kstep = 0; kstep < 2; ++kstep) {
+      float pv[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { pv[r] = s[2 * kstep][r]; pv[4 + r] = s[2 * kstep + 1][r]; }
+      Frag<T> fp;
+      frag_from(fp, pv);
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds)
+        mfma(o[ds], load_frag(&sV[cur][(ds * 16 + ql) * KS + kstep * 32 + g * 8]), fp);
+    }
+    if (t + 1 < n_tiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (qi < w.n_q) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    T *op = (T *)a.o + (size_t)(w.q_row0 + qi) * a.o_stride + h * kHeadDim + 4 * g;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) op[ds * 16 + r] = to_elem<T>(o[ds][r] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// row kernels
+// ---------------------------------------------------------------------------
+
+// h = LayerNorm(x; gain) + type_rows[qtype of the token's sequence]; h may alias x.
+__global__ __launch_bounds__(256) void final_ln_type_kernel(const float *x, const float *__restrict__ gain,
+                                                            const float *__restrict__ type_rows,
+                                                            const int *__restrict__ qtype,
+                                                            const int *__restrict__ tok_seq, int T, float *h) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float *xr = x + (size_t)t * kWidth;
+  float v[6], s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) { v[i] = xr[lane + 64 * i]; s += v[i]; }
+  const float mean = wave_sum(s) * (1.0f / kWidth);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) { const float d = v[i] - mean; q += d * d; }
+  const float rstd = rsqrtf(wave_sum(q) * (1.0f / kWidth) + kLnEps);
+  const float *tr = type_rows + (size_t)qtype[tok_seq[t]] * kWidth;
+  float *hr = h + (size_t)t * kWidth;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int c = lane + 64 * i;
+    hr[c] = (v[i] - mean) * rstd * gain[c] + tr[c];
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const float *__restrict__ src,
+                                                          const int *__restrict__ rows, int n,
+                                                          float *__restrict__ dst) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= n) return;
+  const float *s = src + (size_t)rows[m] * kWidth;
+  float *d = dst + (size_t)m * kWidth;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) d[lane + 64 * i] = s[lane + 64 * i];
+}
+
+__global__ __launch_bounds__(256) void score_dot_kernel(const float *__restrict__ hid,
+                                                        const float *__restrict__ w2,
+                                                        const float *__restrict__ b2, int n,
+                                                        float *__restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= n) return;
+  const float *r = hid + (size_t)m * kWidth;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) s += r[lane + 64 * i] * w2[lane + 64 * i];
+  s = wave_sum(s);
+  if (lane == 0) logits[m] = s + b2[0];
+}
+
+// One wave per question: softmax over its options and the three read-offs.
+__global__ __launch_bounds__(256) void probs_kernel(const float *__restrict__ logits,
+                                                    const int *__restrict__ marker_offsets,
+                                                    const int *__restrict__ qtype, int n_seqs,
+                                                    float *probs, float *answer, int *argmax,
+                                                    float *maxprob) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= n_seqs) return;
+  const int first = marker_offsets[b], n = marker_offsets[b + 1] - first;
+  const bool on = lane < n;
+  const float v = on ? logits[first + lane] : -INFINITY;
+  const float mx = wave_max(v);
+  const float e = on ? expf(v - mx) : 0.f;
+  const float sum = wave_sum(e);
+  const float p = e / sum;
+  // first index holding the maximum
+  int idx = (on && v == mx) ? lane : 64;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) idx = min(idx, __shfl_xor(idx, o, 64));
+  const float expect = wave_sum(on ? (float)lane * p : 0.f);
+  const float p1 = __shfl(p, 1, 64);
+  if (on && probs) probs[first + lane] = p;
+  if (lane == 0) {
+    const int qt = qtype[b];
+    if (answer) answer[b] = qt == 0 ? (float)idx : (qt == 1 ? expect : p1);
+    if (argmax) argmax[b] = idx;
+    if (maxprob) maxprob[b] = 1.0f / sum;
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain, int T,
+                        const int *seq_offsets, int n_seqs, float *x, int *pos, int *tok_seq,
+                        hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  embed_kernel<<<(T + 3) / 4, 256, 0, s>>>(ids, emb, gain, T, seq_offsets, n_seqs, x, pos, tok_seq);
+  return hipGetLastError();
+}
+
+template <typename T, int BM>
+static hipError_t gemm_dispatch(int amode, int emode, const GemmArgs &a, hipStream_t s) {
+  const dim3 grid(a.N / 128, (a.M + BM - 1) / BM);
+#define JL_GEMM(AM, EM)                                                  \
+  if (amode == AM && emode == EM) {                                      \
+    gemm_kernel<T, BM, AM, EM><<<grid, 256, 0, s>>>(a);                  \
+    return hipGetLastError();                                            \
+  }
+  JL_GEMM(A_LN, E_STORE)
+  JL_GEMM(A_ACT, E_RESID)
+  JL_GEMM(A_LN, E_GEGLU)
+  JL_GEMM(A_LN, E_RELU)
+  JL_GEMM(A_LN, E_GELU_F32)
+#undef JL_GEMM
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(bool bf16_mode, int amode, int emode, const GemmArgs &a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  if (a.N % 128 != 0 || a.K % 32 != 0 || (amode == A_LN && a.K != kWidth)) return hipErrorInvalidValue;
+  const bool big = (long)((a.M + 127) / 128) * (a.N / 128) >= 512;
+  if (bf16_mode && emode != E_GELU_F32)
+    return big ? gemm_dispatch<bf16, 128>(amode, emode, a, s) : gemm_dispatch<bf16, 64>(amode, emode, a, s);
+  return big ? gemm_dispatch<float, 128>(amode, emode, a, s) : gemm_dispatch<float, 64>(amode, emode, a, s);
+}
+
+hipError_t launch_attention(bool bf16_mode, const AttnArgs &a, int n_work, hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  const dim3 grid(n_work, kHeads);
+  if (bf16_mode) attn_kernel<bf16><<<grid, 256, 0, s>>>(a);
+  else attn_kernel<float><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_final_ln_type(const float *x, const float *gain, const float *type_rows,
+                                const int *qtype, const int *tok_seq, int T, float *h, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  final_ln_type_kernel<<<(T + 3) / 4, 256, 0, s>>>(x, gain, type_rows, qtype, tok_seq, T, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const float *src, const int *rows, int n, float *dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  gather_rows_kernel<<<(n + 3) / 4, 256, 0, s>>>(src, rows, n, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_dot(const float *hid, const float *w2, const float *b2, int n, float *logits,
+                            hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  score_dot_kernel<<<(n + 3) / 4, 256, 0, s>>>(hid, w2, b2, n, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_probs(const float *logits, const int *marker_offsets, const int *qtype, int n_seqs,
+                        float *probs, float *answer, int *argmax, float *maxprob, hipStream_t s) {
+  if (n_seqs <= 0) return hipSuccess;
+  probs_kernel<<<(n_seqs + 3) / 4, 256, 0, s>>>(logits, marker_offsets, qtype, n_seqs, probs, answer,
+                                                argmax, maxprob);
+  return hipGetLastError();
+}
+
+}  // namespace jl

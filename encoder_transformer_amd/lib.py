@@ -1,0 +1,182 @@
+"""Python binding of libjl (include/jl.h): argument marshalling only.
+
+Every step of the forward pass runs in the library's HIP kernels. PyTorch
+supplies device memory and streams; host-side batch metadata travels as
+NumPy int32 arrays. The binding raises `JLError` on any non-zero status and
+`RuntimeError` when the library has not been built (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjl.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "jl.h")
+
+FP32, BF16 = 0, 1
+OK, ERR_ARG, ERR_OPTIONS, ERR_LENGTH, ERR_QTYPE, ERR_FILE, ERR_DEVICE, ERR_OOM, ERR_CAPACITY = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8)
+STATUS_NAMES = {0: "OK", -1: "ARG", -2: "OPTIONS", -3: "LENGTH", -4: "QTYPE", -5: "FILE",
+                -6: "DEVICE", -7: "OOM", -8: "CAPACITY"}
+K_EMBED, K_QKV, K_ATTN_GLOBAL, K_ATTN_LOCAL, K_OUTPROJ, K_MLP_IN, K_MLP_OUT, K_HEAD_GEMM, K_HEAD_ATTN, K_MISC = range(10)
+KERNEL_CLASS_NAMES = ["embed", "qkv", "attn_global", "attn_local", "outproj", "mlp_in", "mlp_out",
+                      "head_gemm", "head_attn", "misc"]
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_lib = None
+
+
+class JLError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"jl status {code} ({STATUS_NAMES.get(code, '?')}): {message}")
+        self.code = code
+        self.message = message
+
+
+def load_library():
+    """Load libjl.so (built by encoder_transformer_amd.build); raise if missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m encoder_transformer_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.jl_last_error.restype = ctypes.c_char_p
+    L.jl_last_error.argtypes = []
+    L.jl_load_weights.restype = ctypes.c_int
+    L.jl_load_weights.argtypes = [ctypes.c_char_p, ctypes.c_int, i64, i64, ctypes.c_int, ctypes.POINTER(vp)]
+    L.jl_free.restype = None
+    L.jl_free.argtypes = [vp]
+    L.jl_validate.restype = ctypes.c_int
+    L.jl_validate.argtypes = [_i32p, i32, _i32p, i32, _i32p, i64, i64]
+    L.jl_forward.restype = ctypes.c_int
+    L.jl_forward.argtypes = [vp, vp, _i32p, i32, _i32p, i32, _i32p, vp, vp]
+    L.jl_probs.restype = ctypes.c_int
+    L.jl_probs.argtypes = [vp, vp, _i32p, i32, _i32p, i32, _i32p, vp, vp, vp, vp, vp]
+    L.jl_debug_hidden.restype = ctypes.c_int
+    L.jl_debug_hidden.argtypes = [vp, vp, _i32p, i32, _i32p, i32, _i32p, i32, vp, vp]
+    L.jl_profile.restype = ctypes.c_int
+    L.jl_profile.argtypes = [vp, ctypes.c_int, ctypes.c_uint32]
+    L.jl_profile_read.restype = ctypes.c_int
+    L.jl_profile_read.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    L.jl_model_info.restype = ctypes.c_int
+    L.jl_model_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.c_int]
+    _lib = L
+    return L
+
+
+def declared_symbols() -> list:
+    """Names of the functions include/jl.h declares."""
+    with open(HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(jl_[a-z_]+)\s*\(", text)))
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise JLError(rc, load_library().jl_last_error().decode())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_i32p)
+
+
+def validate(seq_offsets, mask_positions, qtype, max_tokens: int, max_markers: int) -> None:
+    so, mp, qt = _i32(seq_offsets), _i32(mask_positions), _i32(qtype)
+    _check(load_library().jl_validate(_p(so), len(qt), _p(mp), len(mp), _p(qt), max_tokens, max_markers))
+
+
+class Model:
+    """One loaded weight set on one device, with a workspace for `max_tokens` tokens."""
+
+    def __init__(self, weight_path: str, precision: int = BF16, max_tokens: int = 16384,
+                 max_markers: Optional[int] = None, device: int = 0):
+        self._lib = load_library()
+        self.device = device
+        self.precision = precision
+        self.max_tokens = int(max_tokens)
+        self.max_markers = int(max_markers if max_markers is not None else max(2, min(max_tokens, 20 * 512)))
+        h = ctypes.c_void_p()
+        _check(self._lib.jl_load_weights(weight_path.encode(), precision, self.max_tokens, self.max_markers,
+                                         device, ctypes.byref(h)))
+        self._h = h
+
+    # -- helpers -----------------------------------------------------------
+    def _stream(self, stream):
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        return ctypes.c_void_p(s.cuda_stream)
+
+    def _meta(self, seq_offsets, mask_positions, qtype):
+        so, mp, qt = _i32(seq_offsets), _i32(mask_positions), _i32(qtype)
+        return so, mp, qt
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.jl_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def info(self) -> dict:
+        buf = (ctypes.c_int64 * 6)()
+        _check(self._lib.jl_model_info(self._h, buf, 6))
+        keys = ["precision", "max_tokens", "max_markers", "device", "weight_bytes", "workspace_bytes"]
+        return dict(zip(keys, list(buf)))
+
+    # -- entry points --------------------------------------------------------
+    def forward(self, ids, seq_offsets, mask_positions, qtype, out=None, stream=None):
+        """Option logits [n_markers] (torch float32 on the device)."""
+        import torch
+        so, mp, qt = self._meta(seq_offsets, mask_positions, qtype)
+        if out is None:
+            out = torch.empty(len(mp), dtype=torch.float32, device=f"cuda:{self.device}")
+        _check(self._lib.jl_forward(self._h, ctypes.c_void_p(ids.data_ptr()), _p(so), len(qt), _p(mp), len(mp),
+                                    _p(qt), ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
+        return out
+
+    def probs(self, logits, seq_offsets, mask_positions, qtype, stream=None):
+        """(probs [M], answer [B], argmax [B] int32, maxprob [B]) as torch tensors on the device."""
+        import torch
+        so, mp, qt = self._meta(seq_offsets, mask_positions, qtype)
+        dev = f"cuda:{self.device}"
+        probs = torch.empty(len(mp), dtype=torch.float32, device=dev)
+        answer = torch.empty(len(qt), dtype=torch.float32, device=dev)
+        argmax = torch.empty(len(qt), dtype=torch.int32, device=dev)
+        maxprob = torch.empty(len(qt), dtype=torch.float32, device=dev)
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+        _check(self._lib.jl_probs(self._h, ptr(logits), _p(so), len(qt), _p(mp), len(mp), _p(qt), ptr(probs),
+                                  ptr(answer), ptr(argmax), ptr(maxprob), self._stream(stream)))
+        return probs, answer, argmax, maxprob
+
+    def debug_hidden(self, ids, seq_offsets, mask_positions, qtype, stage: int, stream=None):
+        import torch
+        so, mp, qt = self._meta(seq_offsets, mask_positions, qtype)
+        rows = len(mp) if stage == 25 else int(so[-1])
+        out = torch.empty((rows, 384), dtype=torch.float32, device=f"cuda:{self.device}")
+        _check(self._lib.jl_debug_hidden(self._h, ctypes.c_void_p(ids.data_ptr()), _p(so), len(qt), _p(mp),
+                                         len(mp), _p(qt), stage, ctypes.c_void_p(out.data_ptr()),
+                                         self._stream(stream)))
+        return out
+
+    def profile(self, enable: bool, class_mask: int = 0x3FF):
+        _check(self._lib.jl_profile(self._h, int(enable), class_mask))
+
+    def profile_read(self, kernel_class: int):
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(self._lib.jl_profile_read(self._h, kernel_class, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value

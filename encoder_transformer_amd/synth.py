@@ -283,6 +283,12 @@ CONFIG_NAMES = {
 }
 
 
+def concat(batches: Sequence[Batch]) -> Batch:
+    """One packed batch holding every sequence of ``batches`` in order."""
+    parts = [b.sequence(i) for b in batches for i in range(b.n_seqs)]
+    return pack([p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts])
+
+
 def make_batch(config: int, seed: Optional[int] = None) -> Batch:
     """The packed batch of one of the five workload configurations."""
     rng = np.random.default_rng(1000 + config if seed is None else seed)

@@ -1,0 +1,171 @@
+/*
+ * jl.h -- C ABI of the MI355X (gfx950) forward pass of the Julia-1 decision model.
+ *
+ * The model: an mmBERT-small encoder (ModernBERT block: 22 pre-norm layers of
+ * width 384, 6 heads of 64, RoPE, a +-64-token window on two of every three
+ * layers, GEGLU feed-forward of 1,152), a type row added to every position,
+ * two pre-norm transformer layers (feed-forward 1,536, ReLU, biases), a gather
+ * at the option markers and a LayerNorm -> Linear(384,384) -> GELU ->
+ * Linear(384,1) scorer, one logit per option, then a softmax across each
+ * question's options.  Sources: "Julia-1: one score per mask token ..." (The
+ * decision head; Three modes through one head), "Julia-1 MLX" (Performance),
+ * "julia1 - Rust runtime for Julia-1" (Use; Why it is faster).
+ *
+ * Conventions for every entry point:
+ *   - Return value: JL_OK (0) or a negative jl_status; jl_last_error() then
+ *     holds a message (thread-local, valid until the next call on the thread).
+ *   - Validation runs on the host before anything is enqueued.  On an error
+ *     nothing is enqueued and no output is touched.  Inputs are never
+ *     truncated: an over-long or malformed batch is rejected.
+ *   - Calls return once their work is enqueued on `stream` (a hipStream_t, or
+ *     NULL for the default stream); the caller synchronizes that stream before
+ *     reading outputs.  A handle owns one workspace: calls on one handle must
+ *     be ordered (one stream, or the caller orders them), never concurrent.
+ *   - "_dev" pointers are device memory on the handle's device, caller-owned.
+ *     All other pointers are host memory, caller-owned, read only during the
+ *     call.
+ */
+#ifndef JL_H
+#define JL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct jl_model jl_model; /* opaque: weights on the device + workspace */
+
+enum jl_precision {
+  JL_FP32 = 0, /* every product in FP32 (FP32 matrix cores)                    */
+  JL_BF16 = 1  /* GEMM and attention operands in bf16 (round to nearest even),  */
+               /* FP32 accumulation; residual stream, LayerNorms, embeddings,   */
+               /* RoPE tables, scorer and softmax stay FP32 ("Julia-1 MLX",     */
+               /* Performance: the residual carries outliers near 4,000)        */
+};
+
+enum jl_status {
+  JL_OK = 0,
+  JL_ERR_ARG = -1,      /* null pointer, negative count, bad precision/stage   */
+  JL_ERR_OPTIONS = -2,  /* a question with <2 or >20 options, noul without 2,  */
+                        /* markers unsorted, duplicated or outside every seq  */
+  JL_ERR_LENGTH = -3,   /* a sequence of length 0 or > 8,192, offsets not      */
+                        /* increasing from 0                                   */
+  JL_ERR_QTYPE = -4,    /* a question type outside {0,1,2}                     */
+  JL_ERR_FILE = -5,     /* weight file missing, truncated, bad magic/checksum  */
+  JL_ERR_DEVICE = -6,   /* a HIP runtime error (message holds its string)      */
+  JL_ERR_OOM = -7,      /* device or pinned-host allocation failed at load     */
+  JL_ERR_CAPACITY = -8  /* more tokens or markers than the handle was sized for */
+};
+
+enum jl_qtype { JL_CHOICE = 0, JL_SCORE = 1, JL_NOUL = 2 };
+
+#define JL_MAX_SEQ_LEN 8192 /* tokens per sequence (explainer: 8,192 in all) */
+#define JL_MIN_OPTIONS 2    /* options per question: 2-20 (all pages)          */
+#define JL_MAX_OPTIONS 20
+
+/*
+ * Load a weight file written by the seeded generator (format "JLW1": header
+ * with tensor names, shapes, offsets and per-tensor checksums, then FP32
+ * data) onto `device`, convert it for `precision` and size a workspace for
+ * batches of up to `max_tokens` packed tokens and `max_markers` options.
+ * Checks every tensor's presence, shape and checksum.  On success *out holds
+ * a new handle that the caller releases with jl_free.
+ */
+int jl_load_weights(const char *path, int precision, int64_t max_tokens,
+                    int64_t max_markers, int device, jl_model **out);
+
+/* Release a handle and all its device memory (NULL is allowed). */
+void jl_free(jl_model *m);
+
+/*
+ * Host-only check of a packed batch; jl_forward and jl_probs call it first.
+ *   seq_offsets  [n_seqs+1] cumulative lengths: seq_offsets[0] = 0, strictly
+ *                increasing, every length in [1, 8192], total <= max_tokens.
+ *   mask_positions [n_markers] absolute packed indices of the <mask> markers,
+ *                strictly increasing; each sequence owns the markers inside
+ *                [start, end), 2 to 20 of them, exactly 2 for a noul question
+ *                (options [false, true]); n_markers <= max_markers.
+ *   qtype        [n_seqs] 0 choice, 1 score, 2 noul.
+ * n_seqs = 0 (an empty batch) is valid.
+ */
+int jl_validate(const int32_t *seq_offsets, int32_t n_seqs,
+                const int32_t *mask_positions, int32_t n_markers,
+                const int32_t *qtype, int64_t max_tokens, int64_t max_markers);
+
+/*
+ * Option logits of a packed batch: logits_dev[k] is the score of marker k
+ * (FP32, [n_markers]).  ids_dev: int32 token ids [seq_offsets[n_seqs]] on the
+ * device; an id outside [0, 256000) makes its whole sequence's logits NaN.
+ * Sequences never attend to each other.  Ragged lengths need no padding.
+ */
+int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets,
+               int32_t n_seqs, const int32_t *mask_positions, int32_t n_markers,
+               const int32_t *qtype, float *logits_dev, void *stream);
+
+/*
+ * Softmax across each question's options (temperature 1) and the answers of
+ * the three modes ("Julia-1: one score per mask token ...", Three modes
+ * through one head):
+ *   probs_dev   [n_markers] FP32 option probabilities;
+ *   answer_dev  [n_seqs] FP32: choice -> index of the argmax option,
+ *               score -> expected index sum_i i * p_i (0-based),
+ *               noul -> p(true) = p_1;
+ *   argmax_dev  [n_seqs] int32, the first maximum on ties;
+ *   maxprob_dev [n_seqs] FP32, the largest probability.
+ * Any output pointer may be NULL to skip it.
+ */
+int jl_probs(jl_model *m, const float *logits_dev, const int32_t *seq_offsets,
+             int32_t n_seqs, const int32_t *mask_positions, int32_t n_markers,
+             const int32_t *qtype, float *probs_dev, float *answer_dev,
+             int32_t *argmax_dev, float *maxprob_dev, void *stream);
+
+/*
+ * Diagnostic: run the forward pass up to `stage` and copy a hidden state out
+ * (FP32, row-major, width 384):
+ *   0..22  the residual stream after the embedding and `stage` encoder
+ *          layers, [T, 384];
+ *   23     the head input: final encoder LayerNorm plus the type row, [T, 384];
+ *   24     after the first head layer, [T, 384];
+ *   25     after the second head layer, marker rows only, [n_markers, 384].
+ */
+int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets,
+                    int32_t n_seqs, const int32_t *mask_positions, int32_t n_markers,
+                    const int32_t *qtype, int32_t stage, float *out_dev, void *stream);
+
+/* Kernel classes reported by the per-kernel timer. */
+enum jl_kernel_class {
+  JL_K_EMBED = 0,      /* embedding gather + LayerNorm                         */
+  JL_K_QKV = 1,        /* encoder QKV GEMM (LayerNorm on load, RoPE on store)   */
+  JL_K_ATTN_GLOBAL = 2,/* encoder attention, global layers                      */
+  JL_K_ATTN_LOCAL = 3, /* encoder attention, +-64 window layers                 */
+  JL_K_OUTPROJ = 4,    /* encoder out-projection GEMM + residual                */
+  JL_K_MLP_IN = 5,     /* encoder Wi GEMM (LayerNorm on load) + GEGLU           */
+  JL_K_MLP_OUT = 6,    /* encoder Wo GEMM + residual                            */
+  JL_K_HEAD_GEMM = 7,  /* decision-head GEMMs                                   */
+  JL_K_HEAD_ATTN = 8,  /* decision-head attention                               */
+  JL_K_MISC = 9,       /* final LayerNorm + type row, gathers, scorer, softmax  */
+  JL_K_NCLASS = 10
+};
+
+/* Turn the per-kernel timer on (1) or off (0); it brackets every launch of
+ * the classes in `class_mask` (bit i = class i) with HIP events recorded on
+ * the launch stream.  Turning it on clears previous records. */
+int jl_profile(jl_model *m, int enable, uint32_t class_mask);
+
+/* Total device time (ms) and launch count of one class since jl_profile(1).
+ * Synchronizes on the recorded events. */
+int jl_profile_read(jl_model *m, int kernel_class, double *total_ms, int64_t *launches);
+
+/* info[0..n): precision, max_tokens, max_markers, device, device bytes of
+ * weights, device bytes of workspace. */
+int jl_model_info(const jl_model *m, int64_t *info, int n);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *jl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JL_H */
