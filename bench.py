@@ -56,6 +56,7 @@ def class_flops(batch):
         "head_attn": 1536 * glob + 1536 * int(sum(len(batch.sequence(b)[1]) * lens[b]
                                                   for b in range(batch.n_seqs))),
         "misc": 2 * M * D * D + 2 * M * D,
+        "ln": 0, "embed": 0,
     }
     launches = {"qkv": 22, "outproj": 22, "mlp_in": 22, "mlp_out": 22, "attn_global": 8, "attn_local": 14}
     return f, launches
@@ -73,11 +74,11 @@ def time_workload(model, batch, steps, warmup, profile_class=None):
         model.probs(logits, so, mp, qt)
 
     # warm-up with every class timed, to find where the device time goes
-    model.profile(True, 0x3FF)
+    model.profile(True, (1 << lib.N_KERNEL_CLASSES) - 1)
     for _ in range(max(1, warmup)):
         step()
     torch.cuda.synchronize()
-    per_class = {lib.KERNEL_CLASS_NAMES[c]: model.profile_read(c) for c in range(10)}
+    per_class = {lib.KERNEL_CLASS_NAMES[c]: model.profile_read(c) for c in range(lib.N_KERNEL_CLASSES)}
     dominant = max(per_class, key=lambda k: per_class[k][0]) if profile_class is None else profile_class
     cls_id = lib.KERNEL_CLASS_NAMES.index(dominant)
     model.profile(True, 1 << cls_id)
@@ -93,19 +94,19 @@ def time_workload(model, batch, steps, warmup, profile_class=None):
 
 
 def cpu_baseline():
-    """The oracle on two 1,024-token sequences of the throughput batch."""
+    """The oracle on six 1,024-token sequences of the throughput batch."""
     from threadpoolctl import threadpool_info
     from encoder_transformer_amd import synth
     from oracle import julia_oracle as jo
     W = jo.OracleWeights(synth.make_weights())
     batch = synth.make_batch(2)
-    seqs = [0, 1]
+    seqs = [0, 1, 2, 3, 4, 5]
     t0 = time.perf_counter()
     jo.forward(W, batch, seqs)
     t = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": round(len(seqs) / t, 4), "unit": "decisions/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"2 of the 16 x 1,024-token sequences (2,048 tokens), float64 NumPy, {t:.1f} s"}
+            "sample": f"6 of the 16 x 1,024-token sequences (6,144 tokens), float64 NumPy, {t:.1f} s"}
 
 
 def main():

@@ -95,14 +95,19 @@ struct jl_model {
   const float *rope_cos[2] = {nullptr, nullptr}, *rope_sin[2] = {nullptr, nullptr};  // [0] local, [1] global
 
   // workspace
-  float *x = nullptr, *z = nullptr, *sh = nullptr;
+  float *x = nullptr, *z = nullptr, *zu = nullptr, *sh = nullptr;
   char *qkv = nullptr, *o = nullptr, *act = nullptr, *qm = nullptr, *om = nullptr, *actm = nullptr;
   int *pos = nullptr, *tok_seq = nullptr;
-  int *meta = nullptr;
+  // Batch metadata ring: call i uses slot i % kMetaSlots (pinned staging +
+  // device copy); slot_done[k] is recorded after the last kernel that reads
+  // slot k, so the host may run up to kMetaSlots - 1 calls ahead of the GPU.
+  static constexpr int kMetaSlots = 4;
+  int *meta[kMetaSlots] = {};
+  int *host_meta[kMetaSlots] = {};
+  hipEvent_t slot_done[kMetaSlots] = {};
+  bool slot_pending[kMetaSlots] = {};
+  int next_slot = 0;
   size_t meta_ints = 0;
-  int *host_meta = nullptr;  // pinned staging
-  hipEvent_t upload_done = nullptr;
-  bool upload_pending = false;
 
   // per-kernel timer
   bool prof = false;
@@ -256,12 +261,14 @@ extern "C" int jl_validate(const int32_t *seq_offsets, int32_t n_seqs, const int
 extern "C" void jl_free(jl_model *m) {
   if (!m) return;
   DeviceGuard dg(m->device);
-  if (m->upload_done) {
-    (void)hipEventSynchronize(m->upload_done);
-    (void)hipEventDestroy(m->upload_done);
+  for (int k = 0; k < jl_model::kMetaSlots; ++k) {
+    if (m->slot_done[k]) {
+      (void)hipEventSynchronize(m->slot_done[k]);
+      (void)hipEventDestroy(m->slot_done[k]);
+    }
+    if (m->host_meta[k]) (void)hipHostFree(m->host_meta[k]);
   }
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
-  if (m->host_meta) (void)hipHostFree(m->host_meta);
   if (m->ws) (void)hipFree(m->ws);
   if (m->warena) (void)hipFree(m->warena);
   delete m;
@@ -474,15 +481,18 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
   reserve((void **)&m->om, Mm * D * es);
   reserve((void **)&m->actm, Mm * kHeadFfn * es);
   reserve((void **)&m->sh, Mm * D * 4);
-  reserve((void **)&m->meta, m->meta_ints * 4);
+  reserve((void **)&m->zu, Mm * D * 4);
+  for (int k = 0; k < jl_model::kMetaSlots; ++k) reserve((void **)&m->meta[k], m->meta_ints * 4);
   m->wsbytes = (off + 255) & ~size_t(255);
   if (hipMalloc((void **)&m->ws, m->wsbytes) != hipSuccess)
     return bail(JL_ERR_OOM, "cannot allocate the device workspace");
   for (auto &sl : slots) *sl.first = m->ws + sl.second;
-  if (hipHostMalloc((void **)&m->host_meta, m->meta_ints * 4, hipHostMallocDefault) != hipSuccess)
-    return bail(JL_ERR_OOM, "cannot allocate pinned staging memory");
-  if (hipEventCreateWithFlags(&m->upload_done, hipEventDisableTiming) != hipSuccess)
-    return bail(JL_ERR_DEVICE, "cannot create an event");
+  for (int k = 0; k < jl_model::kMetaSlots; ++k) {
+    if (hipHostMalloc((void **)&m->host_meta[k], m->meta_ints * 4, hipHostMallocDefault) != hipSuccess)
+      return bail(JL_ERR_OOM, "cannot allocate pinned staging memory");
+    if (hipEventCreateWithFlags(&m->slot_done[k], hipEventDisableTiming) != hipSuccess)
+      return bail(JL_ERR_DEVICE, "cannot create an event");
+  }
   *out = m;
   return JL_OK;
 }
@@ -502,6 +512,7 @@ extern "C" int jl_model_info(const jl_model *m, int64_t *info, int n) {
 namespace {
 
 struct Plan {
+  int slot = 0;
   int B = 0, M = 0, T = 0;
   int n_work = 0;
   const int *d_so = nullptr, *d_mo = nullptr, *d_qt = nullptr, *d_mp = nullptr;
@@ -514,11 +525,15 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
   pl.B = B;
   pl.M = M;
   pl.T = so[B];
-  if (m->upload_pending) {
-    JL_HIP(hipEventSynchronize(m->upload_done));
-    m->upload_pending = false;
+  const int slot = m->next_slot;
+  m->next_slot = (slot + 1) % jl_model::kMetaSlots;
+  if (m->slot_pending[slot]) {
+    JL_HIP(hipEventSynchronize(m->slot_done[slot]));
+    m->slot_pending[slot] = false;
   }
-  int *h = m->host_meta;
+  pl.slot = slot;
+  int *h = m->host_meta[slot];
+  int *dmeta = m->meta[slot];
   size_t o = 0;
   const size_t o_so = o;
   for (int b = 0; b <= B; ++b) h[o++] = so[b];
@@ -559,16 +574,26 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
     o += 8;
   }
   if (o > m->meta_ints) return fail(JL_ERR_CAPACITY, "batch metadata exceeds the staging buffer");
-  JL_HIP(hipMemcpyAsync(m->meta, h, o * 4, hipMemcpyHostToDevice, s));
-  JL_HIP(hipEventRecord(m->upload_done, s));
-  m->upload_pending = true;
+  JL_HIP(hipMemcpyAsync(dmeta, h, o * 4, hipMemcpyHostToDevice, s));
   pl.n_work = nw;
-  pl.d_so = m->meta + o_so;
-  pl.d_mo = m->meta + o_mo;
-  pl.d_qt = m->meta + o_qt;
-  pl.d_mp = m->meta + o_mp;
-  pl.d_aw = (const AttnWork *)(m->meta + o_aw);
-  pl.d_mw = (const AttnWork *)(m->meta + o_mw);
+  pl.d_so = dmeta + o_so;
+  pl.d_mo = dmeta + o_mo;
+  pl.d_qt = dmeta + o_qt;
+  pl.d_mp = dmeta + o_mp;
+  pl.d_aw = (const AttnWork *)(dmeta + o_aw);
+  pl.d_mw = (const AttnWork *)(dmeta + o_mw);
+  return JL_OK;
+}
+
+// After the last launch that reads the slot's metadata (always, even after an
+// error, so that the slot is never left without a completion marker).
+int finish_plan(jl_model *m, const Plan &pl, hipStream_t s, int rc) {
+  if (hipEventRecord(m->slot_done[pl.slot], s) == hipSuccess) {
+    m->slot_pending[pl.slot] = true;
+  } else if (rc == JL_OK) {
+    JL_HIP(hipStreamSynchronize(s));
+  }
+  return rc;
   return JL_OK;
 }
 
@@ -611,13 +636,11 @@ struct Launch {
     if (e_ != hipSuccess) return fail(JL_ERR_DEVICE, std::string("kernel launch failed: ") + hipGetErrorString(e_)); \
   } while (0)
 
-GemmArgs gemm(const void *A, int lda, const float *g, const float *b, const void *W, int ldw, const float *bias,
-              void *C, int ldc, int M, int N, int K) {
+GemmArgs gemm(const void *A, int lda, const void *W, int ldw, const float *bias, void *C, int ldc, int M, int N,
+              int K) {
   GemmArgs a{};
   a.A = A;
   a.lda = lda;
-  a.ln_g = g;
-  a.ln_b = b;
   a.W = W;
   a.ldw = ldw;
   a.bias = bias;
@@ -630,10 +653,15 @@ GemmArgs gemm(const void *A, int lda, const float *g, const float *b, const void
 }
 
 // Enqueue the forward pass up to `stop` (see jl_debug_hidden; 26 = logits).
+//   x   FP32 residual stream [T, 384] (the head's h from the final LayerNorm on)
+//   u   normalized GEMM operand [T, 384] (shares the attention-output buffer o)
+//   qkv [T, 1152]; head layer 2 keeps keys|values there as [T, 768]
+//   act [T, 1152] GEGLU output / [T, 1536] head FFN hidden
 int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float *out, hipStream_t s) {
   const bool bf = m->bf16;
   const size_t es = m->esize;
   const int T = pl.T, M = pl.M, D = kWidth;
+  char *u = m->o;
   auto copy_out = [&](const float *src, size_t rows) -> int {
     JL_HIP(hipMemcpyAsync(out, src, rows * D * 4, hipMemcpyDeviceToDevice, s));
     return JL_OK;
@@ -653,24 +681,20 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   for (int l = 0; l < kLayers; ++l) {
     const LayerW &W = m->L[l];
     const bool glob = layer_is_global(l);
-    GemmArgs q = gemm(m->x, D, W.attn_norm, nullptr, W.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D);
+    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, W.attn_norm, nullptr, T, u, s));
+    GemmArgs q = gemm(u, D, W.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D);
     q.rope_cos = m->rope_cos[glob];
     q.rope_sin = m->rope_sin[glob];
     q.pos = m->pos;
     q.rope_cols = 2 * D;
-    JL_LAUNCH(JL_K_QKV, launch_gemm(bf, A_LN, E_STORE, q, s));
+    JL_LAUNCH(JL_K_QKV, launch_gemm(bf, E_STORE, q, s));
     at.half_window = glob ? -1 : kHalfWindow;
     JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, launch_attention(bf, at, pl.n_work, s));
-    JL_LAUNCH(JL_K_OUTPROJ,
-              launch_gemm(bf, A_ACT, E_RESID, gemm(m->o, D, nullptr, nullptr, W.Wo, D, nullptr, m->x, D, T, D, D), s));
-    JL_LAUNCH(JL_K_MLP_IN, launch_gemm(bf, A_LN, E_GEGLU,
-                                       gemm(m->x, D, W.mlp_norm, nullptr, W.Wi, D, nullptr, m->act, kGeglu, T,
-                                            2 * kGeglu, D),
-                                       s));
-    JL_LAUNCH(JL_K_MLP_OUT, launch_gemm(bf, A_ACT, E_RESID,
-                                        gemm(m->act, kGeglu, nullptr, nullptr, W.Wout, kGeglu, nullptr, m->x, D, T,
-                                             D, kGeglu),
-                                        s));
+    JL_LAUNCH(JL_K_OUTPROJ, launch_gemm(bf, E_RESID, gemm(m->o, D, W.Wo, D, nullptr, m->x, D, T, D, D), s));
+    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, W.mlp_norm, nullptr, T, u, s));
+    JL_LAUNCH(JL_K_MLP_IN, launch_gemm(bf, E_GEGLU, gemm(u, D, W.Wi, D, nullptr, m->act, kGeglu, T, 2 * kGeglu, D), s));
+    JL_LAUNCH(JL_K_MLP_OUT,
+              launch_gemm(bf, E_RESID, gemm(m->act, kGeglu, W.Wout, kGeglu, nullptr, m->x, D, T, D, kGeglu), s));
     if (stop == l + 1) return copy_out(m->x, T);
   }
   // head input: final LayerNorm + type row (in place)
@@ -680,21 +704,16 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   // head layer 1 over every token
   {
     const HeadW &H = m->H[0];
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_STORE,
-                                          gemm(m->x, D, H.n1_w, H.n1_b, H.in_w, D, H.in_b, m->qkv, 3 * D, T, 3 * D, D),
-                                          s));
+    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n1_w, H.n1_b, T, u, s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_STORE, gemm(u, D, H.in_w, D, H.in_b, m->qkv, 3 * D, T, 3 * D, D), s));
     at.half_window = -1;
     JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, at, pl.n_work, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_ACT, E_RESID,
-                                          gemm(m->o, D, nullptr, nullptr, H.out_w, D, H.out_b, m->x, D, T, D, D), s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_RELU,
-                                          gemm(m->x, D, H.n2_w, H.n2_b, H.l1_w, D, H.l1_b, m->act, kHeadFfn, T,
-                                               kHeadFfn, D),
-                                          s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_ACT, E_RESID,
-                                          gemm(m->act, kHeadFfn, nullptr, nullptr, H.l2_w, kHeadFfn, H.l2_b, m->x, D,
-                                               T, D, kHeadFfn),
-                                          s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->o, D, H.out_w, D, H.out_b, m->x, D, T, D, D), s));
+    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n2_w, H.n2_b, T, u, s));
+    JL_LAUNCH(JL_K_HEAD_GEMM,
+              launch_gemm(bf, E_RELU, gemm(u, D, H.l1_w, D, H.l1_b, m->act, kHeadFfn, T, kHeadFfn, D), s));
+    JL_LAUNCH(JL_K_HEAD_GEMM,
+              launch_gemm(bf, E_RESID, gemm(m->act, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, m->x, D, T, D, kHeadFfn), s));
   }
   if (stop == 24) return copy_out(m->x, T);
 
@@ -702,13 +721,15 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   {
     const HeadW &H = m->H[1];
     char *kv = m->qkv;  // [T, 768]: k then v
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_STORE,
-                                          gemm(m->x, D, H.n1_w, H.n1_b, (const char *)H.in_w + (size_t)D * D * es, D,
-                                               H.in_b + D, kv, 2 * D, T, 2 * D, D),
+    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n1_w, H.n1_b, T, u, s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_STORE,
+                                          gemm(u, D, (const char *)H.in_w + (size_t)D * D * es, D, H.in_b + D, kv,
+                                               2 * D, T, 2 * D, D),
                                           s));
     JL_LAUNCH(JL_K_MISC, launch_gather_rows(m->x, pl.d_mp, M, m->z, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_STORE,
-                                          gemm(m->z, D, H.n1_w, H.n1_b, H.in_w, D, H.in_b, m->qm, D, M, D, D), s));
+    char *um = m->om;  // normalized marker rows, then the marker attention output
+    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->z, H.n1_w, H.n1_b, M, um, s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_STORE, gemm(um, D, H.in_w, D, H.in_b, m->qm, D, M, D, D), s));
     AttnArgs mk{};
     mk.q = m->qm;
     mk.q_stride = D;
@@ -720,22 +741,19 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     mk.work = pl.d_mw;
     mk.half_window = -1;
     JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, mk, pl.B, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_ACT, E_RESID,
-                                          gemm(m->om, D, nullptr, nullptr, H.out_w, D, H.out_b, m->z, D, M, D, D), s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_LN, E_RELU,
-                                          gemm(m->z, D, H.n2_w, H.n2_b, H.l1_w, D, H.l1_b, m->actm, kHeadFfn, M,
-                                               kHeadFfn, D),
-                                          s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, A_ACT, E_RESID,
-                                          gemm(m->actm, kHeadFfn, nullptr, nullptr, H.l2_w, kHeadFfn, H.l2_b, m->z, D,
-                                               M, D, kHeadFfn),
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->om, D, H.out_w, D, H.out_b, m->z, D, M, D, D), s));
+    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->z, H.n2_w, H.n2_b, M, um, s));
+    JL_LAUNCH(JL_K_HEAD_GEMM,
+              launch_gemm(bf, E_RELU, gemm(um, D, H.l1_w, D, H.l1_b, m->actm, kHeadFfn, M, kHeadFfn, D), s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID,
+                                          gemm(m->actm, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, m->z, D, M, D, kHeadFfn),
                                           s));
   }
   if (stop == 25) return copy_out(m->z, M);
 
   // scorer (FP32 in both modes)
-  JL_LAUNCH(JL_K_MISC, launch_gemm(bf, A_LN, E_GELU_F32,
-                                   gemm(m->z, D, m->sc_nw, m->sc_nb, m->sc_w1, D, m->sc_b1, m->sh, D, M, D, D), s));
+  JL_LAUNCH(JL_K_MISC, launch_ln_rows(false, m->z, m->sc_nw, m->sc_nb, M, m->zu, s));
+  JL_LAUNCH(JL_K_MISC, launch_gemm(bf, E_GELU_F32, gemm(m->zu, D, m->sc_w1, D, m->sc_b1, m->sh, D, M, D, D), s));
   JL_LAUNCH(JL_K_MISC, launch_score_dot(m->sh, m->sc_w2, m->sc_b2, M, out, s));
   return JL_OK;
 }
@@ -754,7 +772,7 @@ extern "C" int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *se
   hipStream_t s = (hipStream_t)stream;
   Plan pl;
   if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl)) return rc;
-  return run_forward(m, ids_dev, pl, 26, logits_dev, s);
+  return finish_plan(m, pl, s, run_forward(m, ids_dev, pl, 26, logits_dev, s));
 }
 
 extern "C" int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
@@ -770,7 +788,7 @@ extern "C" int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_
   hipStream_t s = (hipStream_t)stream;
   Plan pl;
   if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl)) return rc;
-  return run_forward(m, ids_dev, pl, stage, out_dev, s);
+  return finish_plan(m, pl, s, run_forward(m, ids_dev, pl, stage, out_dev, s));
 }
 
 extern "C" int jl_probs(jl_model *m, const float *logits_dev, const int32_t *seq_offsets, int32_t n_seqs,
@@ -785,9 +803,12 @@ extern "C" int jl_probs(jl_model *m, const float *logits_dev, const int32_t *seq
   hipStream_t s = (hipStream_t)stream;
   Plan pl;
   if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl)) return rc;
-  JL_LAUNCH(JL_K_MISC, launch_probs(logits_dev, pl.d_mo, pl.d_qt, n_seqs, probs_dev, answer_dev, argmax_dev,
-                                    maxprob_dev, s));
-  return JL_OK;
+  auto launch = [&]() -> int {
+    JL_LAUNCH(JL_K_MISC, launch_probs(logits_dev, pl.d_mo, pl.d_qt, n_seqs, probs_dev, answer_dev, argmax_dev,
+                                      maxprob_dev, s));
+    return JL_OK;
+  };
+  return finish_plan(m, pl, s, launch());
 }
 
 extern "C" int jl_profile(jl_model *m, int enable, uint32_t class_mask) {

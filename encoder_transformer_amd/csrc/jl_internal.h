@@ -24,15 +24,12 @@ constexpr float kLnEps = 1e-5f;
 // A layer is global when its index is a multiple of 3 (layers 0, 3, ..., 21).
 inline bool layer_is_global(int l) { return l % 3 == 0; }
 
-enum AMode { A_ACT = 0, A_LN = 1 };                    // GEMM A-operand source
 enum EMode { E_STORE = 0, E_RESID = 1, E_GEGLU = 2, E_RELU = 3, E_GELU_F32 = 4 };
 
-// C[M, N] = A[M, K] . W[N, K]^T with a fused prologue (A_LN) and epilogue.
+// C[M, N] = A[M, K] . W[N, K]^T with a fused epilogue.
 struct GemmArgs {
-  const void *A;        // A_ACT: element matrix [M, lda]; A_LN: FP32 [M, lda], K == 384
+  const void *A;        // element matrix [M, lda]
   int lda;
-  const float *ln_g;    // A_LN: LayerNorm gain (nullptr: no normalization)
-  const float *ln_b;    // A_LN: LayerNorm shift (nullptr: none)
   const void *W;        // element matrix [N, ldw] (GEGLU: rows interleaved by 16)
   int ldw;
   const float *bias;    // [N] or nullptr
@@ -67,7 +64,9 @@ struct AttnArgs {
 hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain, int T,
                         const int *seq_offsets, int n_seqs, float *x, int *pos, int *tok_seq,
                         hipStream_t s);
-hipError_t launch_gemm(bool bf16, int amode, int emode, const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm(bool bf16, int emode, const GemmArgs &a, hipStream_t s);
+hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, const float *shift, int n, void *out,
+                          hipStream_t s);
 hipError_t launch_attention(bool bf16, const AttnArgs &a, int n_work, hipStream_t s);
 hipError_t launch_final_ln_type(const float *x, const float *gain, const float *type_rows,
                                 const int *qtype, const int *tok_seq, int T, float *h,

@@ -127,14 +127,16 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// GEMM: C = A . W^T, 256 threads as 2 x 2 waves, wave tile (BM/2) x 64
+// GEMM: C = A . W^T, 256 threads as 2 x 2 waves, wave tile (BM/2) x 64.
+// A is an element matrix (LayerNorm, where the model has one, is applied by
+// ln_rows_kernel beforehand, once per row).
 // ---------------------------------------------------------------------------
 
 template <typename T> struct LdsStride;            // padded row strides: conflict-free
 template <> struct LdsStride<bf16> { static constexpr int v = 40; };   // 80 B rows
 template <> struct LdsStride<float> { static constexpr int v = 36; };  // 144 B rows
 
-template <typename T, int BM, int AM, int EM>
+template <typename T, int BM, int EM>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   constexpr int BN = 128, BK = 32, WN = 2;
   constexpr int TM = BM / 2, TN = BN / WN;
@@ -145,33 +147,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   static_assert(NT == 4, "epilogues assume 64 columns per wave");
   __shared__ __attribute__((aligned(16))) T sA[2][BM * LS];
   __shared__ __attribute__((aligned(16))) T sB[2][BN * LS];
-  __shared__ float sMean[BM], sRstd[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int M = g.M;
-
-  const bool do_ln = (AM == A_LN) && g.ln_g != nullptr;
-  if (do_ln) {
-    for (int r = wave; r < BM; r += 4) {
-      const int row = m0 + r;
-      float mean = 0.f, rstd = 0.f;
-      if (row < M) {
-        const float *xr = (const float *)g.A + (size_t)row * g.lda;
-        float v[6], s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 6; ++i) { v[i] = xr[lane + 64 * i]; s += v[i]; }
-        mean = wave_sum(s) * (1.0f / kWidth);
-        float q = 0.f;
-#pragma unroll
-        for (int i = 0; i < 6; ++i) { const float d = v[i] - mean; q += d * d; }
-        rstd = rsqrtf(wave_sum(q) * (1.0f / kWidth) + kLnEps);
-      }
-      if (lane == 0) { sMean[r] = mean; sRstd[r] = rstd; }
-    }
-    __syncthreads();
-  }
 
   Frag<T> ra[A_CH], rb[B_CH];
   auto load_tiles = [&](int kt) {
@@ -180,23 +160,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     for (int c = 0; c < A_CH; ++c) {
       const int idx = tid + c * 256, r = idx >> 2, kc = (idx & 3) * 8;
       const int row = min(m0 + r, M - 1);
-      if (AM == A_ACT) {
-        ra[c] = load_frag((const T *)g.A + (size_t)row * g.lda + k0 + kc);
-      } else {
-        const float *src = (const float *)g.A + (size_t)row * g.lda + k0 + kc;
-        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(src);
-        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(src + 4);
-        float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        if (do_ln) {
-          const float mu = sMean[r], rs = sRstd[r];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            v[e] = (v[e] - mu) * rs * g.ln_g[k0 + kc + e];
-            if (g.ln_b) v[e] += g.ln_b[k0 + kc + e];
-          }
-        }
-        frag_from(ra[c], v);
-      }
+      ra[c] = load_frag((const T *)g.A + (size_t)row * g.lda + k0 + kc);
     }
 #pragma unroll
     for (int c = 0; c < B_CH; ++c) {
@@ -481,6 +445,41 @@ __global__ __launch_bounds__(256) void final_ln_type_kernel(const float *x, cons
   }
 }
 
+// out[t] = LayerNorm(x[t]; gain, shift) as the GEMM element type; gain == nullptr
+// copies x unchanged (the first layer's identity pre-norm).
+template <typename T>
+__global__ __launch_bounds__(256) void ln_rows_kernel(const float *__restrict__ x, const float *__restrict__ gain,
+                                                      const float *__restrict__ shift, int n, T *__restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n) return;
+  const float *xr = x + (size_t)t * kWidth;
+  float v[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) v[i] = xr[lane + 64 * i];
+  T *o = out + (size_t)t * kWidth;
+  if (gain == nullptr) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) o[lane + 64 * i] = to_elem<T>(v[i]);
+    return;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) s += v[i];
+  const float mean = wave_sum(s) * (1.0f / kWidth);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) { const float d = v[i] - mean; q += d * d; }
+  const float rstd = rsqrtf(wave_sum(q) * (1.0f / kWidth) + kLnEps);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int c = lane + 64 * i;
+    float y = (v[i] - mean) * rstd * gain[c];
+    if (shift) y += shift[c];
+    o[c] = to_elem<T>(y);
+  }
+}
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const float *__restrict__ src,
                                                           const int *__restrict__ rows, int n,
                                                           float *__restrict__ dst) {
@@ -554,29 +553,34 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
 }
 
 template <typename T, int BM>
-static hipError_t gemm_dispatch(int amode, int emode, const GemmArgs &a, hipStream_t s) {
+static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
   const dim3 grid(a.N / 128, (a.M + BM - 1) / BM);
-#define JL_GEMM(AM, EM)                                                  \
-  if (amode == AM && emode == EM) {                                      \
-    gemm_kernel<T, BM, AM, EM><<<grid, 256, 0, s>>>(a);                  \
-    return hipGetLastError();                                            \
+  switch (emode) {
+    case E_STORE: gemm_kernel<T, BM, E_STORE><<<grid, 256, 0, s>>>(a); break;
+    case E_RESID: gemm_kernel<T, BM, E_RESID><<<grid, 256, 0, s>>>(a); break;
+    case E_GEGLU: gemm_kernel<T, BM, E_GEGLU><<<grid, 256, 0, s>>>(a); break;
+    case E_RELU: gemm_kernel<T, BM, E_RELU><<<grid, 256, 0, s>>>(a); break;
+    case E_GELU_F32: gemm_kernel<T, BM, E_GELU_F32><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
   }
-  JL_GEMM(A_LN, E_STORE)
-  JL_GEMM(A_ACT, E_RESID)
-  JL_GEMM(A_LN, E_GEGLU)
-  JL_GEMM(A_LN, E_RELU)
-  JL_GEMM(A_LN, E_GELU_F32)
-#undef JL_GEMM
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
-hipError_t launch_gemm(bool bf16_mode, int amode, int emode, const GemmArgs &a, hipStream_t s) {
+hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  if (a.N % 128 != 0 || a.K % 32 != 0 || (amode == A_LN && a.K != kWidth)) return hipErrorInvalidValue;
+  if (a.N % 128 != 0 || a.K % 32 != 0) return hipErrorInvalidValue;
   const bool big = (long)((a.M + 127) / 128) * (a.N / 128) >= 512;
   if (bf16_mode && emode != E_GELU_F32)
-    return big ? gemm_dispatch<bf16, 128>(amode, emode, a, s) : gemm_dispatch<bf16, 64>(amode, emode, a, s);
-  return big ? gemm_dispatch<float, 128>(amode, emode, a, s) : gemm_dispatch<float, 64>(amode, emode, a, s);
+    return big ? gemm_dispatch<bf16, 128>(emode, a, s) : gemm_dispatch<bf16, 64>(emode, a, s);
+  return big ? gemm_dispatch<float, 128>(emode, a, s) : gemm_dispatch<float, 64>(emode, a, s);
+}
+
+hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, const float *shift, int n, void *out,
+                          hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (bf16_out) ln_rows_kernel<bf16><<<(n + 3) / 4, 256, 0, s>>>(x, gain, shift, n, (bf16 *)out);
+  else ln_rows_kernel<float><<<(n + 3) / 4, 256, 0, s>>>(x, gain, shift, n, (float *)out);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(bool bf16_mode, const AttnArgs &a, int n_work, hipStream_t s) {

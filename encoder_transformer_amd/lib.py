@@ -22,9 +22,11 @@ OK, ERR_ARG, ERR_OPTIONS, ERR_LENGTH, ERR_QTYPE, ERR_FILE, ERR_DEVICE, ERR_OOM, 
     0, -1, -2, -3, -4, -5, -6, -7, -8)
 STATUS_NAMES = {0: "OK", -1: "ARG", -2: "OPTIONS", -3: "LENGTH", -4: "QTYPE", -5: "FILE",
                 -6: "DEVICE", -7: "OOM", -8: "CAPACITY"}
-K_EMBED, K_QKV, K_ATTN_GLOBAL, K_ATTN_LOCAL, K_OUTPROJ, K_MLP_IN, K_MLP_OUT, K_HEAD_GEMM, K_HEAD_ATTN, K_MISC = range(10)
+(K_EMBED, K_QKV, K_ATTN_GLOBAL, K_ATTN_LOCAL, K_OUTPROJ, K_MLP_IN, K_MLP_OUT, K_HEAD_GEMM, K_HEAD_ATTN,
+ K_MISC, K_LN) = range(11)
 KERNEL_CLASS_NAMES = ["embed", "qkv", "attn_global", "attn_local", "outproj", "mlp_in", "mlp_out",
-                      "head_gemm", "head_attn", "misc"]
+                      "head_gemm", "head_attn", "misc", "ln"]
+N_KERNEL_CLASSES = len(KERNEL_CLASS_NAMES)
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _f32p = ctypes.POINTER(ctypes.c_float)
@@ -45,6 +47,10 @@ def load_library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built: run `python -m encoder_transformer_amd.build`")
+    # PyTorch ships its own HIP runtime with the same soname (libamdhip64.so.7).
+    # Loading torch first makes libjl bind to that one runtime instance, so the
+    # streams and device pointers torch hands over are valid in libjl.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.jl_last_error.restype = ctypes.c_char_p
@@ -173,7 +179,7 @@ class Model:
                                          self._stream(stream)))
         return out
 
-    def profile(self, enable: bool, class_mask: int = 0x3FF):
+    def profile(self, enable: bool, class_mask: int = (1 << N_KERNEL_CLASSES) - 1):
         _check(self._lib.jl_profile(self._h, int(enable), class_mask))
 
     def profile_read(self, kernel_class: int):

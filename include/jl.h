@@ -136,16 +136,17 @@ int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offs
 /* Kernel classes reported by the per-kernel timer. */
 enum jl_kernel_class {
   JL_K_EMBED = 0,      /* embedding gather + LayerNorm                         */
-  JL_K_QKV = 1,        /* encoder QKV GEMM (LayerNorm on load, RoPE on store)   */
+  JL_K_QKV = 1,        /* encoder QKV GEMM (RoPE on store)                      */
   JL_K_ATTN_GLOBAL = 2,/* encoder attention, global layers                      */
   JL_K_ATTN_LOCAL = 3, /* encoder attention, +-64 window layers                 */
   JL_K_OUTPROJ = 4,    /* encoder out-projection GEMM + residual                */
-  JL_K_MLP_IN = 5,     /* encoder Wi GEMM (LayerNorm on load) + GEGLU           */
+  JL_K_MLP_IN = 5,     /* encoder Wi GEMM + GEGLU                               */
   JL_K_MLP_OUT = 6,    /* encoder Wo GEMM + residual                            */
   JL_K_HEAD_GEMM = 7,  /* decision-head GEMMs                                   */
   JL_K_HEAD_ATTN = 8,  /* decision-head attention                               */
   JL_K_MISC = 9,       /* final LayerNorm + type row, gathers, scorer, softmax  */
-  JL_K_NCLASS = 10
+  JL_K_LN = 10,        /* LayerNorm rows -> GEMM operand                        */
+  JL_K_NCLASS = 11
 };
 
 /* Turn the per-kernel timer on (1) or off (0); it brackets every launch of
