@@ -29,6 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_FP32_TFLOPS = 157.3
 HBM_GBPS = 8000.0
 D, FFN_HEAD = 384, 1536
+ROW_BLOCK_MIN_TOKENS = 8192  # bf16 batches this large use the row-block layer kernel
 
 
 def band_pairs(L, w=64):
@@ -36,30 +37,32 @@ def band_pairs(L, w=64):
     return int(np.sum(np.minimum(L - 1, p + w) - np.maximum(0, p - w) + 1))
 
 
-def class_flops(batch):
-    """Algorithmic FLOPs per step of each kernel class (masked work not counted)."""
+def class_flops(batch, row_block):
+    """Algorithmic FLOPs per step of each kernel class (masked work not counted).
+
+    `row_block`: the bf16 path for large batches, where one layer kernel per
+    layer runs the out-projection, the MLP and the next layer's QKV.
+    """
     lens = np.diff(batch.seq_offsets).astype(np.int64)
     T, M = int(lens.sum()), batch.n_markers
     glob = int(np.sum(lens * lens))
     band = sum(band_pairs(int(L)) for L in lens)
-    f = {
-        "qkv": 22 * 2 * T * D * 3 * D,
-        "outproj": 22 * 2 * T * D * D,
-        "mlp_in": 22 * 2 * T * D * 2304,
-        "mlp_out": 22 * 2 * T * 1152 * D,
-        "attn_global": 8 * 1536 * glob,
-        "attn_local": 14 * 1536 * band,
-        # head layer 1 on every token, layer 2 keys/values on every token and
-        # the rest on marker rows, attention of marker queries over their sequence
-        "head_gemm": 2 * T * D * (3 * D + D + 2 * FFN_HEAD) + 2 * T * D * 2 * D
-                     + 2 * M * D * (D + D + 2 * FFN_HEAD),
-        "head_attn": 1536 * glob + 1536 * int(sum(len(batch.sequence(b)[1]) * lens[b]
-                                                  for b in range(batch.n_seqs))),
-        "misc": 2 * M * D * D + 2 * M * D,
-        "ln": 0, "embed": 0,
-    }
-    launches = {"qkv": 22, "outproj": 22, "mlp_in": 22, "mlp_out": 22, "attn_global": 8, "attn_local": 14}
-    return f, launches
+    qkv, outp, mlp_in, mlp_out = 2 * T * D * 3 * D, 2 * T * D * D, 2 * T * D * 2304, 2 * T * 1152 * D
+    f = {k: 0 for k in ("embed", "qkv", "outproj", "mlp_in", "mlp_out", "layer", "ln")}
+    if row_block:
+        f["qkv"] = qkv
+        f["layer"] = 22 * (outp + mlp_in + mlp_out) + 21 * qkv
+    else:
+        f.update(qkv=22 * qkv, outproj=22 * outp, mlp_in=22 * mlp_in, mlp_out=22 * mlp_out)
+    f["attn_global"] = 8 * 1536 * glob
+    f["attn_local"] = 14 * 1536 * band
+    # head layer 1 on every token, layer 2 keys/values on every token and the
+    # rest on marker rows, attention of marker queries over their sequence
+    f["head_gemm"] = (2 * T * D * (3 * D + D + 2 * FFN_HEAD) + 2 * T * D * 2 * D
+                      + 2 * M * D * (D + D + 2 * FFN_HEAD))
+    f["head_attn"] = 1536 * glob + 1536 * int(sum(len(batch.sequence(b)[1]) * lens[b] for b in range(batch.n_seqs)))
+    f["misc"] = 2 * M * D * D + 2 * M * D
+    return f
 
 
 def time_workload(model, batch, steps, warmup, profile_class=None):
@@ -131,7 +134,7 @@ def main():
     b2 = synth.make_batch(2)
     t, dom, dom_ms, dom_n, per_class = time_workload(model, b2, args.steps, args.warmup)
     ms_step = 1e3 * t / args.steps
-    flops, launches = class_flops(b2)
+    flops = class_flops(b2, row_block=b2.n_tokens >= ROW_BLOCK_MIN_TOKENS)
     total_flops = sum(flops.values())
     dom_flops_step = flops[dom]
     achieved = dom_flops_step * args.steps / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
@@ -164,7 +167,7 @@ def main():
         for name, cfg, st in [("16x8192", 3, 5), ("ragged256", 4, 5)]:
             b = synth.make_batch(cfg)
             tt, d, dms, dn, _ = time_workload(model, b, st, 2)
-            fl = sum(class_flops(b)[0].values())
+            fl = sum(class_flops(b, row_block=b.n_tokens >= ROW_BLOCK_MIN_TOKENS).values())
             extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2),
                            "tokens_per_s": round(b.n_tokens * st / tt, 1),
                            "step_mfma_frac": round(fl / (tt / st) / 1e12 / PEAK_BF16_TFLOPS, 4),

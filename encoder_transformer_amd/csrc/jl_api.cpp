@@ -24,6 +24,10 @@ using namespace jl;
 
 namespace {
 
+// Default: batches of at least this many tokens (bf16) take the row-block
+// layer kernel (one work-group per 64 rows: 8,192 tokens give 128 of them).
+constexpr int64_t kRowBlockMinTokens = 8192;
+
 thread_local std::string g_err;
 
 int fail(int code, const std::string &msg) {
@@ -56,10 +60,30 @@ uint16_t f32_to_bf16(float f) {  // round to nearest even; NaN stays NaN
   return (uint16_t)(u >> 16);
 }
 
+// Matrix-core fragment order of a row-major W [N, K] (rows = output columns):
+// block (gn, s) holds 64 lanes x 8 bf16, lane l element e = W[16 gn + l % 16]
+// [32 s + 8 (l / 16) + e]; blocks are stored gn-major (index gn * K/32 + s), so a
+// wave's B fragment for 16 output columns and 32 k is one contiguous 1 KB load.
+// `row_of` maps packed row -> source row (GEGLU interleave), or nullptr.
+void pack_fragments(const float *W, int N, int K, const std::vector<int> *row_of, uint16_t *out) {
+  const int ks = K / 32;
+  for (int gn = 0; gn < N / 16; ++gn)
+    for (int s = 0; s < ks; ++s) {
+      uint16_t *blk = out + ((size_t)gn * ks + s) * 512;
+      for (int l = 0; l < 64; ++l) {
+        const int r = 16 * gn + (l & 15);
+        const float *src = W + (size_t)(row_of ? (*row_of)[r] : r) * K + 32 * s + 8 * (l >> 4);
+        for (int e = 0; e < 8; ++e) blk[l * 8 + e] = f32_to_bf16(src[e]);
+      }
+    }
+}
+
 struct LayerW {
   const float *attn_norm = nullptr;
   const void *Wqkv = nullptr, *Wo = nullptr, *Wi = nullptr, *Wout = nullptr;
   const float *mlp_norm = nullptr;
+  // bf16 fragment-ordered copies for the row-block layer kernel
+  const void *pWqkv = nullptr, *pWo = nullptr, *pWi = nullptr, *pWout = nullptr;
 };
 struct HeadW {
   const void *in_w = nullptr, *out_w = nullptr, *l1_w = nullptr, *l2_w = nullptr;
@@ -80,6 +104,7 @@ struct jl_model {
   bool bf16 = true;
   size_t esize = 2;
   int64_t max_tokens = 0, max_markers = 0, max_seqs = 0;
+  int64_t row_block_min_tokens = 8192;
 
   char *warena = nullptr;
   size_t wbytes = 0;
@@ -331,6 +356,12 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     pend.push_back({dst, off});
   };
 
+  auto put_packed = [&](const float *src, int rows, int cols, const void **dst, const std::vector<int> *row_of) {
+    const size_t off = ar.add((size_t)rows * cols * 2);
+    pack_fragments(src, rows, cols, row_of, (uint16_t *)(ar.buf.data() + off));
+    pend.push_back({dst, off});
+  };
+
   jl_model *m = new jl_model();
   m->device = device;
   m->precision = precision;
@@ -339,6 +370,7 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
   m->max_tokens = max_tokens;
   m->max_markers = max_markers;
   m->max_seqs = std::min<int64_t>(max_tokens, max_markers / 2);
+  m->row_block_min_tokens = kRowBlockMinTokens;
 
   const uint32_t D = kWidth;
   const float *t = nullptr;
@@ -367,14 +399,18 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     }
     GET(p + "attn.Wqkv.weight", 3 * D, D);
     put_elem(t, 3 * D, D, &m->L[l].Wqkv, nullptr);
+    if (bf) put_packed(t, 3 * D, D, &m->L[l].pWqkv, nullptr);
     GET(p + "attn.Wo.weight", D, D);
     put_elem(t, D, D, &m->L[l].Wo, nullptr);
+    if (bf) put_packed(t, D, D, &m->L[l].pWo, nullptr);
     GET(p + "mlp_norm.weight", D);
     put_f32(t, D, &m->L[l].mlp_norm);
     GET(p + "mlp.Wi.weight", 2 * kGeglu, D);
     put_elem(t, 2 * kGeglu, D, &m->L[l].Wi, &geglu_rows);
+    if (bf) put_packed(t, 2 * kGeglu, D, &m->L[l].pWi, &geglu_rows);
     GET(p + "mlp.Wo.weight", D, kGeglu);
     put_elem(t, D, kGeglu, &m->L[l].Wout, nullptr);
+    if (bf) put_packed(t, D, kGeglu, &m->L[l].pWout, nullptr);
   }
   GET("final_norm.weight", D);
   put_f32(t, D, &m->final_norm);
@@ -494,6 +530,13 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
       return bail(JL_ERR_DEVICE, "cannot create an event");
   }
   *out = m;
+  return JL_OK;
+}
+
+extern "C" int jl_set_row_block_min_tokens(jl_model *m, int64_t min_tokens) {
+  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (min_tokens < 0) return fail(JL_ERR_ARG, "min_tokens must be >= 0");
+  m->row_block_min_tokens = min_tokens;
   return JL_OK;
 }
 
@@ -678,6 +721,49 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   at.o = m->o;
   at.o_stride = D;
   at.work = pl.d_aw;
+  if (bf && T >= m->row_block_min_tokens) {
+    // Row-block path: one attention launch and one layer launch per layer.
+    {
+      const LayerW &W0 = m->L[0];
+      JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, nullptr, nullptr, T, u, s));
+      GemmArgs q = gemm(u, D, W0.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D);
+      q.rope_cos = m->rope_cos[1];
+      q.rope_sin = m->rope_sin[1];
+      q.pos = m->pos;
+      q.rope_cols = 2 * D;
+      JL_LAUNCH(JL_K_QKV, launch_gemm(bf, E_STORE, q, s));
+    }
+    for (int l = 0; l < kLayers; ++l) {
+      const bool glob = layer_is_global(l);
+      at.half_window = glob ? -1 : kHalfWindow;
+      JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, launch_attention(bf, at, pl.n_work, s));
+      LayerArgs la{};
+      const LayerW &W = m->L[l];
+      la.x = m->x;
+      la.o = (const __bf16 *)m->o;
+      la.Wo = (const __bf16 *)W.pWo;
+      la.mlp_norm = W.mlp_norm;
+      la.Wi = (const __bf16 *)W.pWi;
+      la.Wout = (const __bf16 *)W.pWout;
+      la.pos = m->pos;
+      la.qkv_out = (__bf16 *)m->qkv;
+      la.T = T;
+      if (l + 1 < kLayers && stop != l + 1) {
+        const LayerW &N = m->L[l + 1];
+        la.attn_norm_next = N.attn_norm;
+        la.Wqkv_next = (const __bf16 *)N.pWqkv;
+        la.rope_cos_next = m->rope_cos[layer_is_global(l + 1)];
+        la.rope_sin_next = m->rope_sin[layer_is_global(l + 1)];
+      } else if (l + 1 == kLayers && stop != kLayers) {
+        la.final_norm = m->final_norm;
+        la.type_rows = m->type_rows;
+        la.qtype = pl.d_qt;
+        la.tok_seq = m->tok_seq;
+      }
+      JL_LAUNCH(JL_K_LAYER, launch_layer(la, s));
+      if (stop == l + 1) return copy_out(m->x, T);
+    }
+  } else {
   for (int l = 0; l < kLayers; ++l) {
     const LayerW &W = m->L[l];
     const bool glob = layer_is_global(l);
@@ -699,6 +785,7 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   }
   // head input: final LayerNorm + type row (in place)
   JL_LAUNCH(JL_K_MISC, launch_final_ln_type(m->x, m->final_norm, m->type_rows, pl.d_qt, m->tok_seq, T, m->x, s));
+  }
   if (stop == 23) return copy_out(m->x, T);
 
   // head layer 1 over every token

@@ -1,0 +1,86 @@
+// Device helpers shared by the kernel translation units of libjl (gfx950).
+#pragma once
+
+#include "jl_internal.h"
+
+#include <math.h>
+
+namespace jl {
+namespace dev {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// fragments and matrix-core steps
+// ---------------------------------------------------------------------------
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+__device__ inline Frag<bf16> load_frag(const bf16 *p) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8 *>(p);
+  return f;
+}
+__device__ inline Frag<float> load_frag(const float *p) {
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4 *>(p);
+  f.hi = *reinterpret_cast<const f32x4 *>(p + 4);
+  return f;
+}
+__device__ inline void store_frag(bf16 *p, const Frag<bf16> &f) {
+  *reinterpret_cast<bf16x8 *>(p) = f.v;
+}
+__device__ inline void store_frag(float *p, const Frag<float> &f) {
+  *reinterpret_cast<f32x4 *>(p) = f.lo;
+  *reinterpret_cast<f32x4 *>(p + 4) = f.hi;
+}
+__device__ inline float frag_get(const Frag<bf16> &f, int e) { return (float)f.v[e]; }
+__device__ inline float frag_get(const Frag<float> &f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
+
+// Build a fragment from 8 FP32 values (bf16: round to nearest even).
+__device__ inline void frag_from(Frag<bf16> &f, const float *v) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)v[e];
+}
+__device__ inline void frag_from(Frag<float> &f, const float *v) {
+  f.lo = f32x4{v[0], v[1], v[2], v[3]};
+  f.hi = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// acc[16x16] += A(16 x 32) . B(32 x 16); lane (i + 16g) supplies A row i and
+// B column i at k = 8g .. 8g+7.
+__device__ inline void mfma(f32x4 &acc, const Frag<bf16> &a, const Frag<bf16> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ inline void mfma(f32x4 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], acc, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], acc, 0, 0, 0);
+}
+
+template <typename T> __device__ inline T to_elem(float v);
+template <> __device__ inline bf16 to_elem<bf16>(float v) { return (bf16)v; }
+template <> __device__ inline float to_elem<float>(float v) { return v; }
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ inline float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+
+}  // namespace dev
+}  // namespace jl

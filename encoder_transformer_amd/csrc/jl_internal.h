@@ -20,6 +20,7 @@ constexpr int kMaxSeq = 8192;
 constexpr double kThetaLocal = 10000.0;
 constexpr double kThetaGlobal = 160000.0;
 constexpr float kLnEps = 1e-5f;
+constexpr int kLayerRows = 64;      // rows per work-group of the row-block layer kernel
 
 // A layer is global when its index is a multiple of 3 (layers 0, 3, ..., 21).
 inline bool layer_is_global(int l) { return l % 3 == 0; }
@@ -60,7 +61,31 @@ struct AttnArgs {
   int half_window;                  // < 0: attend to the whole sequence
 };
 
-// Launchers (kernels.hip).  `bf16` selects the bf16 instantiation, else FP32.
+// Row-block layer kernel (bf16 only): out-projection + residual, LayerNorm,
+// GEGLU MLP + residual, then the next layer's LayerNorm + QKV (+RoPE), or the
+// final LayerNorm + type row after the last layer.  Weight matrices here are
+// in matrix-core fragment order (see pack_fragments in jl_api.cpp).
+struct LayerArgs {
+  float *x;                     // [T, 384] residual stream (updated in place)
+  const __bf16 *o;              // [T, 384] attention output of this layer
+  const __bf16 *Wo;             // fragment-packed [384 x 384]
+  const float *mlp_norm;        // [384]
+  const __bf16 *Wi;             // fragment-packed [2304 x 384], GEGLU rows interleaved by 16
+  const __bf16 *Wout;           // fragment-packed [384 x 1152]
+  const float *attn_norm_next;  // next layer's attention pre-norm gain
+  const __bf16 *Wqkv_next;      // fragment-packed [1152 x 384]; nullptr after the last layer
+                                // (with final_norm == nullptr too: store the residual only)
+  const float *rope_cos_next, *rope_sin_next;
+  const int *pos;               // [T] position inside the sequence
+  __bf16 *qkv_out;              // [T, 1152]
+  const float *final_norm;      // after the last layer: final LayerNorm gain,
+  const float *type_rows;       //   type table [3, 384],
+  const int *qtype;             //   question type per sequence,
+  const int *tok_seq;           //   sequence of each token
+  int T;
+};
+
+// Launchers (kernels.hip, layer.hip).  `bf16` selects the bf16 instantiation, else FP32.
 hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain, int T,
                         const int *seq_offsets, int n_seqs, float *x, int *pos, int *tok_seq,
                         hipStream_t s);
@@ -68,6 +93,7 @@ hipError_t launch_gemm(bool bf16, int emode, const GemmArgs &a, hipStream_t s);
 hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, const float *shift, int n, void *out,
                           hipStream_t s);
 hipError_t launch_attention(bool bf16, const AttnArgs &a, int n_work, hipStream_t s);
+hipError_t launch_layer(const LayerArgs &a, hipStream_t s);
 hipError_t launch_final_ln_type(const float *x, const float *gain, const float *type_rows,
                                 const int *qtype, const int *tok_seq, int T, float *h,
                                 hipStream_t s);

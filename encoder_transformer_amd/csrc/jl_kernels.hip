@@ -7,86 +7,17 @@
 // feeds the same fragment to eight 16x16x4 steps, so one tiling serves both.
 // Row-wise work (LayerNorm, softmax over options, dot products) uses
 // wavefront reductions.
-#include "jl_internal.h"
+#include "jl_device.h"
 
-#include <math.h>
+// No FMA contraction: unrolled code handles each row of a tile in its own
+// instruction sequence, and a contraction the compiler applies to some of
+// those sequences and not to others would make a row's rounding depend on
+// its place in the tile, and so on how the batch was packed.
+#pragma clang fp contract(off)
 
 namespace jl {
 namespace {
-
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-// ---------------------------------------------------------------------------
-// fragments and matrix-core steps
-// ---------------------------------------------------------------------------
-
-template <typename T> struct Frag;
-template <> struct Frag<bf16> { bf16x8 v; };
-template <> struct Frag<float> { f32x4 lo, hi; };
-
-__device__ inline Frag<bf16> load_frag(const bf16 *p) {
-  Frag<bf16> f;
-  f.v = *reinterpret_cast<const bf16x8 *>(p);
-  return f;
-}
-__device__ inline Frag<float> load_frag(const float *p) {
-  Frag<float> f;
-  f.lo = *reinterpret_cast<const f32x4 *>(p);
-  f.hi = *reinterpret_cast<const f32x4 *>(p + 4);
-  return f;
-}
-__device__ inline void store_frag(bf16 *p, const Frag<bf16> &f) {
-  *reinterpret_cast<bf16x8 *>(p) = f.v;
-}
-__device__ inline void store_frag(float *p, const Frag<float> &f) {
-  *reinterpret_cast<f32x4 *>(p) = f.lo;
-  *reinterpret_cast<f32x4 *>(p + 4) = f.hi;
-}
-__device__ inline float frag_get(const Frag<bf16> &f, int e) { return (float)f.v[e]; }
-__device__ inline float frag_get(const Frag<float> &f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
-
-// Build a fragment from 8 FP32 values (bf16: round to nearest even).
-__device__ inline void frag_from(Frag<bf16> &f, const float *v) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)v[e];
-}
-__device__ inline void frag_from(Frag<float> &f, const float *v) {
-  f.lo = f32x4{v[0], v[1], v[2], v[3]};
-  f.hi = f32x4{v[4], v[5], v[6], v[7]};
-}
-
-// acc[16x16] += A(16 x 32) . B(32 x 16); lane (i + 16g) supplies A row i and
-// B column i at k = 8g .. 8g+7.
-__device__ inline void mfma(f32x4 &acc, const Frag<bf16> &a, const Frag<bf16> &b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
-}
-__device__ inline void mfma(f32x4 &acc, const Frag<float> &a, const Frag<float> &b) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], acc, 0, 0, 0);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], acc, 0, 0, 0);
-}
-
-template <typename T> __device__ inline T to_elem(float v);
-template <> __device__ inline bf16 to_elem<bf16>(float v) { return (bf16)v; }
-template <> __device__ inline float to_elem<float>(float v) { return v; }
-
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ inline float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+using namespace dev;
 
 // ---------------------------------------------------------------------------
 // embedding gather + LayerNorm (gain only); positions and sequence ids
@@ -127,58 +58,75 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// GEMM: C = A . W^T, 256 threads as 2 x 2 waves, wave tile (BM/2) x 64.
-// A is an element matrix (LayerNorm, where the model has one, is applied by
-// ln_rows_kernel beforehand, once per row).
+// GEMM: C = A . W^T (A [M, K] activations, W [N, K] weights, both K-contiguous).
+//
+// 256 threads as 2 x 2 waves; block tile BM x BN, wave tile (BM/2) x (BN/2),
+// K staged in steps of BK (64 bf16 / 32 FP32 elements) through a double-
+// buffered LDS tile.  LDS holds the tiles in matrix-core fragment order: one
+// block of 64 lanes x 8 elements covers 16 rows x 32 k, lane (r + 16 c) holding
+// row r, k = 8c .. 8c+7.  A wave stages one such block per global load (16
+// rows x 64 contiguous bytes), writes it to LDS linearly and every fragment
+// read is one linear 16-byte read per lane: no bank conflicts either way.
+// LayerNorm, where the model has one, is applied beforehand by
+// ln_rows_kernel, once per row.
+//
+// The grid is 1-D.  Work-groups are dispatched to the 8 XCDs round-robin, so
+// block b is remapped to tile t such that every XCD owns a contiguous run of
+// tiles: all N-tiles of an M-block then share one XCD's L2.
 // ---------------------------------------------------------------------------
 
-template <typename T> struct LdsStride;            // padded row strides: conflict-free
-template <> struct LdsStride<bf16> { static constexpr int v = 40; };   // 80 B rows
-template <> struct LdsStride<float> { static constexpr int v = 36; };  // 144 B rows
+template <typename T> struct GemmBK;
+template <> struct GemmBK<bf16> { static constexpr int v = 64; };
+template <> struct GemmBK<float> { static constexpr int v = 32; };
 
-template <typename T, int BM, int EM>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  constexpr int BN = 128, BK = 32, WN = 2;
-  constexpr int TM = BM / 2, TN = BN / WN;
+__device__ inline int xcd_tile(int b, int n_tiles) {
+  const int per = n_tiles >> 3, rem = n_tiles & 7, x = b & 7, local = b >> 3;
+  return x * per + min(x, rem) + local;
+}
+
+template <typename T, int BM, int BN, int EM>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int n_tiles) {
+  constexpr int BK = GemmBK<T>::v, KS = BK / 32;           // 32-wide k sub-steps per stage
+  constexpr int TM = BM / 2, TN = BN / 2;                   // wave tile
   constexpr int MT = TM / 16, NT = TN / 16;
-  constexpr int LS = LdsStride<T>::v;
-  constexpr int A_CH = BM * BK / 8 / 256;
-  constexpr int B_CH = BN * BK / 8 / 256;
-  static_assert(NT == 4, "epilogues assume 64 columns per wave");
-  __shared__ __attribute__((aligned(16))) T sA[2][BM * LS];
-  __shared__ __attribute__((aligned(16))) T sB[2][BN * LS];
+  constexpr int FE = 8;                                      // elements per lane per fragment
+  constexpr int BLK = 64 * FE;                               // elements per fragment block
+  constexpr int A_BLKS = (BM / 16) * KS, B_BLKS = (BN / 16) * KS;
+  constexpr int A_PER_WAVE = A_BLKS / 4, B_PER_WAVE = B_BLKS / 4;
+  static_assert(A_BLKS % 4 == 0 && B_BLKS % 4 == 0, "tile must split over 4 waves");
+  static_assert(NT % 4 == 0, "epilogues pair columns within 64-column groups");
+  __shared__ __attribute__((aligned(16))) T sA[2][A_BLKS * BLK];
+  __shared__ __attribute__((aligned(16))) T sB[2][B_BLKS * BLK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t = xcd_tile(blockIdx.x, n_tiles);
+  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
   const int M = g.M;
+  const int lr = lane & 15, lc = (lane >> 4) * 8;           // lane's row / k offset inside a block
 
-  Frag<T> ra[A_CH], rb[B_CH];
-  auto load_tiles = [&](int kt) {
-    const int k0 = kt * BK;
+  // fragment block q of a tile: row group q / KS, k sub-step q % KS
+  const T *Ab = (const T *)g.A, *Wb = (const T *)g.W;
+  Frag<T> ra[A_PER_WAVE], rb[B_PER_WAVE];
+  auto load_stage = [&](int kt) {
+    const int k0 = kt * BK + lc;
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int idx = tid + c * 256, r = idx >> 2, kc = (idx & 3) * 8;
-      const int row = min(m0 + r, M - 1);
-      ra[c] = load_frag((const T *)g.A + (size_t)row * g.lda + k0 + kc);
+    for (int i = 0; i < A_PER_WAVE; ++i) {
+      const int q = wave * A_PER_WAVE + i;
+      const int row = min(m0 + (q / KS) * 16 + lr, M - 1);
+      ra[i] = load_frag(Ab + (size_t)row * g.lda + k0 + (q % KS) * 32);
     }
 #pragma unroll
-    for (int c = 0; c < B_CH; ++c) {
-      const int idx = tid + c * 256, r = idx >> 2, kc = (idx & 3) * 8;
-      rb[c] = load_frag((const T *)g.W + (size_t)(n0 + r) * g.ldw + k0 + kc);
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+      const int q = wave * B_PER_WAVE + i;
+      rb[i] = load_frag(Wb + (size_t)(n0 + (q / KS) * 16 + lr) * g.ldw + k0 + (q % KS) * 32);
     }
   };
-  auto store_tiles = [&](int buf) {
+  auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int idx = tid + c * 256, r = idx >> 2, kc = (idx & 3) * 8;
-      store_frag(&sA[buf][r * LS + kc], ra[c]);
-    }
+    for (int i = 0; i < A_PER_WAVE; ++i) store_frag(&sA[buf][(wave * A_PER_WAVE + i) * BLK + lane * FE], ra[i]);
 #pragma unroll
-    for (int c = 0; c < B_CH; ++c) {
-      const int idx = tid + c * 256, r = idx >> 2, kc = (idx & 3) * 8;
-      store_frag(&sB[buf][r * LS + kc], rb[c]);
-    }
+    for (int i = 0; i < B_PER_WAVE; ++i) store_frag(&sB[buf][(wave * B_PER_WAVE + i) * BLK + lane * FE], rb[i]);
   };
 
   f32x4 acc[MT][NT];
@@ -188,31 +136,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = g.K / BK;
-  load_tiles(0);
-  store_tiles(0);
+  load_stage(0);
+  store_stage(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) load_tiles(kt + 1);
-    Frag<T> fa[MT], fb[NT];
+    if (kt + 1 < KT) load_stage(kt + 1);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-      fa[i] = load_frag(&sA[cur][(wm * TM + i * 16 + (lane & 15)) * LS + (lane >> 4) * 8]);
+    for (int ks = 0; ks < KS; ++ks) {
+      Frag<T> fa[MT], fb[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      fb[j] = load_frag(&sB[cur][(wn * TN + j * 16 + (lane & 15)) * LS + (lane >> 4) * 8]);
+      for (int i = 0; i < MT; ++i) fa[i] = load_frag(&sA[cur][((wm * MT + i) * KS + ks) * BLK + lane * FE]);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int j = 0; j < NT; ++j) fb[j] = load_frag(&sB[cur][((wn * NT + j) * KS + ks) * BLK + lane * FE]);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) mfma(acc[i][j], fa[i], fb[j]);
-    if (kt + 1 < KT) store_tiles(cur ^ 1);
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) mfma(acc[i][j], fa[i], fb[j]);
+    }
+    if (kt + 1 < KT) store_stage(cur ^ 1);
     __syncthreads();
   }
 
   // epilogue: acc[i][j][r] = C[row0 + 16i + r][col0 + 16j]
   const int row0 = m0 + wm * TM + (lane >> 4) * 4;
-  const int wcol = n0 + wn * TN;            // first of this wave's 64 columns
-  const int col0 = wcol + (lane & 15);
+  const int wcol = n0 + wn * TN;            // first of this wave's TN columns
+  const int col0 = wcol + lr;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -222,10 +171,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       float v[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j) v[j] = acc[i][j][r];
-      if (EM == E_GEGLU) {
-        T *C = (T *)g.C + (size_t)row * g.ldc + wcol / 2 + (lane & 15);
-        C[0] = to_elem<T>(gelu_erf(v[0]) * v[1]);
-        C[16] = to_elem<T>(gelu_erf(v[2]) * v[3]);
+      if (EM == E_GEGLU) {  // sub-tiles (2p, 2p+1) hold matching GELU and gate columns
+        T *C = (T *)g.C + (size_t)row * g.ldc + wcol / 2 + lr;
+#pragma unroll
+        for (int p = 0; p < NT / 2; ++p) C[p * 16] = to_elem<T>(gelu_erf(v[2 * p]) * v[2 * p + 1]);
         continue;
       }
       if (g.bias) {
@@ -233,15 +182,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < NT; ++j) v[j] += g.bias[col0 + j * 16];
       }
       if (EM == E_STORE) {
-        if (g.rope_cos && wcol < g.rope_cols) {  // the wave's 64 columns are one head
+        if (g.rope_cos) {  // each 64-column group is one head: pairs (d, d + 32)
           const int p = g.pos[row];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int d = j * 16 + (lane & 15);
-            const float c = g.rope_cos[p * 32 + d], s = g.rope_sin[p * 32 + d];
-            const float lo = v[j], hi = v[j + 2];
-            v[j] = lo * c - hi * s;
-            v[j + 2] = hi * c + lo * s;
+          for (int hb = 0; hb < NT / 4; ++hb) {
+            if (wcol + hb * 64 >= g.rope_cols) break;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int d = j * 16 + lr;
+              const float c = g.rope_cos[p * 32 + d], s = g.rope_sin[p * 32 + d];
+              const float lo = v[hb * 4 + j], hi = v[hb * 4 + j + 2];
+              v[hb * 4 + j] = lo * c - hi * s;
+              v[hb * 4 + j + 2] = hi * c + lo * s;
+            }
           }
         }
         T *C = (T *)g.C + (size_t)row * g.ldc + col0;
@@ -552,27 +505,32 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
   return hipGetLastError();
 }
 
-template <typename T, int BM>
+template <typename T, int BM, int BN>
 static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
-  const dim3 grid(a.N / 128, (a.M + BM - 1) / BM);
+  const int tiles_n = a.N / BN, n_tiles = ((a.M + BM - 1) / BM) * tiles_n;
   switch (emode) {
-    case E_STORE: gemm_kernel<T, BM, E_STORE><<<grid, 256, 0, s>>>(a); break;
-    case E_RESID: gemm_kernel<T, BM, E_RESID><<<grid, 256, 0, s>>>(a); break;
-    case E_GEGLU: gemm_kernel<T, BM, E_GEGLU><<<grid, 256, 0, s>>>(a); break;
-    case E_RELU: gemm_kernel<T, BM, E_RELU><<<grid, 256, 0, s>>>(a); break;
-    case E_GELU_F32: gemm_kernel<T, BM, E_GELU_F32><<<grid, 256, 0, s>>>(a); break;
+    case E_STORE: gemm_kernel<T, BM, BN, E_STORE><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_RESID: gemm_kernel<T, BM, BN, E_RESID><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_GEGLU: gemm_kernel<T, BM, BN, E_GEGLU><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_RELU: gemm_kernel<T, BM, BN, E_RELU><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_GELU_F32: gemm_kernel<T, BM, BN, E_GELU_F32><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// Tile choice: the largest M tile that still gives at least one tile per CU.
 hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  if (a.N % 128 != 0 || a.K % 32 != 0) return hipErrorInvalidValue;
-  const bool big = (long)((a.M + 127) / 128) * (a.N / 128) >= 512;
-  if (bf16_mode && emode != E_GELU_F32)
-    return big ? gemm_dispatch<bf16, 128>(emode, a, s) : gemm_dispatch<bf16, 64>(emode, a, s);
-  return big ? gemm_dispatch<float, 128>(emode, a, s) : gemm_dispatch<float, 64>(emode, a, s);
+  if (a.N % 128 != 0 || a.K % 64 != 0) return hipErrorInvalidValue;
+  const long nt = a.N / 128;
+  if (bf16_mode && emode != E_GELU_F32) {
+    if (((a.M + 255) / 256) * nt >= 256) return gemm_dispatch<bf16, 256, 128>(emode, a, s);
+    if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<bf16, 128, 128>(emode, a, s);
+    return gemm_dispatch<bf16, 64, 128>(emode, a, s);
+  }
+  if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<float, 128, 128>(emode, a, s);
+  return gemm_dispatch<float, 64, 128>(emode, a, s);
 }
 
 hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, const float *shift, int n, void *out,

@@ -23,9 +23,9 @@ OK, ERR_ARG, ERR_OPTIONS, ERR_LENGTH, ERR_QTYPE, ERR_FILE, ERR_DEVICE, ERR_OOM, 
 STATUS_NAMES = {0: "OK", -1: "ARG", -2: "OPTIONS", -3: "LENGTH", -4: "QTYPE", -5: "FILE",
                 -6: "DEVICE", -7: "OOM", -8: "CAPACITY"}
 (K_EMBED, K_QKV, K_ATTN_GLOBAL, K_ATTN_LOCAL, K_OUTPROJ, K_MLP_IN, K_MLP_OUT, K_HEAD_GEMM, K_HEAD_ATTN,
- K_MISC, K_LN) = range(11)
+ K_MISC, K_LN, K_LAYER) = range(12)
 KERNEL_CLASS_NAMES = ["embed", "qkv", "attn_global", "attn_local", "outproj", "mlp_in", "mlp_out",
-                      "head_gemm", "head_attn", "misc", "ln"]
+                      "head_gemm", "head_attn", "misc", "ln", "layer"]
 N_KERNEL_CLASSES = len(KERNEL_CLASS_NAMES)
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -71,6 +71,8 @@ def load_library():
     L.jl_profile.argtypes = [vp, ctypes.c_int, ctypes.c_uint32]
     L.jl_profile_read.restype = ctypes.c_int
     L.jl_profile_read.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    L.jl_set_row_block_min_tokens.restype = ctypes.c_int
+    L.jl_set_row_block_min_tokens.argtypes = [vp, i64]
     L.jl_model_info.restype = ctypes.c_int
     L.jl_model_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.c_int]
     _lib = L
@@ -178,6 +180,10 @@ class Model:
                                          len(mp), _p(qt), stage, ctypes.c_void_p(out.data_ptr()),
                                          self._stream(stream)))
         return out
+
+    def set_row_block_min_tokens(self, min_tokens: int):
+        """bf16 batches with at least this many tokens use the row-block layer kernel."""
+        _check(self._lib.jl_set_row_block_min_tokens(self._h, int(min_tokens)))
 
     def profile(self, enable: bool, class_mask: int = (1 << N_KERNEL_CLASSES) - 1):
         _check(self._lib.jl_profile(self._h, int(enable), class_mask))

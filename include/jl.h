@@ -133,6 +133,17 @@ int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offs
                     int32_t n_seqs, const int32_t *mask_positions, int32_t n_markers,
                     const int32_t *qtype, int32_t stage, float *out_dev, void *stream);
 
+/*
+ * Tuning: bf16 batches of at least `min_tokens` packed tokens run each encoder
+ * layer as one attention launch plus one row-block layer launch (64 token rows
+ * per work-group: out-projection, LayerNorm, GEGLU MLP and the next layer's
+ * QKV with the rows resident in LDS, weights streamed from L2); smaller
+ * batches, and the FP32 mode, run one launch per GEMM.  Default 8,192; 0
+ * forces the row-block path, INT64_MAX the per-GEMM path.  Both compute the
+ * same function; their bf16 roundings differ in summation order only.
+ */
+int jl_set_row_block_min_tokens(jl_model *m, int64_t min_tokens);
+
 /* Kernel classes reported by the per-kernel timer. */
 enum jl_kernel_class {
   JL_K_EMBED = 0,      /* embedding gather + LayerNorm                         */
@@ -146,7 +157,9 @@ enum jl_kernel_class {
   JL_K_HEAD_ATTN = 8,  /* decision-head attention                               */
   JL_K_MISC = 9,       /* final LayerNorm + type row, gathers, scorer, softmax  */
   JL_K_LN = 10,        /* LayerNorm rows -> GEMM operand                        */
-  JL_K_NCLASS = 11
+  JL_K_LAYER = 11,     /* row-block layer kernel: out-proj, LayerNorm, GEGLU    */
+                       /* MLP and the next layer's QKV (large bf16 batches)     */
+  JL_K_NCLASS = 12
 };
 
 /* Turn the per-kernel timer on (1) or off (0); it brackets every launch of

@@ -50,7 +50,7 @@ def jit_models():
     from encoder_transformer_amd import lib
     w = synth.make_weights(seed=3, norm_jitter=True)
     path = synth.cached_weight_file(seed=3, norm_jitter=True, weights=w)
-    m = {"bf16": lib.Model(path, lib.BF16, 8192, 512), "fp32": lib.Model(path, lib.FP32, 8192, 512), "w": w}
+    m = {"bf16": lib.Model(path, lib.BF16, 20000, 1024), "fp32": lib.Model(path, lib.FP32, 8192, 512), "w": w}
     yield m
     m["bf16"].close()
     m["fp32"].close()
@@ -76,6 +76,37 @@ def test_stage_parity_jittered(jit_models, prec):
         errs[s] = float(np.max(np.abs(got - ref[s])))
     print(prec, {k: f"{v:.2e}" for k, v in errs.items()})
     assert all(np.isfinite(v) and v <= tol for v in errs.values()), errs
+
+
+def rowblock_batch():
+    """Short sequences packed in front of eight 1,024-token ones: over 8,192
+    tokens, so a bf16 forward takes the row-block layer kernel."""
+    return synth.concat([synth.make_batch(0), small_ragged(), synth.make_batch(2).subset(range(8))])
+
+
+def test_stage_parity_rowblock_path(jit_models):
+    """Hidden states of the row-block path (bf16, >= 8,192 tokens) against the
+    oracle, on the batch's first four sequences (the oracle runs only those)."""
+    from oracle import julia_oracle as jo
+    W = jo.OracleWeights(jit_models["w"])
+    batch = rowblock_batch()
+    assert batch.n_tokens >= 8192
+    head = batch.subset([0, 1, 2, 3])
+    rows = int(head.seq_offsets[-1])
+    stages = [1, 2, 3, 4, 12, 22, 23, 24, 25]
+    ref = oracle_stages(W, head, stages)
+    errs = {}
+    for st in stages:
+        got = run_stage(jit_models["bf16"], batch, st)
+        sub = got[:head.n_markers] if st == 25 else got[:rows]
+        errs[st] = float(np.max(np.abs(sub - ref[st])))
+    print("row-block bf16", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert all(np.isfinite(v) and v <= BF16_HIDDEN_TOL for v in errs.values()), errs
+    got = run_logits(jit_models["bf16"], batch)
+    ref_l = jo.forward(W, head)
+    err = float(np.max(np.abs(got[:head.n_markers] - ref_l)))
+    print("row-block bf16 max |dlogit|", err)
+    assert err <= BF16_LOGIT_TIGHT
 
 
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
@@ -165,19 +196,44 @@ def test_probs_and_read_offs(models, oracle_weights, prec):
     assert dp <= BF16_PROB_BOUND
 
 
-@pytest.mark.parametrize("prec", ["fp32", "bf16"])
-def test_batch_composition_and_order(models, prec):
-    """A sequence's logits do not depend on its neighbours or its place in the batch."""
-    batch = synth.make_batch(4).subset(list(range(12)))
-    packed = run_logits(models[prec], batch)
-    sl = marker_slices(batch)
-    for b in (0, 5, 11):
-        alone = run_logits(models[prec], batch.subset([b]))
-        assert np.array_equal(alone, packed[sl[b]]), b
-    perm = [7, 2, 11, 0, 9, 4, 1, 10, 3, 8, 6, 5]
-    got = run_logits(models[prec], batch.subset(perm))
-    expect = np.concatenate([packed[sl[b]] for b in perm])
-    assert np.array_equal(got, expect)
+@pytest.mark.parametrize("path", ["fp32", "bf16-per-gemm", "bf16-row-block"])
+def test_batch_composition_and_order(models, path):
+    """A sequence's logits do not depend on its neighbours or its place in the
+    batch: bitwise, within one code path."""
+    m = models["fp32" if path == "fp32" else "bf16"]
+    if path == "bf16-row-block":
+        m.set_row_block_min_tokens(0)
+    elif path == "bf16-per-gemm":
+        m.set_row_block_min_tokens(1 << 62)
+    try:
+        batch = synth.make_batch(4).subset(list(range(12)))
+        packed = run_logits(m, batch)
+        sl = marker_slices(batch)
+        for b in (0, 5, 11):
+            alone = run_logits(m, batch.subset([b]))
+            assert np.array_equal(alone, packed[sl[b]]), b
+        perm = [7, 2, 11, 0, 9, 4, 1, 10, 3, 8, 6, 5]
+        got = run_logits(m, batch.subset(perm))
+        expect = np.concatenate([packed[sl[b]] for b in perm])
+        assert np.array_equal(got, expect)
+    finally:
+        m.set_row_block_min_tokens(8192)
+
+
+def test_row_block_and_per_gemm_paths_agree(models):
+    """The two bf16 schedules compute the same function (rounding aside)."""
+    m = models["bf16"]
+    batch = synth.make_batch(2)
+    try:
+        m.set_row_block_min_tokens(0)
+        a = run_logits(m, batch)
+        m.set_row_block_min_tokens(1 << 62)
+        b = run_logits(m, batch)
+    finally:
+        m.set_row_block_min_tokens(8192)
+    err = float(np.max(np.abs(a - b)))
+    print("row-block vs per-GEMM max |dlogit|", err)
+    assert err <= BF16_LOGIT_TIGHT
 
 
 def test_determinism(models):
