@@ -498,7 +498,7 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
 
   // workspace
   const size_t T = (size_t)max_tokens, Mm = (size_t)max_markers, Bm = (size_t)m->max_seqs;
-  m->meta_ints = 2 * (Bm + 1) + Bm + Mm + 8 * (T / 64 + Bm + 1) + 8 * Bm + 64;
+  m->meta_ints = 2 * (Bm + 1) + Bm + Mm + 8 * (T / 64 + Bm + 1) + 8 * (T / 128 + Bm + 1) + 8 * Bm + 64;
   size_t off = 0;
   std::vector<std::pair<void **, size_t>> slots;
   auto reserve = [&](void **holder, size_t bytes) {
@@ -557,9 +557,9 @@ namespace {
 struct Plan {
   int slot = 0;
   int B = 0, M = 0, T = 0;
-  int n_work = 0;
+  int n_work = 0, n_work_wide = 0;  // 64-query and 128-query attention items
   const int *d_so = nullptr, *d_mo = nullptr, *d_qt = nullptr, *d_mp = nullptr;
-  const AttnWork *d_aw = nullptr, *d_mw = nullptr;
+  const AttnWork *d_aw = nullptr, *d_aw_wide = nullptr, *d_mw = nullptr;
 };
 
 // Build the metadata in pinned memory and enqueue its upload.
@@ -598,17 +598,23 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
   for (int b = 0; b < B; ++b) order[b] = b;
   std::stable_sort(order.begin(), order.end(),
                    [&](int a, int b) { return so[a + 1] - so[a] > so[b + 1] - so[b]; });
-  const size_t o_aw = o;
-  int nw = 0;
-  for (int b : order) {
-    const int start = so[b], len = so[b + 1] - so[b];
-    for (int q0 = 0; q0 < len; q0 += 64) {
-      AttnWork w{start + q0, std::min(64, len - q0), start, len, q0, 0, 0, 0};
-      std::memcpy(h + o, &w, sizeof(w));
-      o += 8;
-      ++nw;
+  auto work_list = [&](int tile, int &count) {
+    count = 0;
+    for (int b : order) {
+      const int start = so[b], len = so[b + 1] - so[b];
+      for (int q0 = 0; q0 < len; q0 += tile) {
+        AttnWork w{start + q0, std::min(tile, len - q0), start, len, q0, 0, 0, 0};
+        std::memcpy(h + o, &w, sizeof(w));
+        o += 8;
+        ++count;
+      }
     }
-  }
+  };
+  const size_t o_aw = o;
+  int nw = 0, nw_wide = 0;
+  work_list(64, nw);
+  const size_t o_aw_wide = o;
+  work_list(128, nw_wide);
   const size_t o_mw = o;
   for (int b = 0; b < B; ++b) {
     const int first = h[o_mo + b], cnt = h[o_mo + b + 1] - first;
@@ -619,6 +625,8 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
   if (o > m->meta_ints) return fail(JL_ERR_CAPACITY, "batch metadata exceeds the staging buffer");
   JL_HIP(hipMemcpyAsync(dmeta, h, o * 4, hipMemcpyHostToDevice, s));
   pl.n_work = nw;
+  pl.n_work_wide = nw_wide;
+  pl.d_aw_wide = (const AttnWork *)(dmeta + o_aw_wide);
   pl.d_so = dmeta + o_so;
   pl.d_mo = dmeta + o_mo;
   pl.d_qt = dmeta + o_qt;
@@ -679,6 +687,14 @@ struct Launch {
     if (e_ != hipSuccess) return fail(JL_ERR_DEVICE, std::string("kernel launch failed: ") + hipGetErrorString(e_)); \
   } while (0)
 
+// Sequence-wide attention takes 128-query work items (two 16-query sub-tiles
+// per wave reuse every K/V fragment read from LDS); the +-64 window takes
+// 64-query items, which waste fewer masked keys.
+hipError_t attention(bool bf, AttnArgs at, const Plan &pl, bool whole_sequence, hipStream_t s) {
+  at.work = whole_sequence ? pl.d_aw_wide : pl.d_aw;
+  return launch_attention(bf, at, whole_sequence ? pl.n_work_wide : pl.n_work, whole_sequence ? 128 : 64, s);
+}
+
 GemmArgs gemm(const void *A, int lda, const void *W, int ldw, const float *bias, void *C, int ldc, int M, int N,
               int K) {
   GemmArgs a{};
@@ -736,7 +752,7 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     for (int l = 0; l < kLayers; ++l) {
       const bool glob = layer_is_global(l);
       at.half_window = glob ? -1 : kHalfWindow;
-      JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, launch_attention(bf, at, pl.n_work, s));
+      JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, attention(bf, at, pl, glob, s));
       LayerArgs la{};
       const LayerW &W = m->L[l];
       la.x = m->x;
@@ -775,7 +791,7 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     q.rope_cols = 2 * D;
     JL_LAUNCH(JL_K_QKV, launch_gemm(bf, E_STORE, q, s));
     at.half_window = glob ? -1 : kHalfWindow;
-    JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, launch_attention(bf, at, pl.n_work, s));
+    JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, attention(bf, at, pl, glob, s));
     JL_LAUNCH(JL_K_OUTPROJ, launch_gemm(bf, E_RESID, gemm(m->o, D, W.Wo, D, nullptr, m->x, D, T, D, D), s));
     JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, W.mlp_norm, nullptr, T, u, s));
     JL_LAUNCH(JL_K_MLP_IN, launch_gemm(bf, E_GEGLU, gemm(u, D, W.Wi, D, nullptr, m->act, kGeglu, T, 2 * kGeglu, D), s));
@@ -794,7 +810,7 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n1_w, H.n1_b, T, u, s));
     JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_STORE, gemm(u, D, H.in_w, D, H.in_b, m->qkv, 3 * D, T, 3 * D, D), s));
     at.half_window = -1;
-    JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, at, pl.n_work, s));
+    JL_LAUNCH(JL_K_HEAD_ATTN, attention(bf, at, pl, true, s));
     JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->o, D, H.out_w, D, H.out_b, m->x, D, T, D, D), s));
     JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n2_w, H.n2_b, T, u, s));
     JL_LAUNCH(JL_K_HEAD_GEMM,
@@ -827,7 +843,7 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     mk.o_stride = D;
     mk.work = pl.d_mw;
     mk.half_window = -1;
-    JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, mk, pl.B, s));
+    JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, mk, pl.B, 64, s));
     JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->om, D, H.out_w, D, H.out_b, m->z, D, M, D, D), s));
     JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->z, H.n2_w, H.n2_b, M, um, s));
     JL_LAUNCH(JL_K_HEAD_GEMM,

@@ -43,10 +43,11 @@ struct GemmArgs {
   int rope_cols;        // columns [0, rope_cols) are rotated (q and k: 768)
 };
 
-// One attention work item: up to 64 queries of one sequence, one head per blockIdx.y.
+// One attention work item: up to 64 or 128 queries (the launch's tile size) of
+// one sequence, one head per blockIdx.y.
 struct AttnWork {
   int q_row0;   // first query row in the q buffer
-  int n_q;      // queries in this item (1..64)
+  int n_q;      // queries in this item (1..tile size)
   int kv_row0;  // first key row of the sequence in the k/v buffers
   int kv_len;   // sequence length
   int q_pos0;   // position of the first query inside its sequence
@@ -92,7 +93,7 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
 hipError_t launch_gemm(bool bf16, int emode, const GemmArgs &a, hipStream_t s);
 hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, const float *shift, int n, void *out,
                           hipStream_t s);
-hipError_t launch_attention(bool bf16, const AttnArgs &a, int n_work, hipStream_t s);
+hipError_t launch_attention(bool bf16, const AttnArgs &a, int n_work, int queries_per_block, hipStream_t s);
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s);
 hipError_t launch_final_ln_type(const float *x, const float *gain, const float *type_rows,
                                 const int *qtype, const int *tok_seq, int T, float *h,

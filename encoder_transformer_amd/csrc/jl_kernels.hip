@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 }
 
 // ---------------------------------------------------------------------------
-// attention: one block = up to 64 queries of one sequence and one head.
+// attention: one block = up to 64 NSUB queries of one sequence and one head.
 // S^T = K Q^T and O^T = V^T P^T keep each lane's 4 x 4 scores, its running
 // max / sum and its output column on the same query (lane % 16).
 // ---------------------------------------------------------------------------
@@ -245,29 +245,42 @@ __device__ inline void store_vt_pair<float>(float *row, int slot, float a, float
   *reinterpret_cast<float2 *>(row + slot) = make_float2(a, b);
 }
 
-template <typename T>
+// NSUB query sub-tiles of 16 per wave, 4 waves: a block covers 64 NSUB
+// queries.  Masking is evaluated only on key tiles that reach past the
+// sequence end or, on local layers, past the window of some query.
+template <typename T, int NSUB>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int KS = 72;  // LDS row stride (elements)
+  constexpr int QW = 16 * NSUB;
   __shared__ __attribute__((aligned(16))) T sK[2][64 * KS];
   __shared__ __attribute__((aligned(16))) T sV[2][64 * KS];  // [d][slot]
   const AttnWork w = a.work[blockIdx.x];
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 15, g = lane >> 4;
-  const int qi = wave * 16 + ql;
-  const int qpos = w.q_pos0 + qi;
   const float scale = 0.125f * kLog2e;  // 1/sqrt(64), in the exp2 domain
+  const bool local = a.half_window >= 0;
+  const int W = a.half_window;
 
-  const T *qp = (const T *)a.q + (size_t)(w.q_row0 + min(qi, w.n_q - 1)) * a.q_stride + h * kHeadDim;
-  const Frag<T> fq0 = load_frag(qp + g * 8);
-  const Frag<T> fq1 = load_frag(qp + 32 + g * 8);
+  Frag<T> fq[NSUB][2];
+  int qpos[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const int qi = wave * QW + 16 * s + ql;
+    qpos[s] = w.q_pos0 + qi;
+    const T *qp = (const T *)a.q + (size_t)(w.q_row0 + min(qi, w.n_q - 1)) * a.q_stride + h * kHeadDim;
+    fq[s][0] = load_frag(qp + g * 8);
+    fq[s][1] = load_frag(qp + 32 + g * 8);
+  }
 
   int lo = 0, hi = w.kv_len;
-  if (a.half_window >= 0) {
-    lo = max(0, w.q_pos0 - a.half_window);
-    hi = min(w.kv_len, w.q_pos0 + w.n_q + a.half_window);
+  if (local) {
+    lo = max(0, w.q_pos0 - W);
+    hi = min(w.kv_len, w.q_pos0 + w.n_q + W);
   }
   const int n_tiles = (hi - lo + 63) >> 6;
+  // key tiles [base, base + 64) inside every query's window need no mask
+  const int q_first = w.q_pos0, q_last = w.q_pos0 + w.n_q - 1;
 
   const T *kbase = (const T *)a.k + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
   const T *vbase = (const T *)a.v + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
@@ -291,10 +304,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) store_vt_pair<T>(&sV[buf][(c + e) * KS], slot, frag_get(rv0, e), frag_get(rv1, e));
   };
 
-  float m = -INFINITY, l = 0.f;
-  f32x4 o[4];
+  float m[NSUB], l[NSUB];
+  f32x4 o[NSUB][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < NSUB; ++s) {
+    m[s] = -INFINITY;
+    l[s] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   if (n_tiles > 0) {
     load_tile(0);
@@ -304,67 +322,95 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   for (int t = 0; t < n_tiles; ++t) {
     const int cur = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
-    f32x4 s[4];
+    // S^T = K Q^T for each query sub-tile (raw dot products)
+    f32x4 sc[NSUB][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      s[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
       const T *kr = &sK[cur][(ks * 16 + ql) * KS + g * 8];
-      mfma(s[ks], load_frag(kr), fq0);
-      mfma(s[ks], load_frag(kr + 32), fq1);
+      const Frag<T> k0 = load_frag(kr), k1 = load_frag(kr + 32);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        sc[s][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mfma(sc[s][ks], k0, fq[s][0]);
+        mfma(sc[s][ks], k1, fq[s][1]);
+      }
     }
     const int base = lo + t * 64;
-    float mt = -INFINITY;
+    const bool need_mask = base + 64 > hi || (local && (base < q_last - W || base + 63 > q_first + W));
+    if (need_mask) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = base + ks * 16 + 4 * g + r;
-        bool ok = key < hi;
-        if (a.half_window >= 0) ok = ok && abs(qpos - key) <= a.half_window;
-        const float v = ok ? s[ks][r] * scale : -INFINITY;
-        s[ks][r] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m - m_use);
-    m = m_new;
-    l *= alpha;
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] *= alpha;
+          for (int r = 0; r < 4; ++r) {
+            const int key = base + ks * 16 + 4 * g + r;
+            const bool ok = key < hi && (!local || abs(qpos[s] - key) <= W);
+            if (!ok) sc[s][ks][r] = -INFINITY;
+          }
+    }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int s = 0; s < NSUB; ++s) {
+      float mt = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[ks][r] - m_use);
-        s[ks][r] = p;
-        l += p;
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        mt = fmaxf(mt, fmaxf(fmaxf(sc[s][ks][0], sc[s][ks][1]), fmaxf(sc[s][ks][2], sc[s][ks][3])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m[s], mt * scale);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[s] - m_use);
+      m[s] = m_new;
+      l[s] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[s][i] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[s][ks][r], scale, -m_use));
+          sc[s][ks][r] = p;
+          l[s] += p;
+        }
+    }
+    // O^T += V^T P^T
 #pragma unroll
     for (int kstep = 0; kstep < 2; ++kstep) {
-      float pv[8];
+      Frag<T> fp[NSUB];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) { pv[r] = s[2 * kstep][r]; pv[4 + r] = s[2 * kstep + 1][r]; }
-      Frag<T> fp;
-      frag_from(fp, pv);
+      for (int s = 0; s < NSUB; ++s) {
+        float pv[8];
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
-        mfma(o[ds], load_frag(&sV[cur][(ds * 16 + ql) * KS + kstep * 32 + g * 8]), fp);
+        for (int r = 0; r < 4; ++r) {
+          pv[r] = sc[s][2 * kstep][r];
+          pv[4 + r] = sc[s][2 * kstep + 1][r];
+        }
+        frag_from(fp[s], pv);
+      }
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) {
+        const Frag<T> vf = load_frag(&sV[cur][(ds * 16 + ql) * KS + kstep * 32 + g * 8]);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) mfma(o[s][ds], vf, fp[s]);
+      }
     }
     if (t + 1 < n_tiles) store_tile(cur ^ 1);
     __syncthreads();
   }
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (qi < w.n_q) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    T *op = (T *)a.o + (size_t)(w.q_row0 + qi) * a.o_stride + h * kHeadDim + 4 * g;
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
+  for (int s = 0; s < NSUB; ++s) {
+    float lt = l[s];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const int qi = wave * QW + 16 * s + ql;
+    if (qi < w.n_q) {
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      T *op = (T *)a.o + (size_t)(w.q_row0 + qi) * a.o_stride + h * kHeadDim + 4 * g;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) op[ds * 16 + r] = to_elem<T>(o[ds][r] * inv);
+      for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) op[ds * 16 + r] = to_elem<T>(o[s][ds][r] * inv);
+    }
   }
 }
 
@@ -541,11 +587,18 @@ hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, cons
   return hipGetLastError();
 }
 
-hipError_t launch_attention(bool bf16_mode, const AttnArgs &a, int n_work, hipStream_t s) {
+hipError_t launch_attention(bool bf16_mode, const AttnArgs &a, int n_work, int queries_per_block, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
   const dim3 grid(n_work, kHeads);
-  if (bf16_mode) attn_kernel<bf16><<<grid, 256, 0, s>>>(a);
-  else attn_kernel<float><<<grid, 256, 0, s>>>(a);
+  if (queries_per_block == 64) {
+    if (bf16_mode) attn_kernel<bf16, 1><<<grid, 256, 0, s>>>(a);
+    else attn_kernel<float, 1><<<grid, 256, 0, s>>>(a);
+  } else if (queries_per_block == 128) {
+    if (bf16_mode) attn_kernel<bf16, 2><<<grid, 256, 0, s>>>(a);
+    else attn_kernel<float, 2><<<grid, 256, 0, s>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
