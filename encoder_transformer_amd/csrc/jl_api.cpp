@@ -64,8 +64,10 @@ uint16_t f32_to_bf16(float f) {  // round to nearest even; NaN stays NaN
 // block (gn, s) holds 64 lanes x 8 bf16, lane l element e = W[16 gn + l % 16]
 // [32 s + 8 (l / 16) + e]; blocks are stored gn-major (index gn * K/32 + s), so a
 // wave's B fragment for 16 output columns and 32 k is one contiguous 1 KB load.
-// `row_of` maps packed row -> source row (GEGLU interleave), or nullptr.
-void pack_fragments(const float *W, int N, int K, const std::vector<int> *row_of, uint16_t *out) {
+// `row_of` maps packed row -> source row (GEGLU interleave), or nullptr;
+// `row_scale` scales packed rows by powers of two (exact), or nullptr.
+void pack_fragments(const float *W, int N, int K, const std::vector<int> *row_of, uint16_t *out,
+                    const std::vector<float> *row_scale = nullptr) {
   const int ks = K / 32;
   for (int gn = 0; gn < N / 16; ++gn)
     for (int s = 0; s < ks; ++s) {
@@ -73,7 +75,8 @@ void pack_fragments(const float *W, int N, int K, const std::vector<int> *row_of
       for (int l = 0; l < 64; ++l) {
         const int r = 16 * gn + (l & 15);
         const float *src = W + (size_t)(row_of ? (*row_of)[r] : r) * K + 32 * s + 8 * (l >> 4);
-        for (int e = 0; e < 8; ++e) blk[l * 8 + e] = f32_to_bf16(src[e]);
+        const float sc = row_scale ? (*row_scale)[r] : 1.0f;
+        for (int e = 0; e < 8; ++e) blk[l * 8 + e] = f32_to_bf16(sc * src[e]);
       }
     }
 }
@@ -356,9 +359,10 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     pend.push_back({dst, off});
   };
 
-  auto put_packed = [&](const float *src, int rows, int cols, const void **dst, const std::vector<int> *row_of) {
+  auto put_packed = [&](const float *src, int rows, int cols, const void **dst, const std::vector<int> *row_of,
+                        const std::vector<float> *row_scale = nullptr) {
     const size_t off = ar.add((size_t)rows * cols * 2);
-    pack_fragments(src, rows, cols, row_of, (uint16_t *)(ar.buf.data() + off));
+    pack_fragments(src, rows, cols, row_of, (uint16_t *)(ar.buf.data() + off), row_scale);
     pend.push_back({dst, off});
   };
 
@@ -387,9 +391,14 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
   put_f32(t, D, &m->emb_norm);
   // GEGLU rows interleaved by 16: [a0..a15, g0..g15, a16..a31, g16..g31, ...]
   std::vector<int> geglu_rows(2 * kGeglu);
+  // The row-block kernel's packed copy carries the gate rows halved (exact),
+  // so its GEGLU computes gelu(z) g = (z + |z| erf(|z|/sqrt 2)) (g/2).
+  std::vector<float> gate_half(2 * kGeglu);
   for (int o = 0; o < kGeglu; ++o) {
     geglu_rows[32 * (o / 16) + (o % 16)] = o;
     geglu_rows[32 * (o / 16) + 16 + (o % 16)] = kGeglu + o;
+    gate_half[32 * (o / 16) + (o % 16)] = 1.0f;
+    gate_half[32 * (o / 16) + 16 + (o % 16)] = 0.5f;
   }
   for (int l = 0; l < kLayers; ++l) {
     const std::string p = "layers." + std::to_string(l) + ".";
@@ -407,7 +416,7 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     put_f32(t, D, &m->L[l].mlp_norm);
     GET(p + "mlp.Wi.weight", 2 * kGeglu, D);
     put_elem(t, 2 * kGeglu, D, &m->L[l].Wi, &geglu_rows);
-    if (bf) put_packed(t, 2 * kGeglu, D, &m->L[l].pWi, &geglu_rows);
+    if (bf) put_packed(t, 2 * kGeglu, D, &m->L[l].pWi, &geglu_rows, &gate_half);
     GET(p + "mlp.Wo.weight", D, kGeglu);
     put_elem(t, D, kGeglu, &m->L[l].Wout, nullptr);
     if (bf) put_packed(t, D, kGeglu, &m->L[l].pWout, nullptr);

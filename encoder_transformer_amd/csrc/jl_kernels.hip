@@ -7,6 +7,8 @@
 // feeds the same fragment to eight 16x16x4 steps, so one tiling serves both.
 // Row-wise work (LayerNorm, softmax over options, dot products) uses
 // wavefront reductions.
+#include <type_traits>
+
 #include "jl_device.h"
 
 // No FMA contraction: unrolled code handles each row of a tile in its own
@@ -174,7 +176,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
       if (EM == E_GEGLU) {  // sub-tiles (2p, 2p+1) hold matching GELU and gate columns
         T *C = (T *)g.C + (size_t)row * g.ldc + wcol / 2 + lr;
 #pragma unroll
-        for (int p = 0; p < NT / 2; ++p) C[p * 16] = to_elem<T>(gelu_erf(v[2 * p]) * v[2 * p + 1]);
+        for (int p = 0; p < NT / 2; ++p) {  // bf16 output: the cheaper erf is exact enough
+          const float ge = std::is_same<T, bf16>::value ? gelu_erf_fast(v[2 * p]) : gelu_erf(v[2 * p]);
+          C[p * 16] = to_elem<T>(ge * v[2 * p + 1]);
+        }
         continue;
       }
       if (g.bias) {

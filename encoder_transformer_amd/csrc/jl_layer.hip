@@ -35,23 +35,25 @@ namespace jl {
 namespace {
 using namespace dev;
 
+#define DI __device__ __attribute__((always_inline)) inline
+
 constexpr int RB = kLayerRows;    // 64 rows per work-group
 constexpr int NW = 8;             // waves per work-group
 constexpr int KSD = kWidth / 32;  // 12 k-steps over the model width
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline bf16x8 ldg8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-__device__ inline bf16x8 lds8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+DI bf16x8 ldg8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+DI bf16x8 lds8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
 // Element offset of (row, k) in a fragment-ordered [64 x (32 * ksteps)] tile:
 // block (row / 16, k / 32) of 64 lanes x 8 elements, lane (row % 16) + 16 * ((k % 32) / 8).
-__device__ inline int afrag(int row, int k, int ksteps) {
+DI int afrag(int row, int k, int ksteps) {
   return ((row >> 4) * ksteps + (k >> 5)) * 512 + ((row & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
 }
 
 // 4 consecutive columns (k .. k+3, k % 4 == 0) of one row as bf16 into a fragment tile.
-__device__ inline void put4(bf16 *tile, int row, int k, int ksteps, float a, float b, float c, float d) {
+DI void put4(bf16 *tile, int row, int k, int ksteps, float a, float b, float c, float d) {
   bf16x4 v;
   v[0] = (bf16)a;
   v[1] = (bf16)b;
@@ -60,49 +62,62 @@ __device__ inline void put4(bf16 *tile, int row, int k, int ksteps, float a, flo
   *reinterpret_cast<bf16x4 *>(tile + afrag(row, k, ksteps)) = v;
 }
 
+// Raw buffer resource over packed weights: loads take a per-lane byte offset
+// in a VGPR and the k-step offset as a scalar or immediate, so streaming them
+// costs no vector address arithmetic.
+DI __amdgpu_buffer_rsrc_t weight_rsrc(const bf16 *W) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16 *>(W), (short)0, 0x7fffffff, 0x00020000);
+}
+DI bf16x8 ldw(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // acc[i][j] += (A_tile(LDS, 64 x 32*KSTEPS) . Wp^T)^T sub-tiles for this wave's
 // NT groups of 16 output columns (group ng[j]), k-steps ks0 .. ks0+KSTEPS-1 of
-// Wp.  B fragments for steps s .. s+PD-1 are in flight; each register is
-// consumed in place and reloaded right after, so nothing forces an early wait.
-template <int NT, int KSTEPS, int PD>
-__device__ inline void gemm_rows(f32x4 (&acc)[4][NT], const bf16 *sAt, const bf16 *__restrict__ Wp,
-                                 int w_ksteps, const int (&ng)[NT], int ks0, int lane) {
-  static_assert(KSTEPS % PD == 0 && PD % 2 == 0, "k-steps: a multiple of an even prefetch depth");
-  const bf16 *wp[NT];
+// Wp.  Weight fragments for PD k-steps are in flight: each register is
+// reloaded right after the MFMAs that read it; activation fragments are
+// double-buffered one step ahead.  Fully unrolled.
+template <int NT, int KSTEPS, int PD, int NTA = NT>
+DI void gemm_rows(f32x4 (&acc)[4][NTA], const bf16 *sAt, const bf16 *__restrict__ Wp, int w_ksteps,
+                  const int (&ng)[NT], int ks0, int lane) {
+  static_assert(NT <= NTA, "accumulator columns");
+  static_assert(PD <= KSTEPS, "prefetch depth");
+  const __amdgpu_buffer_rsrc_t rw = weight_rsrc(Wp);
+  int vo[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) wp[j] = Wp + ((size_t)ng[j] * w_ksteps + ks0) * 512 + lane * 8;
+  for (int j = 0; j < NT; ++j) vo[j] = ((ng[j] * w_ksteps + ks0) * 64 + lane) * 16;
   const bf16 *ap = sAt + lane * 8;
   bf16x8 fb[PD][NT], fa[2][4];
 #pragma unroll
   for (int p = 0; p < PD; ++p)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) fb[p][j] = ldg8(wp[j] + p * 512);
+    for (int j = 0; j < NT; ++j) fb[p][j] = ldw(rw, vo[j], p * 1024);
 #pragma unroll
   for (int i = 0; i < 4; ++i) fa[0][i] = lds8(ap + (i * KSTEPS) * 512);
-#pragma unroll 1
-  for (int s0 = 0; s0 < KSTEPS; s0 += PD) {
 #pragma unroll
-    for (int p = 0; p < PD; ++p) {
-      const int s = s0 + p;
-      if (s + 1 < KSTEPS) {
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int p = s % PD;
+    if (s + 1 < KSTEPS) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[(p + 1) & 1][i] = lds8(ap + (i * KSTEPS + s + 1) * 512);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[p][j], fa[p & 1][i], acc[i][j], 0, 0, 0);
-      if (s + PD < KSTEPS) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) fb[p][j] = ldg8(wp[j] + (s + PD) * 512);
-      }
+      for (int i = 0; i < 4; ++i) fa[(s + 1) & 1][i] = lds8(ap + (i * KSTEPS + s + 1) * 512);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[p][j], fa[s & 1][i], acc[i][j], 0, 0, 0);
+    if (s + PD < KSTEPS) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) fb[p][j] = ldw(rw, vo[j], (s + PD) * 1024);
+    }
+    // keep each reload right behind the MFMAs that free its registers: the
+    // scheduler would otherwise sink the reloads towards the next wait
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <int NT>
-__device__ inline void zero(f32x4 (&acc)[4][NT]) {
+DI void zero(f32x4 (&acc)[4][NT]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -113,7 +128,7 @@ __device__ inline void zero(f32x4 (&acc)[4][NT]) {
 // 3 sub-tiles; lane (r16 + 16 g) holds row 16 i + r16, columns 16 j + 4 g + r.
 // Two passes (mean, then the mean of squared deviations), reduced over the 4
 // lane groups and then over the 8 waves through LDS.
-__device__ inline void row_stats(const f32x4 (&X)[4][3], float (*sRed)[RB], int lane, int wave,
+DI void row_stats(const f32x4 (&X)[4][3], float (*sRed)[RB], int lane, int wave,
                                  float (&mean)[4], float (&rstd)[4]) {
   const int r16 = lane & 15, g = lane >> 4;
   float part[4];
@@ -171,7 +186,7 @@ __device__ inline void row_stats(const f32x4 (&X)[4][3], float (*sRed)[RB], int 
 }
 
 // sA = bf16(gain * (X - mean) * rstd), fragment order over the full width.
-__device__ inline void write_ln(const f32x4 (&X)[4][3], const float *__restrict__ gain, const float (&mean)[4],
+DI void write_ln(const f32x4 (&X)[4][3], const float *__restrict__ gain, const float (&mean)[4],
                                 const float (&rstd)[4], bf16 *sA, int lane, int wave) {
   const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -190,7 +205,7 @@ __device__ inline void write_ln(const f32x4 (&X)[4][3], const float *__restrict_
 // applied: NT = 4 covers the whole head, NT = 2 the half `half` (d in
 // 16 half .. 16 half + 15 and its partners d + 32).
 template <int NT>
-__device__ inline void rope_heads(const bf16 *sA, const float *sCos, const float *sSin, const LayerArgs &a,
+DI void rope_heads(const bf16 *sA, const float *sCos, const float *sSin, const LayerArgs &a,
                                   int head_col, int half, int lane, int row0, int T) {
   const int r16 = lane & 15, g = lane >> 4;
   f32x4 H[4][NT];
@@ -227,42 +242,90 @@ __device__ inline void rope_heads(const bf16 *sA, const float *sCos, const float
   }
 }
 
-// One MLP chunk: outputs 256 c .. 256 c + 64 PAIRS (PAIRS = 4: 256 outputs,
-// PAIRS = 2: the last 128).  Wave w computes outputs 256 c + 16 PAIRS/2 ... as
-// PAIRS/2 (GELU, gate) group pairs, writes GEGLU into sH, then every wave adds
-// sH . W_out^T over the chunk's k-range into its 48 columns of X.
-template <int NTI>
-__device__ inline void mlp_chunk(f32x4 (&X)[4][3], const bf16 *sA, bf16 *sH, const LayerArgs &a, int c, int lane,
-                                 int wave) {
-  constexpr int OUT = 8 * 8 * NTI;  // outputs in this chunk: 256 (NTI 4) or 128 (NTI 2)
-  constexpr int KS = OUT / 32;      // W_out k-steps of the chunk
+// v = u' . W_v^T for this block's rows: 384 columns, wave w columns
+// 48w .. 48w+47 (reusing X's registers).
+DI void project_v(f32x4 (&X)[4][3], const bf16 *sA, const LayerArgs &a, int lane, int wave, int row0,
+                                 int T) {
   const int r16 = lane & 15, g = lane >> 4;
-  f32x4 H[4][NTI];
-  zero(H);
+  zero(X);
+  const int ng[3] = {48 + 3 * wave, 48 + 3 * wave + 1, 48 + 3 * wave + 2};
+  gemm_rows<3, KSD, 4>(X, sA, a.Wqkv_next, KSD, ng, 0, lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = row0 + 16 * i + r16;
+    if (row >= T) continue;
+    bf16 *v = a.qkv_out + (size_t)row * (3 * kWidth) + 2 * kWidth + 48 * wave + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      bf16x4 t;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] = (bf16)X[i][j][r];
+      *reinterpret_cast<bf16x4 *>(v + 16 * j) = t;
+    }
+  }
+}
+
+// MLP chunk c covers outputs 256 c .. 256 c + 64 NTI - 1 (NTI = 4: 256
+// outputs, NTI = 2: the last 128), i.e. 128 NTI interleaved W_i rows.
+// wi_gemm: wave w's (GELU group, gate group) pairs of the chunk into H[.][0, NTI).
+template <int NTI>
+DI void wi_gemm(f32x4 (&H)[4][4], const bf16 *sA, const LayerArgs &a, int c, int lane, int wave) {
   int ng[NTI];
 #pragma unroll
-  for (int j = 0; j < NTI; ++j) ng[j] = 32 * c + NTI * wave + j;  // 512 W_i rows = 32 groups per full chunk
-  gemm_rows<NTI, KSD, (NTI == 4 ? 2 : 4)>(H, sA, a.Wi, KSD, ng, 0, lane);
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NTI; ++j) H[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NTI; ++j) ng[j] = 32 * c + NTI * wave + j;  // a full chunk is 32 groups of 16 rows
+  gemm_rows<NTI, KSD, (NTI == 4 ? 3 : 4), 4>(H, sA, a.Wi, KSD, ng, 0, lane);
+}
+
+// gelu(z) * g for a gate value gh = g / 2 (the packed W_i carries the gate
+// rows halved): gelu(z) = (z + |z| erf(|z| / sqrt 2)) / 2, erf from
+// Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7), erf = 1 - t P(t) exp(-x^2),
+// t = 1 / (1 + p x), x = |z| / sqrt 2, with 1 / sqrt 2 folded into p and the
+// exponent.  12 vector operations and 2 transcendentals per value.
+DI float geglu_half_gate(float z, float gh) {
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164189450033013f, az, 1.0f));  // p / sqrt 2
+  float q = fmaf(1.061405429f, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  q = q * t;
+  const float e = __builtin_amdgcn_exp2f((z * z) * -0.72134752044448170f);  // exp(-z^2 / 2)
+  const float u = fmaf(-az, q * e, az);                                     // |z| erf(|z| / sqrt 2)
+  return (z + u) * gh;
+}
+
+// GEGLU of H[.][0, NTI) into the chunk buffer sHb (fragment order, 64 x 64 NTI).
+template <int NTI>
+DI void geglu(const f32x4 (&H)[4][4], bf16 *sHb, int lane, int wave) {
+  constexpr int KS = 2 * NTI;  // k-steps of the chunk buffer
+  const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int p = 0; p < NTI / 2; ++p) {
     const int col = 8 * NTI * wave + 16 * p + 4 * g;  // chunk-local output column
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      put4(sH, 16 * i + r16, col, KS, gelu_erf(H[i][2 * p][0]) * H[i][2 * p + 1][0],
-           gelu_erf(H[i][2 * p][1]) * H[i][2 * p + 1][1], gelu_erf(H[i][2 * p][2]) * H[i][2 * p + 1][2],
-           gelu_erf(H[i][2 * p][3]) * H[i][2 * p + 1][3]);
+      put4(sHb, 16 * i + r16, col, KS, geglu_half_gate(H[i][2 * p][0], H[i][2 * p + 1][0]),
+           geglu_half_gate(H[i][2 * p][1], H[i][2 * p + 1][1]), geglu_half_gate(H[i][2 * p][2], H[i][2 * p + 1][2]),
+           geglu_half_gate(H[i][2 * p][3], H[i][2 * p + 1][3]));
   }
-  __syncthreads();
-  {
-    const int ngo[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
-    gemm_rows<3, KS, 4>(X, sH, a.Wout, kGeglu / 32, ngo, 8 * c, lane);
-  }
-  __syncthreads();  // sH is rewritten by the next chunk
+}
+
+// X (wave w: columns 48w .. 48w+47) += chunk buffer . W_out^T over the
+// chunk's k-range.
+template <int NTI>
+DI void mlp_out(f32x4 (&X)[4][3], const bf16 *sHb, const LayerArgs &a, int c, int lane, int wave) {
+  const int ngo[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
+  gemm_rows<3, 2 * NTI, 4>(X, sHb, a.Wout, kGeglu / 32, ngo, 8 * c, lane);
 }
 
 __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sA[RB * kWidth];  // 48 KB: o, then u, then u'
-  __shared__ __attribute__((aligned(16))) bf16 sH[RB * 256];     // 32 KB: one GEGLU chunk
+  __shared__ __attribute__((aligned(16))) bf16 sH0[RB * 256];    // 32 KB: GEGLU chunk buffers,
+  __shared__ __attribute__((aligned(16))) bf16 sH1[RB * 256];    // 32 KB: double-buffered
   __shared__ __attribute__((aligned(16))) float sCos[RB * 32];   // 8 KB: RoPE rows of this block
   __shared__ __attribute__((aligned(16))) float sSin[RB * 32];   // 8 KB
   __shared__ float sRed[NW][RB];
@@ -309,14 +372,53 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   write_ln(X, a.mlp_norm, mean, rstd, sA, lane, wave);
   __syncthreads();
 
-  // 4. MLP: the 1,152 intermediate columns in 4 chunks of 256 and one of 128.
-  //    A chunk of n outputs is 2n interleaved W_i rows; wave w takes its
-  //    share as (GELU group, gate group) pairs of the same 16 outputs.
-  mlp_chunk<4>(X, sA, sH, a, 0, lane, wave);
-  mlp_chunk<4>(X, sA, sH, a, 1, lane, wave);
-  mlp_chunk<4>(X, sA, sH, a, 2, lane, wave);
-  mlp_chunk<4>(X, sA, sH, a, 3, lane, wave);
-  mlp_chunk<2>(X, sA, sH, a, 4, lane, wave);
+  // 4. MLP: the 1,152 intermediate columns in 4 chunks of 256 and one of 128,
+  //    chunk c's GEGLU output in buffer c % 2.  Step c (between barriers)
+  //    completes chunk c's GEGLU and runs chunk c-1's W_out.  Waves 0-3 run
+  //    [W_out(c-1), W_i(c), GEGLU(c)]; waves 4-7 run [GEGLU(c), W_out(c-1),
+  //    W_i(c+1)], keeping the W_i accumulators across the barrier.  On every
+  //    SIMD one wave's GEGLU arithmetic then overlaps its partner's
+  //    matrix-core work.  X receives the chunks in order.
+  const bool lead = wave < NW / 2;
+  f32x4 H[4][4];
+  wi_gemm<4>(H, sA, a, 0, lane, wave);
+  geglu<4>(H, sH0, lane, wave);
+  if (!lead) wi_gemm<4>(H, sA, a, 1, lane, wave);
+  __syncthreads();
+#pragma unroll 1
+  for (int c = 1; c < 3; ++c) {
+    bf16 *prev = (c & 1) ? sH0 : sH1, *cur = (c & 1) ? sH1 : sH0;
+    if (lead) {
+      mlp_out<4>(X, prev, a, c - 1, lane, wave);
+      wi_gemm<4>(H, sA, a, c, lane, wave);
+      geglu<4>(H, cur, lane, wave);
+    } else {
+      geglu<4>(H, cur, lane, wave);
+      mlp_out<4>(X, prev, a, c - 1, lane, wave);
+      wi_gemm<4>(H, sA, a, c + 1, lane, wave);
+    }
+    __syncthreads();
+  }
+  if (lead) {
+    mlp_out<4>(X, sH0, a, 2, lane, wave);
+    wi_gemm<4>(H, sA, a, 3, lane, wave);
+    geglu<4>(H, sH1, lane, wave);
+  } else {
+    geglu<4>(H, sH1, lane, wave);
+    mlp_out<4>(X, sH0, a, 2, lane, wave);
+    wi_gemm<2>(H, sA, a, 4, lane, wave);
+  }
+  __syncthreads();
+  if (lead) {
+    mlp_out<4>(X, sH1, a, 3, lane, wave);
+    wi_gemm<2>(H, sA, a, 4, lane, wave);
+    geglu<2>(H, sH0, lane, wave);
+  } else {
+    geglu<2>(H, sH0, lane, wave);
+    mlp_out<4>(X, sH1, a, 3, lane, wave);
+  }
+  __syncthreads();
+  mlp_out<2>(X, sH0, a, 4, lane, wave);
 
   // 5. after the last layer: h = LayerNorm_final(X) + type row, into x
   if (a.Wqkv_next == nullptr && a.final_norm != nullptr) {
@@ -357,26 +459,17 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   __syncthreads();
   // q and k (12 heads): heads 0-7 one per wave (4 groups: d 0-15, 16-31 and
   // their RoPE partners 32-47, 48-63), then heads 8-11 two waves each (the
-  // wave's half h: groups h and h + 2).
-  rope_heads<4>(sA, sCos, sSin, a, 64 * wave, 0, lane, row0, T);
-  rope_heads<2>(sA, sCos, sSin, a, 512 + 64 * (wave >> 1), wave & 1, lane, row0, T);
-  // v: 384 columns, wave w columns 48w .. 48w+47 (X's registers are free again)
-  zero(X);
-  {
-    const int ng[3] = {48 + 3 * wave, 48 + 3 * wave + 1, 48 + 3 * wave + 2};
-    gemm_rows<3, KSD, 4>(X, sA, a.Wqkv_next, KSD, ng, 0, lane);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = row0 + 16 * i + r16;
-    if (row >= T) continue;
-    bf16 *v = a.qkv_out + (size_t)row * (3 * kWidth) + 2 * kWidth + 48 * wave + 4 * g;
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      bf16x4 t;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] = (bf16)X[i][j][r];
-      *reinterpret_cast<bf16x4 *>(v + 16 * j) = t;
+  // wave's half h: groups h and h + 2); then v.  Waves 4-7 take the three
+  // parts in reverse order so that epilogues overlap matrix-core work.
+#pragma unroll 1
+  for (int h = 0; h < 3; ++h) {
+    const int part = wave < NW / 2 ? h : 2 - h;
+    if (part == 0) {
+      rope_heads<4>(sA, sCos, sSin, a, 64 * wave, 0, lane, row0, T);
+    } else if (part == 1) {
+      rope_heads<2>(sA, sCos, sSin, a, 512 + 64 * (wave >> 1), wave & 1, lane, row0, T);
+    } else {
+      project_v(X, sA, a, lane, wave, row0, T);
     }
   }
 }
