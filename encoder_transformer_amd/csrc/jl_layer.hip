@@ -4,18 +4,20 @@
 // Per block, with its 64 rows resident in LDS and registers:
 //   1. x += o . W_o^T                      (attention out-projection, residual)
 //   2. u  = LayerNorm_mlp(x)               (row statistics across the 8 waves)
-//   3. x += GEGLU(u . W_i^T) . W_out^T     (intermediate in chunks of 128 columns,
-//                                           never stored outside LDS)
+//   3. x += GEGLU(u . W_i^T) . W_out^T     (intermediate in chunks of 256
+//                                           columns, never stored outside LDS)
 //   4. either u' = LayerNorm_attn(next)(x); qkv = u' . W_qkv(next)^T with RoPE
 //      on q and k (stored bf16 for the next attention),
 //      or, after the last layer, h = LayerNorm_final(x) + type row.
 //
-// 512 threads = 8 waves, two per SIMD, so one wave's vector work (LayerNorm,
-// GEGLU, RoPE) overlaps the other's matrix-core work.  The weights stream
+// 512 threads = 8 waves, two per SIMD.  Waves 0-3 and 4-7 run the MLP and
+// QKV phases in rotated orders, so that on each SIMD one wave's vector work
+// (GEGLU, RoPE) overlaps its partner's matrix-core work.  The weights stream
 // from L2 straight into matrix-core fragments: at load they are pre-packed so
 // that each (16 output columns x 32 k) block is the 1 KB a wave consumes, one
-// coalesced load, issued 4 k-steps ahead.  The activations (LayerNorm output,
-// GEGLU chunk) sit in LDS in fragment order.
+// coalesced buffer load; every GEMM runs on a "weight pipe" whose first
+// k-steps were issued during the previous GEMM or before an epilogue.  The
+// activations (LayerNorm output, GEGLU chunk) sit in LDS in fragment order.
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16 with the weight fragment as the A
 // operand and the activation fragment as B, so the accumulator is C^T: lane
@@ -72,31 +74,51 @@ DI bf16x8 ldw(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// acc[i][j] += (A_tile(LDS, 64 x 32*KSTEPS) . Wp^T)^T sub-tiles for this wave's
-// NT groups of 16 output columns (group ng[j]), k-steps ks0 .. ks0+KSTEPS-1 of
-// Wp.  Weight fragments for PD k-steps are in flight: each register is
-// reloaded right after the MFMAs that read it; activation fragments are
-// double-buffered one step ahead.  Fully unrolled.
-template <int NT, int KSTEPS, int PD, int NTA = NT>
-DI void gemm_rows(f32x4 (&acc)[4][NTA], const bf16 *sAt, const bf16 *__restrict__ Wp, int w_ksteps,
-                  const int (&ng)[NT], int ks0, int lane) {
-  static_assert(NT <= NTA, "accumulator columns");
-  static_assert(PD <= KSTEPS, "prefetch depth");
-  const __amdgpu_buffer_rsrc_t rw = weight_rsrc(Wp);
+// A weight pipe: PD k-steps of a wave's NT fragment columns in flight.
+template <int NT, int PD>
+struct WPipe {
+  const bf16 *W;
   int vo[NT];
+  bf16x8 fb[PD][NT];
+};
+
+// Issue the first PD k-steps of the fragments of groups ng[j] (k-steps ks0 ..)
+// of a packed weight with w_ksteps k-steps per group.
+template <int NT, int PD>
+DI void wp_start(WPipe<NT, PD> &w, const bf16 *Wp, int w_ksteps, const int (&ng)[NT], int ks0, int lane) {
+  w.W = Wp;
+  const __amdgpu_buffer_rsrc_t rw = weight_rsrc(Wp);
 #pragma unroll
-  for (int j = 0; j < NT; ++j) vo[j] = ((ng[j] * w_ksteps + ks0) * 64 + lane) * 16;
-  const bf16 *ap = sAt + lane * 8;
-  bf16x8 fb[PD][NT], fa[2][4];
+  for (int j = 0; j < NT; ++j) w.vo[j] = ((ng[j] * w_ksteps + ks0) * 64 + lane) * 16;
 #pragma unroll
   for (int p = 0; p < PD; ++p)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) fb[p][j] = ldw(rw, vo[j], p * 1024);
+    for (int j = 0; j < NT; ++j) w.fb[p][j] = ldw(rw, w.vo[j], p * 1024);
+}
+
+struct NoNext {
+  DI void operator()() const {}
+};
+
+// acc[i][j] += (A_tile(LDS, 64 x 32*KSTEPS) . W^T)^T for a started pipe: each
+// fragment register is reloaded right after the MFMAs that read it;
+// activation fragments are double-buffered one step ahead.  `next()` runs at
+// the start of the last PD steps, once every load of this GEMM is issued: it
+// starts the wave's next pipe, so that GEMM begins with its fragments in
+// flight.  Fully unrolled.
+template <int KSTEPS, int NT, int PD, int NTA, class Next>
+DI void wp_run(f32x4 (&acc)[4][NTA], WPipe<NT, PD> &w, const bf16 *sAt, int lane, Next next) {
+  static_assert(NT <= NTA, "accumulator columns");
+  static_assert(PD <= KSTEPS, "prefetch depth");
+  const __amdgpu_buffer_rsrc_t rw = weight_rsrc(w.W);
+  const bf16 *ap = sAt + lane * 8;
+  bf16x8 fa[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) fa[0][i] = lds8(ap + (i * KSTEPS) * 512);
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     const int p = s % PD;
+    if (s == KSTEPS - PD) next();
     if (s + 1 < KSTEPS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) fa[(s + 1) & 1][i] = lds8(ap + (i * KSTEPS + s + 1) * 512);
@@ -105,10 +127,10 @@ DI void gemm_rows(f32x4 (&acc)[4][NTA], const bf16 *sAt, const bf16 *__restrict_
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[p][j], fa[s & 1][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w.fb[p][j], fa[s & 1][i], acc[i][j], 0, 0, 0);
     if (s + PD < KSTEPS) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) fb[p][j] = ldw(rw, vo[j], (s + PD) * 1024);
+      for (int j = 0; j < NT; ++j) w.fb[p][j] = ldw(rw, w.vo[j], (s + PD) * 1024);
     }
     // keep each reload right behind the MFMAs that free its registers: the
     // scheduler would otherwise sink the reloads towards the next wait
@@ -201,24 +223,60 @@ DI void write_ln(const f32x4 (&X)[4][3], const float *__restrict__ gain, const f
   }
 }
 
-// q/k columns head_col .. head_col+63 of one head for this block's rows, RoPE
-// applied: NT = 4 covers the whole head, NT = 2 the half `half` (d in
-// 16 half .. 16 half + 15 and its partners d + 32).
-template <int NT>
-DI void rope_heads(const bf16 *sA, const float *sCos, const float *sSin, const LayerArgs &a,
-                                  int head_col, int half, int lane, int row0, int T) {
-  const int r16 = lane & 15, g = lane >> 4;
-  f32x4 H[4][NT];
-  zero(H);
-  int ng[NT];
-  if (NT == 4) {
+// Pipe types: out-projection, W_out and v (3 groups); W_i chunks of 256 and
+// the whole-head q/k (4 groups); the last W_i chunk and the half-head q/k (2).
+constexpr int PDO = 3, PDI = 2, PD2 = 4;
+using PipeO = WPipe<3, PDO>;
+using PipeI = WPipe<4, PDI>;
+using Pipe2 = WPipe<2, PD2>;
+
+// W_i chunk c (outputs 256 c .. 256 c + 64 NTI - 1, i.e. 128 NTI interleaved
+// rows): wave w's (GELU group, gate group) pairs, groups 32 c + NTI w + j.
+template <int NTI, int PD>
+DI void start_wi(WPipe<NTI, PD> &w, const LayerArgs &a, int c, int lane, int wave) {
+  int ng[NTI];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) ng[j] = head_col / 16 + j;
-  } else {
-    ng[0] = head_col / 16 + half;
-    ng[1] = head_col / 16 + half + 2;
-  }
-  gemm_rows<NT, KSD, (NT == 4 ? 2 : 4)>(H, sA, a.Wqkv_next, KSD, ng, 0, lane);
+  for (int j = 0; j < NTI; ++j) ng[j] = 32 * c + NTI * wave + j;
+  wp_start(w, a.Wi, KSD, ng, 0, lane);
+}
+// W_out k-steps of chunk c for wave w's 48 output columns.
+DI void start_wout(PipeO &w, const LayerArgs &a, int c, int lane, int wave) {
+  const int ng[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
+  wp_start(w, a.Wout, kGeglu / 32, ng, 8 * c, lane);
+}
+// Next layer's q/k of one whole head (wave w: head w) or of half a head
+// (heads 8-11, two waves each: groups half and half + 2), and v (wave w:
+// columns 48 w .. 48 w + 47).
+DI void start_qk_whole(PipeI &w, const LayerArgs &a, int lane, int wave) {
+  const int ng[4] = {4 * wave, 4 * wave + 1, 4 * wave + 2, 4 * wave + 3};
+  wp_start(w, a.Wqkv_next, KSD, ng, 0, lane);
+}
+DI void start_qk_half(Pipe2 &w, const LayerArgs &a, int lane, int wave) {
+  const int base = 32 + 4 * (wave >> 1), half = wave & 1;
+  const int ng[2] = {base + half, base + half + 2};
+  wp_start(w, a.Wqkv_next, KSD, ng, 0, lane);
+}
+DI void start_v(PipeO &w, const LayerArgs &a, int lane, int wave) {
+  const int ng[3] = {48 + 3 * wave, 48 + 3 * wave + 1, 48 + 3 * wave + 2};
+  wp_start(w, a.Wqkv_next, KSD, ng, 0, lane);
+}
+
+template <int NTA>
+DI void zero_cols(f32x4 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NTA; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// RoPE on q/k accumulators and store: NT = 4 holds a whole head (columns
+// head_col .. head_col + 63, groups d 0-15, 16-31, 32-47, 48-63), NT = 2 the
+// half `half` (groups d 16 half .. and d 32 + 16 half ..).  Rotation pairs
+// are (d, d + 32).
+template <int NT>
+DI void rope_store(const f32x4 (&H)[4][4], const float *sCos, const float *sSin, const LayerArgs &a,
+                   int head_col, int half, int lane, int row0, int T) {
+  const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int jp = 0; jp < NT / 2; ++jp) {
     const int d0 = 16 * (NT == 4 ? jp : half) + 4 * g;  // this lane's rotation indices d0 .. d0+3
@@ -242,14 +300,9 @@ DI void rope_heads(const bf16 *sA, const float *sCos, const float *sSin, const L
   }
 }
 
-// v = u' . W_v^T for this block's rows: 384 columns, wave w columns
-// 48w .. 48w+47 (reusing X's registers).
-DI void project_v(f32x4 (&X)[4][3], const bf16 *sA, const LayerArgs &a, int lane, int wave, int row0,
-                                 int T) {
+// v accumulators (wave w: columns 48 w .. 48 w + 47) to bf16.
+DI void v_store(const f32x4 (&V)[4][3], const LayerArgs &a, int lane, int wave, int row0, int T) {
   const int r16 = lane & 15, g = lane >> 4;
-  zero(X);
-  const int ng[3] = {48 + 3 * wave, 48 + 3 * wave + 1, 48 + 3 * wave + 2};
-  gemm_rows<3, KSD, 4>(X, sA, a.Wqkv_next, KSD, ng, 0, lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = row0 + 16 * i + r16;
@@ -259,25 +312,10 @@ DI void project_v(f32x4 (&X)[4][3], const bf16 *sA, const LayerArgs &a, int lane
     for (int j = 0; j < 3; ++j) {
       bf16x4 t;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] = (bf16)X[i][j][r];
+      for (int r = 0; r < 4; ++r) t[r] = (bf16)V[i][j][r];
       *reinterpret_cast<bf16x4 *>(v + 16 * j) = t;
     }
   }
-}
-
-// MLP chunk c covers outputs 256 c .. 256 c + 64 NTI - 1 (NTI = 4: 256
-// outputs, NTI = 2: the last 128), i.e. 128 NTI interleaved W_i rows.
-// wi_gemm: wave w's (GELU group, gate group) pairs of the chunk into H[.][0, NTI).
-template <int NTI>
-DI void wi_gemm(f32x4 (&H)[4][4], const bf16 *sA, const LayerArgs &a, int c, int lane, int wave) {
-  int ng[NTI];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NTI; ++j) H[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < NTI; ++j) ng[j] = 32 * c + NTI * wave + j;  // a full chunk is 32 groups of 16 rows
-  gemm_rows<NTI, KSD, (NTI == 4 ? 3 : 4), 4>(H, sA, a.Wi, KSD, ng, 0, lane);
 }
 
 // gelu(z) * g for a gate value gh = g / 2 (the packed W_i carries the gate
@@ -314,14 +352,6 @@ DI void geglu(const f32x4 (&H)[4][4], bf16 *sHb, int lane, int wave) {
   }
 }
 
-// X (wave w: columns 48w .. 48w+47) += chunk buffer . W_out^T over the
-// chunk's k-range.
-template <int NTI>
-DI void mlp_out(f32x4 (&X)[4][3], const bf16 *sHb, const LayerArgs &a, int c, int lane, int wave) {
-  const int ngo[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
-  gemm_rows<3, 2 * NTI, 4>(X, sHb, a.Wout, kGeglu / 32, ngo, 8 * c, lane);
-}
-
 __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sA[RB * kWidth];  // 48 KB: o, then u, then u'
   __shared__ __attribute__((aligned(16))) bf16 sH0[RB * 256];    // 32 KB: GEGLU chunk buffers,
@@ -333,6 +363,19 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   const int r16 = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * RB;
   const int T = a.T;
+  const bool lead = wave < NW / 2;
+  const bool next_layer = a.Wqkv_next != nullptr;
+
+  // Every GEMM below runs on a weight pipe started during the previous GEMM's
+  // last steps or before an epilogue, so none begins with an empty pipeline.
+  // Waves take two pipe types in turn.
+  PipeO po;
+  PipeI pi;
+  Pipe2 p2;
+  {
+    const int ngo[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
+    wp_start(po, a.Wo, KSD, ngo, 0, lane);  // needs nothing: first
+  }
 
   // 1. attention output rows -> sA (fragment order); the RoPE table rows of
   //    this block's positions -> LDS, for the next layer's q and k
@@ -341,7 +384,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
     const int src = min(row0 + r, T - 1);
     *reinterpret_cast<bf16x8 *>(&sA[afrag(r, k, KSD)]) = ldg8(a.o + (size_t)src * kWidth + k);
   }
-  if (a.Wqkv_next != nullptr) {
+  if (next_layer) {
     for (int c = tid; c < RB * 8; c += 512) {  // 64 rows x 8 float4 of each table
       const int r = c >> 3, q = (c & 7) * 4;
       const int p = a.pos[min(row0 + r, T - 1)];
@@ -354,10 +397,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   // 2. X = x + o . W_o^T   (wave w: columns 48w .. 48w+47, 3 groups of 16)
   f32x4 X[4][3];
   zero(X);
-  {
-    const int ng[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
-    gemm_rows<3, KSD, 4>(X, sA, a.Wo, KSD, ng, 0, lane);
-  }
+  wp_run<KSD>(X, po, sA, lane, [&] { start_wi(pi, a, 0, lane, wave); });
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = min(row0 + 16 * i + r16, T - 1);
@@ -379,49 +419,64 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   //    W_i(c+1)], keeping the W_i accumulators across the barrier.  On every
   //    SIMD one wave's GEGLU arithmetic then overlaps its partner's
   //    matrix-core work.  X receives the chunks in order.
-  const bool lead = wave < NW / 2;
   f32x4 H[4][4];
-  wi_gemm<4>(H, sA, a, 0, lane, wave);
-  geglu<4>(H, sH0, lane, wave);
-  if (!lead) wi_gemm<4>(H, sA, a, 1, lane, wave);
-  __syncthreads();
+  if (lead) {
+    zero_cols<4>(H);
+    wp_run<KSD>(H, pi, sA, lane, NoNext());
+    start_wout(po, a, 0, lane, wave);
+    geglu<4>(H, sH0, lane, wave);
+    __syncthreads();
 #pragma unroll 1
-  for (int c = 1; c < 3; ++c) {
-    bf16 *prev = (c & 1) ? sH0 : sH1, *cur = (c & 1) ? sH1 : sH0;
-    if (lead) {
-      mlp_out<4>(X, prev, a, c - 1, lane, wave);
-      wi_gemm<4>(H, sA, a, c, lane, wave);
+    for (int c = 1; c < 4; ++c) {
+      bf16 *prev = (c & 1) ? sH0 : sH1, *cur = (c & 1) ? sH1 : sH0;
+      wp_run<8>(X, po, prev, lane, [&] { start_wi(pi, a, c, lane, wave); });
+      zero_cols<4>(H);
+      wp_run<KSD>(H, pi, sA, lane, NoNext());
+      start_wout(po, a, c, lane, wave);
       geglu<4>(H, cur, lane, wave);
-    } else {
-      geglu<4>(H, cur, lane, wave);
-      mlp_out<4>(X, prev, a, c - 1, lane, wave);
-      wi_gemm<4>(H, sA, a, c + 1, lane, wave);
+      __syncthreads();
     }
+    wp_run<8>(X, po, sH1, lane, [&] { start_wi(p2, a, 4, lane, wave); });
+    zero_cols<2>(H);
+    wp_run<KSD>(H, p2, sA, lane, NoNext());
+    start_wout(po, a, 4, lane, wave);
+    geglu<2>(H, sH0, lane, wave);
+    __syncthreads();
+  } else {
+    zero_cols<4>(H);
+    wp_run<KSD>(H, pi, sA, lane, NoNext());
+    start_wi(pi, a, 1, lane, wave);
+    geglu<4>(H, sH0, lane, wave);
+    zero_cols<4>(H);
+    wp_run<KSD>(H, pi, sA, lane, NoNext());
+    start_wout(po, a, 0, lane, wave);
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 1; c < 3; ++c) {
+      bf16 *prev = (c & 1) ? sH0 : sH1, *cur = (c & 1) ? sH1 : sH0;
+      geglu<4>(H, cur, lane, wave);
+      wp_run<8>(X, po, prev, lane, [&] { start_wi(pi, a, c + 1, lane, wave); });
+      zero_cols<4>(H);
+      wp_run<KSD>(H, pi, sA, lane, NoNext());
+      start_wout(po, a, c, lane, wave);
+      __syncthreads();
+    }
+    geglu<4>(H, sH1, lane, wave);
+    wp_run<8>(X, po, sH0, lane, [&] { start_wi(p2, a, 4, lane, wave); });
+    zero_cols<2>(H);
+    wp_run<KSD>(H, p2, sA, lane, NoNext());
+    start_wout(po, a, 3, lane, wave);
+    __syncthreads();
+    geglu<2>(H, sH0, lane, wave);
+    wp_run<8>(X, po, sH1, lane, NoNext());
+    start_wout(po, a, 4, lane, wave);
     __syncthreads();
   }
-  if (lead) {
-    mlp_out<4>(X, sH0, a, 2, lane, wave);
-    wi_gemm<4>(H, sA, a, 3, lane, wave);
-    geglu<4>(H, sH1, lane, wave);
-  } else {
-    geglu<4>(H, sH1, lane, wave);
-    mlp_out<4>(X, sH0, a, 2, lane, wave);
-    wi_gemm<2>(H, sA, a, 4, lane, wave);
-  }
-  __syncthreads();
-  if (lead) {
-    mlp_out<4>(X, sH1, a, 3, lane, wave);
-    wi_gemm<2>(H, sA, a, 4, lane, wave);
-    geglu<2>(H, sH0, lane, wave);
-  } else {
-    geglu<2>(H, sH0, lane, wave);
-    mlp_out<4>(X, sH1, a, 3, lane, wave);
-  }
-  __syncthreads();
-  mlp_out<2>(X, sH0, a, 4, lane, wave);
+  // last W_out
+  wp_run<4>(X, po, sH0, lane, NoNext());
 
   // 5. after the last layer: h = LayerNorm_final(X) + type row, into x
-  if (a.Wqkv_next == nullptr && a.final_norm != nullptr) {
+  if (!next_layer && a.final_norm != nullptr) {
     row_stats(X, sRed, lane, wave, mean, rstd);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -451,26 +506,39 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) *reinterpret_cast<f32x4 *>(xr + 16 * j) = X[i][j];
   }
-  if (a.Wqkv_next == nullptr) return;  // residual only (hidden-state diagnostics)
+  if (!next_layer) return;  // residual only (hidden-state diagnostics)
 
-  // 6. next layer: u' = LayerNorm_attn(X) -> sA; qkv = u' . W_qkv^T
+  // 6. next layer: u' = LayerNorm_attn(X) -> sA; qkv = u' . W_qkv^T.  q and k
+  //    (12 heads): heads 0-7 one per wave, heads 8-11 two waves each; v:
+  //    48 columns per wave.  Waves 0-3 take [whole head, half head, v],
+  //    waves 4-7 [half head, v, whole head], so epilogues overlap
+  //    matrix-core work.
   row_stats(X, sRed, lane, wave, mean, rstd);
   write_ln(X, a.attn_norm_next, mean, rstd, sA, lane, wave);
   __syncthreads();
-  // q and k (12 heads): heads 0-7 one per wave (4 groups: d 0-15, 16-31 and
-  // their RoPE partners 32-47, 48-63), then heads 8-11 two waves each (the
-  // wave's half h: groups h and h + 2); then v.  Waves 4-7 take the three
-  // parts in reverse order so that epilogues overlap matrix-core work.
-#pragma unroll 1
-  for (int h = 0; h < 3; ++h) {
-    const int part = wave < NW / 2 ? h : 2 - h;
-    if (part == 0) {
-      rope_heads<4>(sA, sCos, sSin, a, 64 * wave, 0, lane, row0, T);
-    } else if (part == 1) {
-      rope_heads<2>(sA, sCos, sSin, a, 512 + 64 * (wave >> 1), wave & 1, lane, row0, T);
-    } else {
-      project_v(X, sA, a, lane, wave, row0, T);
-    }
+  const int half_col = 512 + 64 * (wave >> 1), half = wave & 1;
+  if (lead) {
+    start_qk_whole(pi, a, lane, wave);
+    zero_cols<4>(H);
+    wp_run<KSD>(H, pi, sA, lane, [&] { start_qk_half(p2, a, lane, wave); });
+    rope_store<4>(H, sCos, sSin, a, 64 * wave, 0, lane, row0, T);
+    zero_cols<2>(H);
+    wp_run<KSD>(H, p2, sA, lane, [&] { start_v(po, a, lane, wave); });
+    rope_store<2>(H, sCos, sSin, a, half_col, half, lane, row0, T);
+    zero(X);
+    wp_run<KSD>(X, po, sA, lane, NoNext());
+    v_store(X, a, lane, wave, row0, T);
+  } else {
+    start_qk_half(p2, a, lane, wave);
+    zero_cols<2>(H);
+    wp_run<KSD>(H, p2, sA, lane, [&] { start_v(po, a, lane, wave); });
+    rope_store<2>(H, sCos, sSin, a, half_col, half, lane, row0, T);
+    zero(X);
+    wp_run<KSD>(X, po, sA, lane, [&] { start_qk_whole(pi, a, lane, wave); });
+    v_store(X, a, lane, wave, row0, T);
+    zero_cols<4>(H);
+    wp_run<KSD>(H, pi, sA, lane, NoNext());
+    rope_store<4>(H, sCos, sSin, a, 64 * wave, 0, lane, row0, T);
   }
 }
 
