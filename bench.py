@@ -30,6 +30,7 @@ PEAK_FP32_TFLOPS = 157.3
 HBM_GBPS = 8000.0
 D, FFN_HEAD = 384, 1536
 ROW_BLOCK_MIN_TOKENS = 8192  # bf16 batches this large use the row-block layer kernel
+PROFILE_EVERY = 4
 
 
 def band_pairs(L, w=64):
@@ -76,24 +77,31 @@ def time_workload(model, batch, steps, warmup, profile_class=None):
         model.forward(ids, so, mp, qt, out=logits)
         model.probs(logits, so, mp, qt)
 
+    step()  # first call: code objects load, workspace pages in
+    torch.cuda.synchronize()
     # warm-up with every class timed, to find where the device time goes
-    model.profile(True, (1 << lib.N_KERNEL_CLASSES) - 1)
+    model.profile(1, (1 << lib.N_KERNEL_CLASSES) - 1)
     for _ in range(max(1, warmup)):
         step()
     torch.cuda.synchronize()
     per_class = {lib.KERNEL_CLASS_NAMES[c]: model.profile_read(c) for c in range(lib.N_KERNEL_CLASSES)}
     dominant = max(per_class, key=lambda k: per_class[k][0]) if profile_class is None else profile_class
     cls_id = lib.KERNEL_CLASS_NAMES.index(dominant)
-    model.profile(True, 1 << cls_id)
+    # timed region: the dominant class's launches are bracketed by events in
+    # every PROFILE_EVERY-th step (a sample of the region; the event records
+    # themselves cost the stream a little time)
+    model.profile(1, 0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
+        model.profile(2 if i % PROFILE_EVERY == 0 else 0, 1 << cls_id)
         step()
     torch.cuda.synchronize()
     t = time.perf_counter() - t0
     dom_ms, dom_n = model.profile_read(cls_id)
-    model.profile(False, 0)
-    return t, dominant, dom_ms, dom_n, per_class
+    model.profile(0, 0)
+    sampled = (steps + PROFILE_EVERY - 1) // PROFILE_EVERY
+    return t, dominant, dom_ms, dom_n, per_class, sampled
 
 
 def cpu_baseline():
@@ -119,6 +127,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this size (for HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the forward pass shards by "
@@ -132,14 +142,18 @@ def main():
     model = lib.Model(path, lib.BF16, max_tokens=300_000, max_markers=4096, device=0)
 
     b2 = synth.make_batch(2)
-    t, dom, dom_ms, dom_n, per_class = time_workload(model, b2, args.steps, args.warmup)
+    t, dom, dom_ms, dom_n, per_class, sampled = time_workload(model, b2, args.steps, args.warmup)
     ms_step = 1e3 * t / args.steps
     flops = class_flops(b2, row_block=b2.n_tokens >= ROW_BLOCK_MIN_TOKENS)
     total_flops = sum(flops.values())
     dom_flops_step = flops[dom]
-    achieved = dom_flops_step * args.steps / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
+    achieved = dom_flops_step * sampled / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
+    from encoder_transformer_amd import profiling
+    traffic = profiling.read_traffic(os.path.join(ROOT, "profiles"), dom)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if traffic is None else round(traffic),
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "kernel": dom, "launches": dom_n, "avg_launch_us": round(1e3 * dom_ms / max(1, dom_n), 2)}
 
     result = {
@@ -166,7 +180,7 @@ def main():
         extra["1x1024_ms_per_call"] = round(1e3 * t1 / max(args.steps, 20), 4)
         for name, cfg, st in [("16x8192", 3, 5), ("ragged256", 4, 5)]:
             b = synth.make_batch(cfg)
-            tt, d, dms, dn, _ = time_workload(model, b, st, 2)
+            tt, d, dms, dn, _, _ = time_workload(model, b, st, 2)
             fl = sum(class_flops(b, row_block=b.n_tokens >= ROW_BLOCK_MIN_TOKENS).values())
             extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2),
                            "tokens_per_s": round(b.n_tokens * st / tt, 1),
@@ -175,6 +189,13 @@ def main():
         result["extra"] = extra
     result["ms_per_call_1x1024"] = result.get("extra", {}).get("1x1024_ms_per_call")
     model.close()
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 18  # float32 elements
+        src = torch.empty(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

@@ -925,10 +925,13 @@ extern "C" int jl_probs(jl_model *m, const float *logits_dev, const int32_t *seq
 
 extern "C" int jl_profile(jl_model *m, int enable, uint32_t class_mask) {
   if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (enable < 0 || enable > 2) return fail(JL_ERR_ARG, "enable must be 0, 1 or 2");
   m->prof = enable != 0;
   m->prof_mask = class_mask;
-  m->prof_rec.clear();
-  m->ev_used = 0;
+  if (enable == 1) {
+    m->prof_rec.clear();
+    m->ev_used = 0;
+  }
   return JL_OK;
 }
 

@@ -185,7 +185,8 @@ class Model:
         """bf16 batches with at least this many tokens use the row-block layer kernel."""
         _check(self._lib.jl_set_row_block_min_tokens(self._h, int(min_tokens)))
 
-    def profile(self, enable: bool, class_mask: int = (1 << N_KERNEL_CLASSES) - 1):
+    def profile(self, enable: int, class_mask: int = (1 << N_KERNEL_CLASSES) - 1):
+        """1: on, clearing records; 2: on, keeping them; 0: off (records kept)."""
         _check(self._lib.jl_profile(self._h, int(enable), class_mask))
 
     def profile_read(self, kernel_class: int):

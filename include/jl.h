@@ -162,9 +162,10 @@ enum jl_kernel_class {
   JL_K_NCLASS = 12
 };
 
-/* Turn the per-kernel timer on (1) or off (0); it brackets every launch of
- * the classes in `class_mask` (bit i = class i) with HIP events recorded on
- * the launch stream.  Turning it on clears previous records. */
+/* Per-kernel timer: while on, every launch of the classes in `class_mask`
+ * (bit i = class i) is bracketed by HIP events recorded on the launch stream.
+ * enable = 1 turns it on and clears previous records, 2 turns it on and keeps
+ * them (to time a sample of calls), 0 turns it off and keeps them. */
 int jl_profile(jl_model *m, int enable, uint32_t class_mask);
 
 /* Total device time (ms) and launch count of one class since jl_profile(1).
