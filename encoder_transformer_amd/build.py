@@ -21,8 +21,13 @@ SOURCES = ["jl_kernels.hip", "jl_layer.hip", "jl_api.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# -amdgpu-mfma-vgpr-form keeps matrix-core accumulators in ordinary VGPRs:
+# otherwise the compiler may place them in AGPRs, and every vector operation
+# on them (the attention kernel's online-softmax rescale) then costs a copy
+# out and back.
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 

@@ -235,6 +235,12 @@ __device__ inline int vt_slot(int k) {
   return (k & 32) + ((w >> 2) & 3) * 8 + (w >> 4) * 4 + (w & 3);
 }
 
+// V^T rows in LDS are swizzled in granules of 8 elements (one lane's operand
+// read): granule q of row d sits at q ^ ((d >> 3) & 7).  The staging writes
+// put 8 rows 8 apart into one instruction, which would otherwise all land in
+// the same banks; the reads stay contiguous and conflict-free.
+__device__ inline int vt_swz(int d, int slot) { return ((((slot >> 3) ^ (d >> 3)) & 7) << 3) | (slot & 7); }
+
 template <typename T>
 __device__ inline void store_vt_pair(T *row, int slot, float a, float b);
 template <>
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int c = (tid & 7) * 8;
     store_frag(&sK[buf][(tid >> 3) * KS + c], rk0);
     store_frag(&sK[buf][((tid >> 3) + 32) * KS + c], rk1);
-    const int slot = vt_slot(2 * (tid >> 3));
+    const int slot = vt_swz(c, vt_slot(2 * (tid >> 3)));  // rows c .. c+7 share d >> 3
 #pragma unroll
     for (int e = 0; e < 8; ++e) store_vt_pair<T>(&sV[buf][(c + e) * KS], slot, frag_get(rv0, e), frag_get(rv1, e));
   };
@@ -319,10 +325,30 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 4; ++i) o[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  if (n_tiles <= 0) {  // no key (cannot happen for a valid work list): zero output
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const int qi = wave * QW + 16 * s + ql;
+      if (qi < w.n_q) {
+        T *op = (T *)a.o + (size_t)(w.q_row0 + qi) * a.o_stride + h * kHeadDim + 4 * g;
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) op[ds * 16 + r] = to_elem<T>(0.f);
+      }
+    }
+    return;
   }
+  // unconditional preamble: the first tile's stores wait for every earlier
+  // load (the q fragments), so no wait for them is left inside the loop,
+  // where it would also stall on the next tile's prefetch
+  load_tile(0);
+  store_tile(0);
+  // the q fragments must have arrived before the loop: otherwise the
+  // compiler places their wait at its first use inside the loop, where it
+  // would also stall every iteration on the next tile's prefetch
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) frag_touch(fq[s][0], fq[s][1]);
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int cur = t & 1;
@@ -362,13 +388,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         mt = fmaxf(mt, fmaxf(fmaxf(sc[s][ks][0], sc[s][ks][1]), fmaxf(sc[s][ks][2], sc[s][ks][3])));
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m[s], mt * scale);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[s] - m_use);
-      m[s] = m_new;
-      l[s] *= alpha;
+      // Lazy rescale: o and l keep the reference m[s] until a tile's maximum
+      // exceeds it by more than 8 (exp2 domain), so p <= 2^8; the ratio o / l
+      // is unchanged.  Most tiles after the first need no rescale at all.
+      const float mt_s = mt * scale;
+      const bool grow = mt_s > m[s] + 8.f;
+      if (__any(grow)) {
+        const float m_new = grow ? mt_s : m[s];
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m[s] - m_new) : 1.f;
+        m[s] = m_new;
+        l[s] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[s][i] *= alpha;
+        for (int i = 0; i < 4; ++i) o[s][i] *= alpha;
+      }
+      const float m_use = (m[s] == -INFINITY) ? 0.f : m[s];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -394,7 +427,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) {
-        const Frag<T> vf = load_frag(&sV[cur][(ds * 16 + ql) * KS + kstep * 32 + g * 8]);
+        const int d = ds * 16 + ql;
+        const Frag<T> vf = load_frag(&sV[cur][d * KS + vt_swz(d, kstep * 32 + g * 8)]);
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) mfma(o[s][ds], vf, fp[s]);
       }
