@@ -236,10 +236,14 @@ __device__ inline int vt_slot(int k) {
 }
 
 // V^T rows in LDS are swizzled in granules of 8 elements (one lane's operand
-// read): granule q of row d sits at q ^ ((d >> 3) & 7).  The staging writes
-// put 8 rows 8 apart into one instruction, which would otherwise all land in
-// the same banks; the reads stay contiguous and conflict-free.
-__device__ inline int vt_swz(int d, int slot) { return ((((slot >> 3) ^ (d >> 3)) & 7) << 3) | (slot & 7); }
+// read): granule q of row d sits at q ^ (2 ((d >> 4) & 3)).  The staging
+// writes put 8 rows 8 apart into one instruction, which would otherwise land
+// in the same banks (8-way); with the swizzle they are 2-way, the least this
+// thread mapping allows, while the operand reads (16 consecutive rows, one
+// swizzle value) stay conflict-free.
+__device__ inline int vt_swz(int d, int slot) {
+  return ((((slot >> 3) ^ (((d >> 4) & 3) << 1)) & 7) << 3) | (slot & 7);
+}
 
 template <typename T>
 __device__ inline void store_vt_pair(T *row, int slot, float a, float b);
@@ -261,7 +265,9 @@ __device__ inline void store_vt_pair<float>(float *row, int slot, float a, float
 // sequence end or, on local layers, past the window of some query.
 template <typename T, int NSUB>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  constexpr int KS = 72;  // LDS row stride (elements)
+  // LDS row stride (elements): 80 makes the 16-byte operand reads (16 rows x
+  // 4 chunks per 16 lanes) conflict-free on gfx950; 72 measured 2-way.
+  constexpr int KS = 80;
   constexpr int QW = 16 * NSUB;
   __shared__ __attribute__((aligned(16))) T sK[2][64 * KS];
   __shared__ __attribute__((aligned(16))) T sV[2][64 * KS];  // [d][slot]
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int c = (tid & 7) * 8;
     store_frag(&sK[buf][(tid >> 3) * KS + c], rk0);
     store_frag(&sK[buf][((tid >> 3) + 32) * KS + c], rk1);
-    const int slot = vt_swz(c, vt_slot(2 * (tid >> 3)));  // rows c .. c+7 share d >> 3
+    const int slot = vt_swz(c, vt_slot(2 * (tid >> 3)));  // rows c .. c+7 share d >> 4
 #pragma unroll
     for (int e = 0; e < 8; ++e) store_vt_pair<T>(&sV[buf][(c + e) * KS], slot, frag_get(rv0, e), frag_get(rv1, e));
   };
