@@ -131,6 +131,21 @@ struct jl_model {
   // slot k, so the host may run up to kMetaSlots - 1 calls ahead of the GPU.
   static constexpr int kMetaSlots = 4;
   int *meta[kMetaSlots] = {};
+  // Graph mode: jl_forward replays a captured HIP graph per batch shape; the
+  // graphs read their metadata from this one device buffer, which each call
+  // refills on the stream before its replay.
+  int *gmeta = nullptr;
+  struct GraphEntry {
+    int T, B, M, n_work, n_work_wide;
+    bool row_block;
+    const void *ids, *out;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+    uint64_t last_use;
+  };
+  std::vector<GraphEntry> graphs;
+  int graph_cap = 0;
+  uint64_t graph_clock = 0;
   int *host_meta[kMetaSlots] = {};
   hipEvent_t slot_done[kMetaSlots] = {};
   bool slot_pending[kMetaSlots] = {};
@@ -297,6 +312,10 @@ extern "C" void jl_free(jl_model *m) {
     if (m->host_meta[k]) (void)hipHostFree(m->host_meta[k]);
   }
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
+  for (auto &g : m->graphs) {
+    (void)hipGraphExecDestroy(g.exec);
+    (void)hipGraphDestroy(g.graph);
+  }
   if (m->ws) (void)hipFree(m->ws);
   if (m->warena) (void)hipFree(m->warena);
   delete m;
@@ -528,6 +547,7 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
   reserve((void **)&m->sh, Mm * D * 4);
   reserve((void **)&m->zu, Mm * D * 4);
   for (int k = 0; k < jl_model::kMetaSlots; ++k) reserve((void **)&m->meta[k], m->meta_ints * 4);
+  reserve((void **)&m->gmeta, m->meta_ints * 4);
   m->wsbytes = (off + 255) & ~size_t(255);
   if (hipMalloc((void **)&m->ws, m->wsbytes) != hipSuccess)
     return bail(JL_ERR_OOM, "cannot allocate the device workspace");
@@ -573,7 +593,7 @@ struct Plan {
 
 // Build the metadata in pinned memory and enqueue its upload.
 int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, int32_t M, const int32_t *qt,
-                hipStream_t s, Plan &pl) {
+                hipStream_t s, Plan &pl, bool to_graph_buffer = false) {
   pl.B = B;
   pl.M = M;
   pl.T = so[B];
@@ -585,7 +605,7 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
   }
   pl.slot = slot;
   int *h = m->host_meta[slot];
-  int *dmeta = m->meta[slot];
+  int *dmeta = to_graph_buffer ? m->gmeta : m->meta[slot];
   size_t o = 0;
   const size_t o_so = o;
   for (int b = 0; b <= B; ++b) h[o++] = so[b];
@@ -870,7 +890,62 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   return JL_OK;
 }
 
+// Replay (capturing on first use) the forward pass of this batch shape.
+int forward_graph(jl_model *m, const int32_t *ids, const Plan &pl, float *out, hipStream_t s) {
+  const bool row_block = m->bf16 && pl.T >= m->row_block_min_tokens;
+  jl_model::GraphEntry *hit = nullptr;
+  for (auto &g : m->graphs)
+    if (g.T == pl.T && g.B == pl.B && g.M == pl.M && g.n_work == pl.n_work && g.n_work_wide == pl.n_work_wide &&
+        g.row_block == row_block && g.ids == ids && g.out == out) {
+      hit = &g;
+      break;
+    }
+  if (!hit) {
+    if ((int)m->graphs.size() >= m->graph_cap) {  // evict the least recently used
+      size_t lru = 0;
+      for (size_t i = 1; i < m->graphs.size(); ++i)
+        if (m->graphs[i].last_use < m->graphs[lru].last_use) lru = i;
+      (void)hipGraphExecDestroy(m->graphs[lru].exec);
+      (void)hipGraphDestroy(m->graphs[lru].graph);
+      m->graphs.erase(m->graphs.begin() + lru);
+    }
+    JL_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    const int rc = run_forward(m, ids, pl, 26, out, s);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(s, &g);
+    if (rc != JL_OK) {
+      if (g) (void)hipGraphDestroy(g);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(JL_ERR_DEVICE, std::string("graph capture failed: ") + hipGetErrorString(e));
+    hipGraphExec_t ge = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+    if (ei != hipSuccess) {
+      (void)hipGraphDestroy(g);
+      return fail(JL_ERR_DEVICE, std::string("graph instantiation failed: ") + hipGetErrorString(ei));
+    }
+    m->graphs.push_back({pl.T, pl.B, pl.M, pl.n_work, pl.n_work_wide, row_block, ids, out, g, ge, 0});
+    hit = &m->graphs.back();
+  }
+  hit->last_use = ++m->graph_clock;
+  JL_HIP(hipGraphLaunch(hit->exec, s));
+  return JL_OK;
+}
+
 }  // namespace
+
+extern "C" int jl_set_graph_cache(jl_model *m, int max_graphs) {
+  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (max_graphs < 0 || max_graphs > 64) return fail(JL_ERR_ARG, "max_graphs must be in 0..64");
+  DeviceGuard dg(m->device);
+  for (auto &g : m->graphs) {
+    (void)hipGraphExecDestroy(g.exec);
+    (void)hipGraphDestroy(g.graph);
+  }
+  m->graphs.clear();
+  m->graph_cap = max_graphs;
+  return JL_OK;
+}
 
 extern "C" int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
                           const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, float *logits_dev,
@@ -883,8 +958,11 @@ extern "C" int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *se
   DeviceGuard dg(m->device);
   hipStream_t s = (hipStream_t)stream;
   Plan pl;
-  if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl)) return rc;
-  return finish_plan(m, pl, s, run_forward(m, ids_dev, pl, 26, logits_dev, s));
+  // graphs need a capturable stream and no per-launch timer events
+  const bool use_graph = m->graph_cap > 0 && s != nullptr && !m->prof;
+  if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl, use_graph)) return rc;
+  if (!use_graph) return finish_plan(m, pl, s, run_forward(m, ids_dev, pl, 26, logits_dev, s));
+  return finish_plan(m, pl, s, forward_graph(m, ids_dev, pl, logits_dev, s));
 }
 
 extern "C" int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,

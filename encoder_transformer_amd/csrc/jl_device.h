@@ -44,16 +44,6 @@ __device__ inline float frag_get(const Frag<bf16> &f, int e) { return (float)f.v
 __device__ inline float frag_get(const Frag<float> &f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
 
 // Build a fragment from 8 FP32 values (bf16: round to nearest even).
-// An empty instruction that reads the fragments: everything that produces
-// them (loads in flight) must have completed here.  Emits no code.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ inline void frag_touch(const Frag<bf16> &a, const Frag<bf16> &b) {
-  asm volatile("" ::"v"(__builtin_bit_cast(i32x4, a.v)), "v"(__builtin_bit_cast(i32x4, b.v)));
-}
-__device__ inline void frag_touch(const Frag<float> &a, const Frag<float> &b) {
-  asm volatile("" ::"v"(a.lo), "v"(a.hi), "v"(b.lo), "v"(b.hi));
-}
-
 __device__ inline void frag_from(Frag<bf16> &f, const float *v) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) f.v[e] = (bf16)v[e];

@@ -235,6 +235,16 @@ __device__ inline int vt_slot(int k) {
   return (k & 32) + ((w >> 2) & 3) * 8 + (w >> 4) * 4 + (w & 3);
 }
 
+// An empty instruction that reads the fragments: everything that produces
+// them (loads in flight) must have completed here.  Emits no code.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ inline void frag_touch(const Frag<bf16> &a, const Frag<bf16> &b) {
+  asm volatile("" ::"v"(__builtin_bit_cast(i32x4, a.v)), "v"(__builtin_bit_cast(i32x4, b.v)));
+}
+__device__ inline void frag_touch(const Frag<float> &a, const Frag<float> &b) {
+  asm volatile("" ::"v"(a.lo), "v"(a.hi), "v"(b.lo), "v"(b.hi));
+}
+
 // V^T rows in LDS are swizzled in granules of 8 elements (one lane's operand
 // read): granule q of row d sits at q ^ (2 ((d >> 4) & 3)).  The staging
 // writes put 8 rows 8 apart into one instruction, which would otherwise land

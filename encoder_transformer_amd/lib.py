@@ -67,6 +67,8 @@ def load_library():
     L.jl_probs.argtypes = [vp, vp, _i32p, i32, _i32p, i32, _i32p, vp, vp, vp, vp, vp]
     L.jl_debug_hidden.restype = ctypes.c_int
     L.jl_debug_hidden.argtypes = [vp, vp, _i32p, i32, _i32p, i32, _i32p, i32, vp, vp]
+    L.jl_set_graph_cache.restype = ctypes.c_int
+    L.jl_set_graph_cache.argtypes = [vp, ctypes.c_int]
     L.jl_profile.restype = ctypes.c_int
     L.jl_profile.argtypes = [vp, ctypes.c_int, ctypes.c_uint32]
     L.jl_profile_read.restype = ctypes.c_int
@@ -184,6 +186,10 @@ class Model:
     def set_row_block_min_tokens(self, min_tokens: int):
         """bf16 batches with at least this many tokens use the row-block layer kernel."""
         _check(self._lib.jl_set_row_block_min_tokens(self._h, int(min_tokens)))
+
+    def set_graph_cache(self, max_graphs: int):
+        """Replay jl_forward from captured HIP graphs, keeping up to max_graphs shapes (0: off)."""
+        _check(self._lib.jl_set_graph_cache(self._h, int(max_graphs)))
 
     def profile(self, enable: int, class_mask: int = (1 << N_KERNEL_CLASSES) - 1):
         """1: on, clearing records; 2: on, keeping them; 0: off (records kept)."""

@@ -144,6 +144,21 @@ int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offs
  */
 int jl_set_row_block_min_tokens(jl_model *m, int64_t min_tokens);
 
+/*
+ * Graph mode: with max_graphs > 0, jl_forward captures its launch sequence
+ * for each batch shape into a HIP graph on first use and replays it after
+ * (per-launch host cost ~10 us becomes one graph launch; this matters for
+ * small batches, whose forward pass is ~180 launches).  A shape is the token,
+ * marker and sequence counts, the attention work-item counts, the schedule
+ * and the ids_dev / logits_dev pointers; up to max_graphs shapes are kept,
+ * least recently used evicted.  Each call still uploads its own batch
+ * metadata first (to one graph-owned device buffer, ordered on the stream),
+ * so any batch of a cached shape is computed exactly as eagerly.  Calls on
+ * the NULL stream, and calls while the per-kernel timer is on, run eagerly.
+ * 0 (the default) turns graphs off and releases the cached graphs; at most 64.
+ */
+int jl_set_graph_cache(jl_model *m, int max_graphs);
+
 /* Kernel classes reported by the per-kernel timer. */
 enum jl_kernel_class {
   JL_K_EMBED = 0,      /* embedding gather + LayerNorm                         */
