@@ -934,6 +934,8 @@ int forward_graph(jl_model *m, const int32_t *ids, const Plan &pl, float *out, h
 
 }  // namespace
 
+int jl::set_error(int code, const char *msg) { return fail(code, msg); }
+
 extern "C" int jl_set_graph_cache(jl_model *m, int max_graphs) {
   if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
   if (max_graphs < 0 || max_graphs > 64) return fail(JL_ERR_ARG, "max_graphs must be in 0..64");

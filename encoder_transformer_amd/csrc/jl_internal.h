@@ -105,4 +105,7 @@ hipError_t launch_probs(const float *logits, const int *marker_offsets, const in
                         int n_seqs, float *probs, float *answer, int *argmax, float *maxprob,
                         hipStream_t s);
 
+// Sets the calling thread's jl_last_error() message; returns `code`.
+int set_error(int code, const char *msg);
+
 }  // namespace jl

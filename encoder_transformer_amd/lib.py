@@ -30,6 +30,10 @@ N_KERNEL_CLASSES = len(KERNEL_CLASS_NAMES)
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _f32p = ctypes.POINTER(ctypes.c_float)
+# int score(void *user, const int32_t *ids, const int32_t *seq_offsets, int32_t n_seqs,
+#           const int32_t *mask_positions, int32_t n_markers, float *probs)
+SCORE_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, _i32p, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32,
+                            _f32p)
 _lib = None
 
 
@@ -69,6 +73,13 @@ def load_library():
     L.jl_debug_hidden.argtypes = [vp, vp, _i32p, i32, _i32p, i32, _i32p, i32, vp, vp]
     L.jl_set_graph_cache.restype = ctypes.c_int
     L.jl_set_graph_cache.argtypes = [vp, ctypes.c_int]
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    route_io = [i32, _i32p, i64p, _i32p, i64p, _i32p, i64p, _i32p, i32,
+                _i32p, _f32p, _i32p, _i32p, _f32p, _i32p, _i32p]
+    L.jl_route.restype = ctypes.c_int
+    L.jl_route.argtypes = [vp] + route_io + [vp]
+    L.jl_route_with_scorer.restype = ctypes.c_int
+    L.jl_route_with_scorer.argtypes = [SCORE_FN, vp, i64, i64] + route_io
     L.jl_profile.restype = ctypes.c_int
     L.jl_profile.argtypes = [vp, ctypes.c_int, ctypes.c_uint32]
     L.jl_profile_read.restype = ctypes.c_int
@@ -99,6 +110,61 @@ def _i32(a) -> np.ndarray:
 
 def _p(a: np.ndarray):
     return a.ctypes.data_as(_i32p)
+
+
+class RouteResult:
+    """Per question: pick (question-local option index), pick_prob, final
+    candidates and their final probabilities, groups scored, rounds."""
+
+    def __init__(self, pick, pick_prob, n_final, final_idx, final_prob, calls, rounds):
+        self.pick, self.pick_prob, self.calls, self.rounds = pick, pick_prob, calls, rounds
+        self.final = [list(final_idx[q, :n_final[q]]) for q in range(len(pick))]
+        self.final_prob = [final_prob[q, :n_final[q]].copy() for q in range(len(pick))]
+
+
+def _route_args(questions, mask_id):
+    """questions: list of (prefix ids, suffix ids, [option ids, ...])."""
+    nq = len(questions)
+    cat = lambda parts: _i32(np.concatenate([np.asarray(p, np.int32) for p in parts])) if parts else _i32([])
+    offs = lambda parts: np.ascontiguousarray(np.concatenate([[0], np.cumsum([len(p) for p in parts])]), np.int64)
+    prefixes = [q[0] for q in questions]
+    suffixes = [q[1] for q in questions]
+    options = [o for q in questions for o in q[2]]
+    q_opts = _i32(np.concatenate([[0], np.cumsum([len(q[2]) for q in questions])]))
+    arrays = [cat(prefixes), offs(prefixes), cat(suffixes), offs(suffixes), cat(options), offs(options), q_opts]
+    out = [np.zeros(nq, np.int32), np.zeros(nq, np.float32), np.zeros(nq, np.int32),
+           np.zeros((nq, 20), np.int32), np.zeros((nq, 20), np.float32), np.zeros(nq, np.int32),
+           np.zeros(nq, np.int32)]
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    ptr = lambda a: a.ctypes.data_as(i64p if a.dtype == np.int64 else (_f32p if a.dtype == np.float32 else _i32p))
+    args = [nq] + [ptr(a) for a in arrays] + [mask_id] + [ptr(a) for a in out]
+    return args, arrays, out
+
+
+def route_with_scorer(score, questions, mask_id: int = 4, max_tokens: int = 65536,
+                      max_markers: int = 4096) -> RouteResult:
+    """The router with a Python scorer: score(ids, seq_offsets, mask_positions)
+    returns the option probabilities (NumPy, one per marker)."""
+    failure = []
+
+    def cb(_user, ids, so, n_seqs, mp, n_markers, probs):
+        try:
+            so_a = np.ctypeslib.as_array(so, (n_seqs + 1,)).copy()
+            ids_a = np.ctypeslib.as_array(ids, (int(so_a[-1]),)).copy() if so_a[-1] > 0 else np.zeros(0, np.int32)
+            mp_a = np.ctypeslib.as_array(mp, (n_markers,)).copy()
+            p = np.asarray(score(ids_a, so_a, mp_a), np.float32)
+            np.ctypeslib.as_array(probs, (n_markers,))[:] = p
+            return 0
+        except Exception as e:  # noqa: BLE001 - re-raised below
+            failure.append(e)
+            return ERR_ARG
+    fn = SCORE_FN(cb)
+    args, _keep, out = _route_args(questions, mask_id)
+    rc = load_library().jl_route_with_scorer(fn, None, max_tokens, max_markers, *args)
+    if rc != 0 and failure:
+        raise failure[0]
+    _check(rc)
+    return RouteResult(*out)
 
 
 def validate(seq_offsets, mask_positions, qtype, max_tokens: int, max_markers: int) -> None:
@@ -186,6 +252,12 @@ class Model:
     def set_row_block_min_tokens(self, min_tokens: int):
         """bf16 batches with at least this many tokens use the row-block layer kernel."""
         _check(self._lib.jl_set_row_block_min_tokens(self._h, int(min_tokens)))
+
+    def route(self, questions, mask_id: int = 4, stream=None) -> RouteResult:
+        """The router (jl_route) over questions of (prefix ids, suffix ids, [option ids, ...])."""
+        args, _keep, out = _route_args(questions, mask_id)
+        _check(self._lib.jl_route(self._h, *args, self._stream(stream)))
+        return RouteResult(*out)
 
     def set_graph_cache(self, max_graphs: int):
         """Replay jl_forward from captured HIP graphs, keeping up to max_graphs shapes (0: off)."""

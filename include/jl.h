@@ -159,6 +159,64 @@ int jl_set_row_block_min_tokens(jl_model *m, int64_t min_tokens);
  */
 int jl_set_graph_cache(jl_model *m, int max_graphs);
 
+/*
+ * Router: choice questions with more than 20 options ("Julia-1: one score per
+ * mask token ...", More than 20 options: the Router).  Per question, the
+ * candidates are split, in order, into consecutive groups of at most 20; every
+ * group is scored as one choice question; a group keeps its winner alone when
+ * the winner's probability is above 0.95 and every other option's is below
+ * 0.045, else its top two; rounds repeat until at most 20 candidates remain,
+ * then one final call scores them.  Readings where the page is silent: a group
+ * of a single candidate passes it on unscored; survivors keep their order;
+ * ties go to the earlier candidate.  All groups of all questions in a round
+ * share one packed jl_forward call (several when the handle's capacity is
+ * exceeded).
+ *
+ * Each question's scored sequence is
+ *     prefix, then (mask_id, option tokens) for each of its candidates, then suffix
+ * (the prefix holds everything before the first option marker, the suffix
+ * everything after the last option), with question type choice.
+ *   n_questions        number of questions (0 is valid).
+ *   prefix_ids / prefix_offsets [n_questions+1]: concatenated prefixes.
+ *   suffix_ids / suffix_offsets [n_questions+1]: concatenated suffixes.
+ *   option_ids / option_offsets [n_options_total+1]: concatenated options of
+ *              all questions, each 1 or more tokens.
+ *   question_options [n_questions+1]: question q owns options
+ *              question_options[q] .. question_options[q+1]-1; 2 to 4,096 each.
+ * Outputs (host memory, caller-owned): pick[q] the chosen option's index
+ * within its question, pick_prob[q] its final probability, n_final[q] the
+ * final candidate count (<= 20), final_idx/final_prob [n_questions x 20] the
+ * final candidates (question-local indices, in order) and their final
+ * probabilities, calls[q] the groups scored for the question (final call
+ * included), rounds[q] the rounds before the final call.  Any of calls,
+ * rounds, final_idx, final_prob, n_final may be NULL.
+ * Errors: JL_ERR_ARG for malformed inputs, JL_ERR_LENGTH when one group's
+ * sequence is longer than 8,192 tokens or the handle's capacity; plus those of
+ * jl_forward.  Synchronous: returns when the pick is known.
+ */
+int jl_route(jl_model *m, int32_t n_questions, const int32_t *prefix_ids, const int64_t *prefix_offsets,
+             const int32_t *suffix_ids, const int64_t *suffix_offsets, const int32_t *option_ids,
+             const int64_t *option_offsets, const int32_t *question_options, int32_t mask_id,
+             int32_t *pick, float *pick_prob, int32_t *n_final, int32_t *final_idx, float *final_prob,
+             int32_t *calls, int32_t *rounds, void *stream);
+
+/*
+ * The same tournament with a caller-supplied scorer instead of the model, for
+ * other engines and for testing the rule on the host: `score` receives one
+ * packed batch (host arrays; question type choice for every sequence) and
+ * writes the option probabilities [n_markers] (softmax across each sequence's
+ * markers), returning 0 or an error code, which aborts the routing.  Batches
+ * hold at most max_tokens tokens and max_markers markers.
+ */
+typedef int (*jl_score_fn)(void *user, const int32_t *ids, const int32_t *seq_offsets, int32_t n_seqs,
+                           const int32_t *mask_positions, int32_t n_markers, float *probs);
+int jl_route_with_scorer(jl_score_fn score, void *user, int64_t max_tokens, int64_t max_markers,
+                         int32_t n_questions, const int32_t *prefix_ids, const int64_t *prefix_offsets,
+                         const int32_t *suffix_ids, const int64_t *suffix_offsets, const int32_t *option_ids,
+                         const int64_t *option_offsets, const int32_t *question_options, int32_t mask_id,
+                         int32_t *pick, float *pick_prob, int32_t *n_final, int32_t *final_idx,
+                         float *final_prob, int32_t *calls, int32_t *rounds);
+
 /* Kernel classes reported by the per-kernel timer. */
 enum jl_kernel_class {
   JL_K_EMBED = 0,      /* embedding gather + LayerNorm                         */
