@@ -11,10 +11,11 @@ the ragged serving mix (256 sequences of 64-2,048 tokens).
 
 `roofline` covers the kernel class with the most device time in the timed
 region, measured with HIP events bracketing each of its launches on the
-launch stream; `cpu_baseline` times the CPU oracle on two of the 1,024-token
+launch stream; `cpu_baseline` times the CPU oracle on six of the 1,024-token
 sequences. Prints one JSON line.
 """
 import argparse
+import gc
 import json
 import os
 import sys
@@ -42,25 +43,31 @@ def class_flops(batch, row_block):
     """Algorithmic FLOPs per step of each kernel class (masked work not counted).
 
     `row_block`: the bf16 path for large batches, where one layer kernel per
-    layer runs the out-projection, the MLP and the next layer's QKV.
+    layer runs the out-projection, the MLP and the next layer's QKV (the last
+    one the head's first in-projection), and one head-layer kernel the rest of
+    the first head layer and the second's keys and values.
     """
     lens = np.diff(batch.seq_offsets).astype(np.int64)
     T, M = int(lens.sum()), batch.n_markers
     glob = int(np.sum(lens * lens))
     band = sum(band_pairs(int(L)) for L in lens)
     qkv, outp, mlp_in, mlp_out = 2 * T * D * 3 * D, 2 * T * D * D, 2 * T * D * 2304, 2 * T * 1152 * D
-    f = {k: 0 for k in ("embed", "qkv", "outproj", "mlp_in", "mlp_out", "layer", "ln")}
+    f = {k: 0 for k in ("embed", "qkv", "outproj", "mlp_in", "mlp_out", "layer", "head_layer", "ln")}
+    # head layer 1 on every token (in-projection, out-projection, feed-forward),
+    # layer 2 keys/values on every token and the rest on marker rows
+    head_in, head_rest, head_kv = 2 * T * D * 3 * D, 2 * T * D * (D + 2 * FFN_HEAD), 2 * T * D * 2 * D
+    head_markers = 2 * M * D * (D + D + 2 * FFN_HEAD)
     if row_block:
         f["qkv"] = qkv
-        f["layer"] = 22 * (outp + mlp_in + mlp_out) + 21 * qkv
+        f["layer"] = 22 * (outp + mlp_in + mlp_out) + 21 * qkv + head_in
+        f["head_layer"] = head_rest + head_kv
+        f["head_gemm"] = head_markers
     else:
         f.update(qkv=22 * qkv, outproj=22 * outp, mlp_in=22 * mlp_in, mlp_out=22 * mlp_out)
+        f["head_gemm"] = head_in + head_rest + head_kv + head_markers
     f["attn_global"] = 8 * 1536 * glob
     f["attn_local"] = 14 * 1536 * band
-    # head layer 1 on every token, layer 2 keys/values on every token and the
-    # rest on marker rows, attention of marker queries over their sequence
-    f["head_gemm"] = (2 * T * D * (3 * D + D + 2 * FFN_HEAD) + 2 * T * D * 2 * D
-                      + 2 * M * D * (D + D + 2 * FFN_HEAD))
+    # attention of marker queries over their sequence
     f["head_attn"] = 1536 * glob + 1536 * int(sum(len(batch.sequence(b)[1]) * lens[b] for b in range(batch.n_seqs)))
     f["misc"] = 2 * M * D * D + 2 * M * D
     return f
@@ -96,12 +103,21 @@ def time_workload(model, batch, steps, warmup, profile_class=None):
     # themselves cost the stream a little time)
     model.profile(1, 0)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        model.profile(2 if i % PROFILE_EVERY == 0 else 0, 1 << cls_id)
-        step()
-    torch.cuda.synchronize()
-    t = time.perf_counter() - t0
+    # Python's cyclic garbage collector is paused in the timed region (as
+    # timeit does): a full collection of this interpreter's heap stalls the
+    # host for ~40 ms, which starves the GPU and belongs to the calling
+    # program, not to the library
+    gc.collect()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            model.profile(2 if i % PROFILE_EVERY == 0 else 0, 1 << cls_id)
+            step()
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t0
+    finally:
+        gc.enable()
     dom_ms, dom_n = model.profile_read(cls_id)
     model.profile(0, 0)
     sampled = (steps + PROFILE_EVERY - 1) // PROFILE_EVERY

@@ -92,6 +92,10 @@ struct HeadW {
   const void *in_w = nullptr, *out_w = nullptr, *l1_w = nullptr, *l2_w = nullptr;
   const float *in_b = nullptr, *out_b = nullptr, *l1_b = nullptr, *l2_b = nullptr;
   const float *n1_w = nullptr, *n1_b = nullptr, *n2_w = nullptr, *n2_b = nullptr;
+  // bf16 fragment-ordered copies for the row-block kernels: the first layer's
+  // in-projection, out-projection and feed-forward; the second layer's key
+  // and value rows of the in-projection
+  const void *pIn = nullptr, *pOut = nullptr, *pL1 = nullptr, *pL2 = nullptr, *pKV = nullptr;
 };
 
 struct ProfRec {
@@ -449,18 +453,23 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     HeadW &h = m->H[j];
     GET(p + "self_attn.in_proj_weight", 3 * D, D);
     put_elem(t, 3 * D, D, &h.in_w, nullptr);
+    if (bf && j == 0) put_packed(t, 3 * D, D, &h.pIn, nullptr);
+    if (bf && j == 1) put_packed(t + (size_t)D * D, 2 * D, D, &h.pKV, nullptr);
     GET(p + "self_attn.in_proj_bias", 3 * D);
     put_f32(t, 3 * D, &h.in_b);
     GET(p + "self_attn.out_proj.weight", D, D);
     put_elem(t, D, D, &h.out_w, nullptr);
+    if (bf && j == 0) put_packed(t, D, D, &h.pOut, nullptr);
     GET(p + "self_attn.out_proj.bias", D);
     put_f32(t, D, &h.out_b);
     GET(p + "linear1.weight", (uint32_t)kHeadFfn, D);
     put_elem(t, kHeadFfn, D, &h.l1_w, nullptr);
+    if (bf && j == 0) put_packed(t, kHeadFfn, D, &h.pL1, nullptr);
     GET(p + "linear1.bias", (uint32_t)kHeadFfn);
     put_f32(t, kHeadFfn, &h.l1_b);
     GET(p + "linear2.weight", D, (uint32_t)kHeadFfn);
     put_elem(t, D, kHeadFfn, &h.l2_w, nullptr);
+    if (bf && j == 0) put_packed(t, D, kHeadFfn, &h.pL2, nullptr);
     GET(p + "linear2.bias", D);
     put_f32(t, D, &h.l2_b);
     GET(p + "norm1.weight", D);
@@ -674,7 +683,6 @@ int finish_plan(jl_model *m, const Plan &pl, hipStream_t s, int rc) {
     JL_HIP(hipStreamSynchronize(s));
   }
   return rc;
-  return JL_OK;
 }
 
 hipEvent_t prof_event(jl_model *m) {
@@ -766,7 +774,8 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   at.o = m->o;
   at.o_stride = D;
   at.work = pl.d_aw;
-  if (bf && T >= m->row_block_min_tokens) {
+  const bool row_block = bf && T >= m->row_block_min_tokens;
+  if (row_block) {
     // Row-block path: one attention launch and one layer launch per layer.
     {
       const LayerW &W0 = m->L[0];
@@ -804,6 +813,13 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
         la.type_rows = m->type_rows;
         la.qtype = pl.d_qt;
         la.tok_seq = m->tok_seq;
+        if (stop != kLayers + 1) {  // continue into the head's first attention input
+          const HeadW &H = m->H[0];
+          la.attn_norm_next = H.n1_w;
+          la.attn_shift_next = H.n1_b;
+          la.Wqkv_next = (const __bf16 *)H.pIn;
+          la.qkv_bias_next = H.in_b;
+        }
       }
       JL_LAUNCH(JL_K_LAYER, launch_layer(la, s));
       if (stop == l + 1) return copy_out(m->x, T);
@@ -833,31 +849,63 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   }
   if (stop == 23) return copy_out(m->x, T);
 
-  // head layer 1 over every token
+  // head layer 1 over every token (row-block path: its LayerNorm and
+  // in-projection ran in the last encoder layer's kernel; everything after
+  // its attention, with the second layer's keys and values, in one kernel)
+  char *kv = m->qkv;  // head layer 2's keys and values, [T, 768]: k then v
   {
     const HeadW &H = m->H[0];
-    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n1_w, H.n1_b, T, u, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_STORE, gemm(u, D, H.in_w, D, H.in_b, m->qkv, 3 * D, T, 3 * D, D), s));
+    if (!row_block) {
+      JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n1_w, H.n1_b, T, u, s));
+      JL_LAUNCH(JL_K_HEAD_GEMM,
+                launch_gemm(bf, E_STORE, gemm(u, D, H.in_w, D, H.in_b, m->qkv, 3 * D, T, 3 * D, D), s));
+    }
     at.half_window = -1;
     JL_LAUNCH(JL_K_HEAD_ATTN, attention(bf, at, pl, true, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->o, D, H.out_w, D, H.out_b, m->x, D, T, D, D), s));
-    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n2_w, H.n2_b, T, u, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM,
-              launch_gemm(bf, E_RELU, gemm(u, D, H.l1_w, D, H.l1_b, m->act, kHeadFfn, T, kHeadFfn, D), s));
-    JL_LAUNCH(JL_K_HEAD_GEMM,
-              launch_gemm(bf, E_RESID, gemm(m->act, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, m->x, D, T, D, kHeadFfn), s));
+    if (row_block) {
+      const HeadW &N = m->H[1];
+      HeadArgs ha{};
+      ha.x = m->x;
+      ha.o = (const __bf16 *)m->o;
+      ha.Wo = (const __bf16 *)H.pOut;
+      ha.bo = H.out_b;
+      ha.n2_w = H.n2_w;
+      ha.n2_b = H.n2_b;
+      ha.W1 = (const __bf16 *)H.pL1;
+      ha.b1 = H.l1_b;
+      ha.W2 = (const __bf16 *)H.pL2;
+      ha.b2 = H.l2_b;
+      if (stop != 24) {
+        ha.nk_w = N.n1_w;
+        ha.nk_b = N.n1_b;
+        ha.Wkv = (const __bf16 *)N.pKV;
+        ha.bkv = N.in_b + D;
+        ha.kv_out = (__bf16 *)kv;
+      }
+      ha.T = T;
+      JL_LAUNCH(JL_K_HEAD_LAYER, launch_head_layer(ha, s));
+    } else {
+      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->o, D, H.out_w, D, H.out_b, m->x, D, T, D, D), s));
+      JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n2_w, H.n2_b, T, u, s));
+      JL_LAUNCH(JL_K_HEAD_GEMM,
+                launch_gemm(bf, E_RELU, gemm(u, D, H.l1_w, D, H.l1_b, m->act, kHeadFfn, T, kHeadFfn, D), s));
+      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID,
+                                            gemm(m->act, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, m->x, D, T, D, kHeadFfn),
+                                            s));
+    }
   }
   if (stop == 24) return copy_out(m->x, T);
 
   // head layer 2: keys and values for every token, the rest at marker rows only
   {
     const HeadW &H = m->H[1];
-    char *kv = m->qkv;  // [T, 768]: k then v
-    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n1_w, H.n1_b, T, u, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_STORE,
-                                          gemm(u, D, (const char *)H.in_w + (size_t)D * D * es, D, H.in_b + D, kv,
-                                               2 * D, T, 2 * D, D),
-                                          s));
+    if (!row_block) {
+      JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n1_w, H.n1_b, T, u, s));
+      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_STORE,
+                                            gemm(u, D, (const char *)H.in_w + (size_t)D * D * es, D, H.in_b + D, kv,
+                                                 2 * D, T, 2 * D, D),
+                                            s));
+    }
     JL_LAUNCH(JL_K_MISC, launch_gather_rows(m->x, pl.d_mp, M, m->z, s));
     char *um = m->om;  // normalized marker rows, then the marker attention output
     JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->z, H.n1_w, H.n1_b, M, um, s));

@@ -77,12 +77,39 @@ struct LayerArgs {
   const __bf16 *Wqkv_next;      // fragment-packed [1152 x 384]; nullptr after the last layer
                                 // (with final_norm == nullptr too: store the residual only)
   const float *rope_cos_next, *rope_sin_next;
+  // After the last layer, with final_norm set: the first head layer's
+  // attention input instead of a next encoder layer (Wqkv_next = its packed
+  // in-projection, attn_norm_next / attn_shift_next its pre-norm, no RoPE).
+  const float *attn_shift_next; // pre-norm shift, or nullptr
+  const float *qkv_bias_next;   // [1152] in-projection bias; non-null selects the head mode
   const int *pos;               // [T] position inside the sequence
   __bf16 *qkv_out;              // [T, 1152]
   const float *final_norm;      // after the last layer: final LayerNorm gain,
   const float *type_rows;       //   type table [3, 384],
   const int *qtype;             //   question type per sequence,
   const int *tok_seq;           //   sequence of each token
+  int T;
+};
+
+// Row-block head-layer kernel (bf16 only): everything of one head layer
+// (torch pre-norm encoder layer) after its attention -- biased out-projection
+// + residual, LayerNorm with shift, ReLU feed-forward with biases + residual
+// -- then the next head layer's LayerNorm and biased key/value projection.
+struct HeadArgs {
+  float *x;                     // [T, 384] residual stream (updated in place)
+  const __bf16 *o;              // [T, 384] attention output of this layer
+  const __bf16 *Wo;             // fragment-packed [384 x 384]
+  const float *bo;              // [384]
+  const float *n2_w, *n2_b;     // feed-forward pre-norm gain and shift
+  const __bf16 *W1;             // fragment-packed [1536 x 384]
+  const float *b1;              // [1536]
+  const __bf16 *W2;             // fragment-packed [384 x 1536]
+  const float *b2;              // [384]
+  const float *nk_w, *nk_b;     // next layer's attention pre-norm gain and shift
+  const __bf16 *Wkv;            // fragment-packed [768 x 384]: the next layer's key and
+                                // value rows; nullptr: store the residual only
+  const float *bkv;             // [768]
+  __bf16 *kv_out;               // [T, 768]: keys, then values
   int T;
 };
 
@@ -95,6 +122,7 @@ hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, cons
                           hipStream_t s);
 hipError_t launch_attention(bool bf16, const AttnArgs &a, int n_work, int queries_per_block, hipStream_t s);
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s);
+hipError_t launch_head_layer(const HeadArgs &a, hipStream_t s);
 hipError_t launch_final_ln_type(const float *x, const float *gain, const float *type_rows,
                                 const int *qtype, const int *tok_seq, int T, float *h,
                                 hipStream_t s);

@@ -207,19 +207,27 @@ DI void row_stats(const f32x4 (&X)[4][3], float (*sRed)[RB], int lane, int wave,
   __syncthreads();
 }
 
-// sA = bf16(gain * (X - mean) * rstd), fragment order over the full width.
-DI void write_ln(const f32x4 (&X)[4][3], const float *__restrict__ gain, const float (&mean)[4],
-                                const float (&rstd)[4], bf16 *sA, int lane, int wave) {
+// sA = bf16(gain * (X - mean) * rstd [+ shift]), fragment order over the full width.
+template <bool kShift>
+DI void write_ln(const f32x4 (&X)[4][3], const float *__restrict__ gain, const float *__restrict__ shift,
+                 const float (&mean)[4], const float (&rstd)[4], bf16 *sA, int lane, int wave) {
   const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int col = 48 * wave + 16 * j + 4 * g;
     const f32x4 gm = *reinterpret_cast<const f32x4 *>(gain + col);
+    f32x4 sh = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kShift) sh = *reinterpret_cast<const f32x4 *>(shift + col);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      put4(sA, 16 * i + r16, col, KSD, (X[i][j][0] - mean[i]) * rstd[i] * gm[0],
-           (X[i][j][1] - mean[i]) * rstd[i] * gm[1], (X[i][j][2] - mean[i]) * rstd[i] * gm[2],
-           (X[i][j][3] - mean[i]) * rstd[i] * gm[3]);
+    for (int i = 0; i < 4; ++i) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = (X[i][j][r] - mean[i]) * rstd[i] * gm[r];
+        if constexpr (kShift) v[r] = v[r] + sh[r];
+      }
+      put4(sA, 16 * i + r16, col, KSD, v[0], v[1], v[2], v[3]);
+    }
   }
 }
 
@@ -247,17 +255,32 @@ DI void start_wout(PipeO &w, const LayerArgs &a, int c, int lane, int wave) {
 // Next layer's q/k of one whole head (wave w: head w) or of half a head
 // (heads 8-11, two waves each: groups half and half + 2), and v (wave w:
 // columns 48 w .. 48 w + 47).
+DI void ng_qk_whole(int (&ng)[4], int wave) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ng[j] = 4 * wave + j;
+}
+DI void ng_qk_half(int (&ng)[2], int wave) {
+  const int base = 32 + 4 * (wave >> 1), half = wave & 1;
+  ng[0] = base + half;
+  ng[1] = base + half + 2;
+}
+DI void ng_v(int (&ng)[3], int wave) {
+#pragma unroll
+  for (int j = 0; j < 3; ++j) ng[j] = 48 + 3 * wave + j;
+}
 DI void start_qk_whole(PipeI &w, const LayerArgs &a, int lane, int wave) {
-  const int ng[4] = {4 * wave, 4 * wave + 1, 4 * wave + 2, 4 * wave + 3};
+  int ng[4];
+  ng_qk_whole(ng, wave);
   wp_start(w, a.Wqkv_next, KSD, ng, 0, lane);
 }
 DI void start_qk_half(Pipe2 &w, const LayerArgs &a, int lane, int wave) {
-  const int base = 32 + 4 * (wave >> 1), half = wave & 1;
-  const int ng[2] = {base + half, base + half + 2};
+  int ng[2];
+  ng_qk_half(ng, wave);
   wp_start(w, a.Wqkv_next, KSD, ng, 0, lane);
 }
 DI void start_v(PipeO &w, const LayerArgs &a, int lane, int wave) {
-  const int ng[3] = {48 + 3 * wave, 48 + 3 * wave + 1, 48 + 3 * wave + 2};
+  int ng[3];
+  ng_v(ng, wave);
   wp_start(w, a.Wqkv_next, KSD, ng, 0, lane);
 }
 
@@ -318,6 +341,28 @@ DI void v_store(const f32x4 (&V)[4][3], const LayerArgs &a, int lane, int wave, 
   }
 }
 
+// Biased projection columns to bf16 rows of `out` (row stride `stride`):
+// accumulator column j holds output columns 16 ng[j] .. 16 ng[j] + 15.
+template <int NT, int NTA>
+DI void bias_store(const f32x4 (&H)[4][NTA], const int (&ng)[NT], const float *bias, bf16 *out, int stride,
+                   int lane, int row0, int T) {
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int col = 16 * ng[j] + 4 * g;
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(bias + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + 16 * i + r16;
+      if (row >= T) continue;
+      bf16x4 t;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] = (bf16)(H[i][j][r] + b[r]);
+      *reinterpret_cast<bf16x4 *>(out + (size_t)row * stride + col) = t;
+    }
+  }
+}
+
 // gelu(z) * g for a gate value gh = g / 2 (the packed W_i carries the gate
 // rows halved): gelu(z) = (z + |z| erf(|z| / sqrt 2)) / 2, erf from
 // Abramowitz & Stegun 7.1.26 (|error| <= 1.5e-7), erf = 1 - t P(t) exp(-x^2),
@@ -352,6 +397,9 @@ DI void geglu(const f32x4 (&H)[4][4], bf16 *sHb, int lane, int wave) {
   }
 }
 
+// kHeadNext: after the last layer, continue into the first head layer's
+// LayerNorm (with shift) and biased in-projection, without RoPE.
+template <bool kHeadNext>
 __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sA[RB * kWidth];  // 48 KB: o, then u, then u'
   __shared__ __attribute__((aligned(16))) bf16 sH0[RB * 256];    // 32 KB: GEGLU chunk buffers,
@@ -384,7 +432,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
     const int src = min(row0 + r, T - 1);
     *reinterpret_cast<bf16x8 *>(&sA[afrag(r, k, KSD)]) = ldg8(a.o + (size_t)src * kWidth + k);
   }
-  if (next_layer) {
+  if (!kHeadNext && next_layer) {
     for (int c = tid; c < RB * 8; c += 512) {  // 64 rows x 8 float4 of each table
       const int r = c >> 3, q = (c & 7) * 4;
       const int p = a.pos[min(row0 + r, T - 1)];
@@ -409,7 +457,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   // 3. u = LayerNorm_mlp(X) -> sA (the syncs in row_stats also retire every read of o)
   float mean[4], rstd[4];
   row_stats(X, sRed, lane, wave, mean, rstd);
-  write_ln(X, a.mlp_norm, mean, rstd, sA, lane, wave);
+  write_ln<false>(X, a.mlp_norm, nullptr, mean, rstd, sA, lane, wave);
   __syncthreads();
 
   // 4. MLP: the 1,152 intermediate columns in 4 chunks of 256 and one of 128,
@@ -475,78 +523,256 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   // last W_out
   wp_run<4>(X, po, sH0, lane, NoNext());
 
-  // 5. after the last layer: h = LayerNorm_final(X) + type row, into x
-  if (!next_layer && a.final_norm != nullptr) {
+  // 5. after the last layer: h = LayerNorm_final(X) + type row, into x (in
+  //    head mode also kept in X for the head's first layer); otherwise the
+  //    residual stream
+  if constexpr (kHeadNext) {
     row_stats(X, sRed, lane, wave, mean, rstd);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = row0 + 16 * i + r16;
-      if (row >= T) continue;
-      const float *tr = a.type_rows + (size_t)a.qtype[a.tok_seq[row]] * kWidth;
+      const float *tr = a.type_rows + (size_t)a.qtype[a.tok_seq[min(row, T - 1)]] * kWidth;
       float *xr = a.x + (size_t)row * kWidth;
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         const int col = 48 * wave + 16 * j + 4 * g;
         const f32x4 gm = *reinterpret_cast<const f32x4 *>(a.final_norm + col);
         const f32x4 ty = *reinterpret_cast<const f32x4 *>(tr + col);
-        f32x4 h;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) h[r] = (X[i][j][r] - mean[i]) * rstd[i] * gm[r] + ty[r];
-        *reinterpret_cast<f32x4 *>(xr + col) = h;
+        for (int r = 0; r < 4; ++r) X[i][j][r] = (X[i][j][r] - mean[i]) * rstd[i] * gm[r] + ty[r];
+        if (row < T) *reinterpret_cast<f32x4 *>(xr + col) = X[i][j];
       }
     }
-    return;
-  }
-  // otherwise store the residual stream
+  } else {
+    if (!next_layer && a.final_norm != nullptr) {
+      row_stats(X, sRed, lane, wave, mean, rstd);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = row0 + 16 * i + r16;
-    if (row >= T) continue;
-    float *xr = a.x + (size_t)row * kWidth + 48 * wave + 4 * g;
+      for (int i = 0; i < 4; ++i) {
+        const int row = row0 + 16 * i + r16;
+        if (row >= T) continue;
+        const float *tr = a.type_rows + (size_t)a.qtype[a.tok_seq[row]] * kWidth;
+        float *xr = a.x + (size_t)row * kWidth;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) *reinterpret_cast<f32x4 *>(xr + 16 * j) = X[i][j];
+        for (int j = 0; j < 3; ++j) {
+          const int col = 48 * wave + 16 * j + 4 * g;
+          const f32x4 gm = *reinterpret_cast<const f32x4 *>(a.final_norm + col);
+          const f32x4 ty = *reinterpret_cast<const f32x4 *>(tr + col);
+          f32x4 h;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = (X[i][j][r] - mean[i]) * rstd[i] * gm[r] + ty[r];
+          *reinterpret_cast<f32x4 *>(xr + col) = h;
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + 16 * i + r16;
+      if (row >= T) continue;
+      float *xr = a.x + (size_t)row * kWidth + 48 * wave + 4 * g;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) *reinterpret_cast<f32x4 *>(xr + 16 * j) = X[i][j];
+    }
+    if (!next_layer) return;  // residual only (hidden-state diagnostics)
   }
-  if (!next_layer) return;  // residual only (hidden-state diagnostics)
 
-  // 6. next layer: u' = LayerNorm_attn(X) -> sA; qkv = u' . W_qkv^T.  q and k
-  //    (12 heads): heads 0-7 one per wave, heads 8-11 two waves each; v:
-  //    48 columns per wave.  Waves 0-3 take [whole head, half head, v],
+  // 6. next layer: u' = LayerNorm_attn(next)(X) -> sA; qkv = u' . W_qkv^T.
+  //    q and k (12 heads): heads 0-7 one per wave, heads 8-11 two waves each;
+  //    v: 48 columns per wave.  Waves 0-3 take [whole head, half head, v],
   //    waves 4-7 [half head, v, whole head], so epilogues overlap
-  //    matrix-core work.
+  //    matrix-core work.  Encoder layers rotate q and k; the head's first
+  //    layer adds the in-projection bias instead.
   row_stats(X, sRed, lane, wave, mean, rstd);
-  write_ln(X, a.attn_norm_next, mean, rstd, sA, lane, wave);
+  write_ln<kHeadNext>(X, a.attn_norm_next, a.attn_shift_next, mean, rstd, sA, lane, wave);
   __syncthreads();
   const int half_col = 512 + 64 * (wave >> 1), half = wave & 1;
+  int ngw[4], ngh[2], ngv[3];
+  ng_qk_whole(ngw, wave);
+  ng_qk_half(ngh, wave);
+  ng_v(ngv, wave);
+  constexpr int QS = 3 * kWidth;
   if (lead) {
     start_qk_whole(pi, a, lane, wave);
     zero_cols<4>(H);
     wp_run<KSD>(H, pi, sA, lane, [&] { start_qk_half(p2, a, lane, wave); });
-    rope_store<4>(H, sCos, sSin, a, 64 * wave, 0, lane, row0, T);
+    if constexpr (kHeadNext) bias_store<4>(H, ngw, a.qkv_bias_next, a.qkv_out, QS, lane, row0, T);
+    else rope_store<4>(H, sCos, sSin, a, 64 * wave, 0, lane, row0, T);
     zero_cols<2>(H);
     wp_run<KSD>(H, p2, sA, lane, [&] { start_v(po, a, lane, wave); });
-    rope_store<2>(H, sCos, sSin, a, half_col, half, lane, row0, T);
+    if constexpr (kHeadNext) bias_store<2>(H, ngh, a.qkv_bias_next, a.qkv_out, QS, lane, row0, T);
+    else rope_store<2>(H, sCos, sSin, a, half_col, half, lane, row0, T);
     zero(X);
     wp_run<KSD>(X, po, sA, lane, NoNext());
-    v_store(X, a, lane, wave, row0, T);
+    if constexpr (kHeadNext) bias_store<3>(X, ngv, a.qkv_bias_next, a.qkv_out, QS, lane, row0, T);
+    else v_store(X, a, lane, wave, row0, T);
   } else {
     start_qk_half(p2, a, lane, wave);
     zero_cols<2>(H);
     wp_run<KSD>(H, p2, sA, lane, [&] { start_v(po, a, lane, wave); });
-    rope_store<2>(H, sCos, sSin, a, half_col, half, lane, row0, T);
+    if constexpr (kHeadNext) bias_store<2>(H, ngh, a.qkv_bias_next, a.qkv_out, QS, lane, row0, T);
+    else rope_store<2>(H, sCos, sSin, a, half_col, half, lane, row0, T);
     zero(X);
     wp_run<KSD>(X, po, sA, lane, [&] { start_qk_whole(pi, a, lane, wave); });
-    v_store(X, a, lane, wave, row0, T);
+    if constexpr (kHeadNext) bias_store<3>(X, ngv, a.qkv_bias_next, a.qkv_out, QS, lane, row0, T);
+    else v_store(X, a, lane, wave, row0, T);
     zero_cols<4>(H);
     wp_run<KSD>(H, pi, sA, lane, NoNext());
-    rope_store<4>(H, sCos, sSin, a, 64 * wave, 0, lane, row0, T);
+    if constexpr (kHeadNext) bias_store<4>(H, ngw, a.qkv_bias_next, a.qkv_out, QS, lane, row0, T);
+    else rope_store<4>(H, sCos, sSin, a, 64 * wave, 0, lane, row0, T);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Head layer (torch pre-norm encoder layer, biases everywhere) after its
+// attention, for 64 token rows per work-group, with the same weight pipes and
+// fragment-order LDS tiles as the encoder layer:
+//   1. x += o . W_o^T + b_o
+//   2. u  = LayerNorm_2(x)                          (gain and shift)
+//   3. x += relu(u . W_1^T + b_1) . W_2^T + b_2     (1,536 hidden columns in 6
+//                                                    chunks of 256, LDS only)
+//   4. store x; then the next head layer's u' = LayerNorm_1(next)(x) and its
+//      keys and values u' . W_kv^T + b_kv (bf16, [T, 768]).
+// The ReLU epilogue is a few operations per value, so all 8 waves run the
+// same order: W_1 chunk, epilogue, barrier, W_2 chunk.
+
+constexpr int KSF = kHeadFfn / 32;  // 48 k-steps over the head's hidden width
+constexpr int kHeadChunks = kHeadFfn / 256;
+
+// W_1 chunk c (hidden columns 256 c .. 256 c + 255): wave w's groups 16 c + 2 w + j.
+DI void start_w1(Pipe2 &w, const HeadArgs &a, int c, int lane, int wave) {
+  const int ng[2] = {16 * c + 2 * wave, 16 * c + 2 * wave + 1};
+  wp_start(w, a.W1, KSD, ng, 0, lane);
+}
+// W_2 k-steps of chunk c for wave w's 48 output columns.
+DI void start_w2(PipeO &w, const HeadArgs &a, int c, int lane, int wave) {
+  const int ng[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
+  wp_start(w, a.W2, KSF, ng, 8 * c, lane);
+}
+
+// relu(H + b_1) of chunk c into the chunk buffer sHb (fragment order, 64 x 256):
+// wave w holds chunk-local columns 32 w .. 32 w + 31.
+DI void relu_store(const f32x4 (&H)[4][2], const float *b1, int c, bf16 *sHb, int lane, int wave) {
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = 32 * wave + 16 * j + 4 * g;
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(b1 + 256 * c + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      put4(sHb, 16 * i + r16, col, 8, fmaxf(H[i][j][0] + b[0], 0.f), fmaxf(H[i][j][1] + b[1], 0.f),
+           fmaxf(H[i][j][2] + b[2], 0.f), fmaxf(H[i][j][3] + b[3], 0.f));
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void head_kernel(HeadArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 sA[RB * kWidth];  // 48 KB: o, then u, then u'
+  __shared__ __attribute__((aligned(16))) bf16 sH0[RB * 256];    // 32 KB: ReLU chunk buffers,
+  __shared__ __attribute__((aligned(16))) bf16 sH1[RB * 256];    // 32 KB: double-buffered
+  __shared__ float sRed[NW][RB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int row0 = blockIdx.x * RB;
+  const int T = a.T;
+
+  PipeO po;
+  PipeI pi;
+  Pipe2 p2;
+  {
+    const int ngo[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
+    wp_start(po, a.Wo, KSD, ngo, 0, lane);
+  }
+  for (int c = tid; c < RB * (kWidth / 8); c += 512) {
+    const int r = c / (kWidth / 8), k = (c % (kWidth / 8)) * 8;
+    const int src = min(row0 + r, T - 1);
+    *reinterpret_cast<bf16x8 *>(&sA[afrag(r, k, KSD)]) = ldg8(a.o + (size_t)src * kWidth + k);
+  }
+  __syncthreads();
+
+  // 1. X = x + o . W_o^T + b_o   (wave w: columns 48w .. 48w+47)
+  f32x4 X[4][3];
+  zero(X);
+  wp_run<KSD>(X, po, sA, lane, [&] { start_w1(p2, a, 0, lane, wave); });
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int col = 48 * wave + 16 * j + 4 * g;
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(a.bo + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = min(row0 + 16 * i + r16, T - 1);
+      X[i][j] = *reinterpret_cast<const f32x4 *>(a.x + (size_t)row * kWidth + col) + (X[i][j] + b);
+    }
+  }
+
+  // 2. u = LayerNorm_2(X) -> sA (the syncs in row_stats retire every read of o)
+  float mean[4], rstd[4];
+  row_stats(X, sRed, lane, wave, mean, rstd);
+  write_ln<true>(X, a.n2_w, a.n2_b, mean, rstd, sA, lane, wave);
+  __syncthreads();
+
+  // 3. feed-forward: chunk c's ReLU output in buffer c % 2; W_2(c) runs after
+  //    the barrier that publishes it, while the next chunk's W_1 fragments
+  //    are already in flight
+  f32x4 H[4][2];
+#pragma unroll 1
+  for (int c = 0; c < kHeadChunks; ++c) {
+    bf16 *buf = (c & 1) ? sH1 : sH0;
+    zero(H);
+    wp_run<KSD>(H, p2, sA, lane, NoNext());
+    start_w2(po, a, c, lane, wave);
+    relu_store(H, a.b1, c, buf, lane, wave);
+    __syncthreads();
+    wp_run<8>(X, po, buf, lane, [&] {
+      if (c + 1 < kHeadChunks) start_w1(p2, a, c + 1, lane, wave);
+    });
+  }
+
+  // 4. X += b_2 -> x; the next layer's keys and values
+  const bool kv = a.Wkv != nullptr;
+  if (kv) {
+    const int ng[4] = {6 * wave, 6 * wave + 1, 6 * wave + 2, 6 * wave + 3};
+    wp_start(pi, a.Wkv, KSD, ng, 0, lane);
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int col = 48 * wave + 16 * j + 4 * g;
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(a.b2 + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      X[i][j] += b;
+      const int row = row0 + 16 * i + r16;
+      if (row < T) *reinterpret_cast<f32x4 *>(a.x + (size_t)row * kWidth + col) = X[i][j];
+    }
+  }
+  if (!kv) return;
+  row_stats(X, sRed, lane, wave, mean, rstd);
+  write_ln<true>(X, a.nk_w, a.nk_b, mean, rstd, sA, lane, wave);
+  __syncthreads();
+  // 768 columns = 48 groups, 6 per wave: 4 on one pipe, 2 on the other
+  const int ng4[4] = {6 * wave, 6 * wave + 1, 6 * wave + 2, 6 * wave + 3};
+  const int ng2[2] = {6 * wave + 4, 6 * wave + 5};
+  f32x4 K4[4][4];
+  zero(K4);
+  wp_run<KSD>(K4, pi, sA, lane, [&] { wp_start(p2, a.Wkv, KSD, ng2, 0, lane); });
+  bias_store<4>(K4, ng4, a.bkv, a.kv_out, 2 * kWidth, lane, row0, T);
+  zero(H);
+  wp_run<KSD>(H, p2, sA, lane, NoNext());
+  bias_store<2>(H, ng2, a.bkv, a.kv_out, 2 * kWidth, lane, row0, T);
 }
 
 }  // namespace
 
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  layer_kernel<<<(a.T + RB - 1) / RB, 512, 0, s>>>(a);
+  if (a.qkv_bias_next != nullptr)
+    layer_kernel<true><<<(a.T + RB - 1) / RB, 512, 0, s>>>(a);
+  else
+    layer_kernel<false><<<(a.T + RB - 1) / RB, 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_layer(const HeadArgs &a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  head_kernel<<<(a.T + RB - 1) / RB, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -23,9 +23,9 @@ OK, ERR_ARG, ERR_OPTIONS, ERR_LENGTH, ERR_QTYPE, ERR_FILE, ERR_DEVICE, ERR_OOM, 
 STATUS_NAMES = {0: "OK", -1: "ARG", -2: "OPTIONS", -3: "LENGTH", -4: "QTYPE", -5: "FILE",
                 -6: "DEVICE", -7: "OOM", -8: "CAPACITY"}
 (K_EMBED, K_QKV, K_ATTN_GLOBAL, K_ATTN_LOCAL, K_OUTPROJ, K_MLP_IN, K_MLP_OUT, K_HEAD_GEMM, K_HEAD_ATTN,
- K_MISC, K_LN, K_LAYER) = range(12)
+ K_MISC, K_LN, K_LAYER, K_HEAD_LAYER) = range(13)
 KERNEL_CLASS_NAMES = ["embed", "qkv", "attn_global", "attn_local", "outproj", "mlp_in", "mlp_out",
-                      "head_gemm", "head_attn", "misc", "ln", "layer"]
+                      "head_gemm", "head_attn", "misc", "ln", "layer", "head_layer"]
 N_KERNEL_CLASSES = len(KERNEL_CLASS_NAMES)
 
 _i32p = ctypes.POINTER(ctypes.c_int32)

@@ -232,7 +232,9 @@ enum jl_kernel_class {
   JL_K_LN = 10,        /* LayerNorm rows -> GEMM operand                        */
   JL_K_LAYER = 11,     /* row-block layer kernel: out-proj, LayerNorm, GEGLU    */
                        /* MLP and the next layer's QKV (large bf16 batches)     */
-  JL_K_NCLASS = 12
+  JL_K_HEAD_LAYER = 12,/* row-block head-layer kernel: the first head layer     */
+                       /* after its attention + the second's keys and values    */
+  JL_K_NCLASS = 13
 };
 
 /* Per-kernel timer: while on, every launch of the classes in `class_mask`
