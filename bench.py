@@ -58,7 +58,7 @@ def class_flops(batch, row_block):
     head_in, head_rest, head_kv = 2 * T * D * 3 * D, 2 * T * D * (D + 2 * FFN_HEAD), 2 * T * D * 2 * D
     head_markers = 2 * M * D * (D + D + 2 * FFN_HEAD)
     if row_block:
-        f["qkv"] = qkv
+        f["embed"] = qkv  # the embedding kernel computes the first layer's QKV
         f["layer"] = 22 * (outp + mlp_in + mlp_out) + 21 * qkv + head_in
         f["head_layer"] = head_rest + head_kv
         f["head_gemm"] = head_markers

@@ -762,7 +762,26 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     JL_HIP(hipMemcpyAsync(out, src, rows * D * 4, hipMemcpyDeviceToDevice, s));
     return JL_OK;
   };
-  JL_LAUNCH(JL_K_EMBED, launch_embed(ids, m->emb, m->emb_norm, T, pl.d_so, pl.B, m->x, m->pos, m->tok_seq, s));
+  const bool row_block = bf && T >= m->row_block_min_tokens;
+  if (row_block) {  // the embedding kernel also computes the first layer's QKV
+    EmbedArgs ea{};
+    ea.ids = ids;
+    ea.emb = m->emb;
+    ea.gain = m->emb_norm;
+    ea.seq_offsets = pl.d_so;
+    ea.n_seqs = pl.B;
+    ea.x = m->x;
+    ea.pos = m->pos;
+    ea.tok_seq = m->tok_seq;
+    ea.Wqkv = (const __bf16 *)m->L[0].pWqkv;
+    ea.rope_cos = m->rope_cos[layer_is_global(0)];
+    ea.rope_sin = m->rope_sin[layer_is_global(0)];
+    ea.qkv_out = (__bf16 *)m->qkv;
+    ea.T = T;
+    JL_LAUNCH(JL_K_EMBED, launch_embed_qkv(ea, s));
+  } else {
+    JL_LAUNCH(JL_K_EMBED, launch_embed(ids, m->emb, m->emb_norm, T, pl.d_so, pl.B, m->x, m->pos, m->tok_seq, s));
+  }
   if (stop == 0) return copy_out(m->x, T);
 
   AttnArgs at{};
@@ -774,19 +793,8 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   at.o = m->o;
   at.o_stride = D;
   at.work = pl.d_aw;
-  const bool row_block = bf && T >= m->row_block_min_tokens;
   if (row_block) {
     // Row-block path: one attention launch and one layer launch per layer.
-    {
-      const LayerW &W0 = m->L[0];
-      JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, nullptr, nullptr, T, u, s));
-      GemmArgs q = gemm(u, D, W0.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D);
-      q.rope_cos = m->rope_cos[1];
-      q.rope_sin = m->rope_sin[1];
-      q.pos = m->pos;
-      q.rope_cols = 2 * D;
-      JL_LAUNCH(JL_K_QKV, launch_gemm(bf, E_STORE, q, s));
-    }
     for (int l = 0; l < kLayers; ++l) {
       const bool glob = layer_is_global(l);
       at.half_window = glob ? -1 : kHalfWindow;

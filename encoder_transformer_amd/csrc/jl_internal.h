@@ -113,7 +113,25 @@ struct HeadArgs {
   int T;
 };
 
-// Launchers (kernels.hip, layer.hip).  `bf16` selects the bf16 instantiation, else FP32.
+// Row-block embedding kernel (bf16 only): token embedding gather + its
+// LayerNorm into x, each token's sequence and position, and the first
+// layer's QKV with RoPE (that layer has no attention pre-norm).
+struct EmbedArgs {
+  const int32_t *ids;           // [T] token ids (out-of-range ids give NaN rows)
+  const float *emb;             // [vocab, 384]
+  const float *gain;            // embedding LayerNorm gain
+  const int *seq_offsets;       // [n_seqs + 1]
+  int n_seqs;
+  float *x;                     // [T, 384] out: residual stream
+  int *pos;                     // [T] out: position inside the sequence
+  int *tok_seq;                 // [T] out: sequence of each token
+  const __bf16 *Wqkv;           // first layer, fragment-packed [1152 x 384]
+  const float *rope_cos, *rope_sin;  // the first layer's RoPE table [8192, 32]
+  __bf16 *qkv_out;              // [T, 1152]
+  int T;
+};
+
+// Launchers (jl_kernels.hip, jl_layer.hip, jl_head.hip, jl_embed.hip).  `bf16` selects the bf16 instantiation, else FP32.
 hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain, int T,
                         const int *seq_offsets, int n_seqs, float *x, int *pos, int *tok_seq,
                         hipStream_t s);
@@ -123,6 +141,7 @@ hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, cons
 hipError_t launch_attention(bool bf16, const AttnArgs &a, int n_work, int queries_per_block, hipStream_t s);
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s);
 hipError_t launch_head_layer(const HeadArgs &a, hipStream_t s);
+hipError_t launch_embed_qkv(const EmbedArgs &a, hipStream_t s);
 hipError_t launch_final_ln_type(const float *x, const float *gain, const float *type_rows,
                                 const int *qtype, const int *tok_seq, int T, float *h,
                                 hipStream_t s);

@@ -26,8 +26,9 @@ CSRC = os.path.join(PKG, "csrc")
 
 # kernel class (as bench.py names it) -> device function and the sources it is built from
 KERNELS = {
-    "layer": ("layer_kernel", ["jl_layer.hip", "jl_device.h", "jl_internal.h"]),
-    "head_layer": ("head_kernel", ["jl_layer.hip", "jl_device.h", "jl_internal.h"]),
+    "layer": ("layer_kernel", ["jl_layer.hip", "jl_rowblock.h", "jl_device.h", "jl_internal.h"]),
+    "head_layer": ("head_kernel", ["jl_head.hip", "jl_rowblock.h", "jl_device.h", "jl_internal.h"]),
+    "embed": ("embed_qkv_kernel", ["jl_embed.hip", "jl_rowblock.h", "jl_device.h", "jl_internal.h"]),
     "attn_global": ("attn_kernel", ["jl_kernels.hip", "jl_device.h", "jl_internal.h"]),
     "attn_local": ("attn_kernel", ["jl_kernels.hip", "jl_device.h", "jl_internal.h"]),
 }

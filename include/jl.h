@@ -219,7 +219,8 @@ int jl_route_with_scorer(jl_score_fn score, void *user, int64_t max_tokens, int6
 
 /* Kernel classes reported by the per-kernel timer. */
 enum jl_kernel_class {
-  JL_K_EMBED = 0,      /* embedding gather + LayerNorm                         */
+  JL_K_EMBED = 0,      /* embedding gather + LayerNorm (row-block path: also   */
+                       /* the first layer's QKV)                                */
   JL_K_QKV = 1,        /* encoder QKV GEMM (RoPE on store)                      */
   JL_K_ATTN_GLOBAL = 2,/* encoder attention, global layers                      */
   JL_K_ATTN_LOCAL = 3, /* encoder attention, +-64 window layers                 */

@@ -284,6 +284,30 @@ def test_edge_cases(models, oracle_weights):
     assert torch.all(out == 7.0)
 
 
+@pytest.mark.parametrize("path", ["fp32", "bf16-per-gemm", "bf16-row-block"])
+def test_out_of_range_id_poisons_its_sequence_only(models, path):
+    m = models["fp32" if path == "fp32" else "bf16"]
+    if path == "bf16-row-block":
+        m.set_row_block_min_tokens(0)
+    elif path == "bf16-per-gemm":
+        m.set_row_block_min_tokens(1 << 62)
+    try:
+        bad = synth.make_batch(4).subset([0, 1, 2])
+        for pos, val in ((bad.seq_offsets[1] + 3, synth.VOCAB), (bad.seq_offsets[2] + 70, -1)):
+            ids = bad.ids.copy()
+            ids[pos] = val
+            got = run_logits(m, synth.Batch(ids, bad.seq_offsets, bad.mask_positions, bad.qtype))
+            clean = run_logits(m, bad)
+            sl = marker_slices(bad)
+            hit = int(np.searchsorted(bad.seq_offsets, pos, side="right") - 1)
+            assert np.all(np.isnan(got[sl[hit]])), (path, pos)
+            for b in range(3):
+                if b != hit:
+                    assert np.array_equal(got[sl[b]], clean[sl[b]]), (path, pos, b)
+    finally:
+        m.set_row_block_min_tokens(8192)
+
+
 def test_capacity_error():
     import torch
     from encoder_transformer_amd import lib
