@@ -423,6 +423,15 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     gate_half[32 * (o / 16) + (o % 16)] = 1.0f;
     gate_half[32 * (o / 16) + 16 + (o % 16)] = 0.5f;
   }
+  // Attention consumes q scaled by log2(e) / sqrt(64) (scores in the exp2
+  // domain): the factor goes into the q rows of every in-projection (and the
+  // q bias) here, in FP32 before the element conversion.
+  std::vector<float> qscaled;
+  auto scale_q_rows = [&](const float *w, size_t rows, size_t cols) -> const float * {
+    qscaled.assign(w, w + rows * cols);
+    for (size_t i = 0; i < (size_t)D * cols; ++i) qscaled[i] *= kQScale;
+    return qscaled.data();
+  };
   for (int l = 0; l < kLayers; ++l) {
     const std::string p = "layers." + std::to_string(l) + ".";
     if (l != 0) {
@@ -430,6 +439,7 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
       put_f32(t, D, &m->L[l].attn_norm);
     }
     GET(p + "attn.Wqkv.weight", 3 * D, D);
+    t = scale_q_rows(t, 3 * D, D);
     put_elem(t, 3 * D, D, &m->L[l].Wqkv, nullptr);
     if (bf) put_packed(t, 3 * D, D, &m->L[l].pWqkv, nullptr);
     GET(p + "attn.Wo.weight", D, D);
@@ -452,10 +462,12 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     const std::string p = "head.layers." + std::to_string(j) + ".";
     HeadW &h = m->H[j];
     GET(p + "self_attn.in_proj_weight", 3 * D, D);
+    t = scale_q_rows(t, 3 * D, D);
     put_elem(t, 3 * D, D, &h.in_w, nullptr);
     if (bf && j == 0) put_packed(t, 3 * D, D, &h.pIn, nullptr);
     if (bf && j == 1) put_packed(t + (size_t)D * D, 2 * D, D, &h.pKV, nullptr);
     GET(p + "self_attn.in_proj_bias", 3 * D);
+    t = scale_q_rows(t, 3 * D, 1);
     put_f32(t, 3 * D, &h.in_b);
     GET(p + "self_attn.out_proj.weight", D, D);
     put_elem(t, D, D, &h.out_w, nullptr);
@@ -535,7 +547,8 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
 
   // workspace
   const size_t T = (size_t)max_tokens, Mm = (size_t)max_markers, Bm = (size_t)m->max_seqs;
-  m->meta_ints = 2 * (Bm + 1) + Bm + Mm + 8 * (T / 64 + Bm + 1) + 8 * (T / 128 + Bm + 1) + 8 * Bm + 64;
+  // work lists: items plus at most half as many empty ones (and 8 more)
+  m->meta_ints = 2 * (Bm + 1) + Bm + Mm + 12 * (T / 64 + Bm + 8) + 12 * (T / 128 + Bm + 8) + 8 * Bm + 64;
   size_t off = 0;
   std::vector<std::pair<void **, size_t>> slots;
   auto reserve = [&](void **holder, size_t bytes) {
@@ -636,23 +649,76 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
   for (int b = 0; b < B; ++b) order[b] = b;
   std::stable_sort(order.begin(), order.end(),
                    [&](int a, int b) { return so[a + 1] - so[a] > so[b + 1] - so[b]; });
-  auto work_list = [&](int tile, int &count) {
-    count = 0;
+  // Work-groups go to the 8 XCDs round-robin by flattened index, and the
+  // grid's x extent is a multiple of 8, so item x runs on XCD x % 8 for every
+  // head.  Items are laid out per XCD: sequences, longest first, go whole to
+  // the least loaded XCD (cost = keys read per item), a sequence costing more
+  // than an eighth of the total in contiguous runs of about that cost; XCD c's
+  // items sit at x = 8 k + c in order.  The query tiles of a sequence, which
+  // read the same keys and values, then share one XCD's L2.  Shorter lists
+  // are padded with empty items (n_q = 0); if padding would exceed half the
+  // items, the plain order is used instead.
+  auto work_list = [&](int tile, bool whole_seq, int &count) {
+    auto cost_of = [&](int len) {
+      return (double)(whole_seq ? len : std::min(len, tile + 2 * kHalfWindow));
+    };
+    double total = 0.0;
+    int n_items = 0;
+    for (int b = 0; b < B; ++b) {
+      const int len = so[b + 1] - so[b];
+      n_items += (len + tile - 1) / tile;
+      total += ((len + tile - 1) / tile) * cost_of(len);
+    }
+    std::vector<AttnWork> per[8];
+    double load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const double cap = total / 8.0;
+    auto least = [&]() {
+      int c = 0;
+      for (int i = 1; i < 8; ++i)
+        if (load[i] < load[c]) c = i;
+      return c;
+    };
     for (int b : order) {
       const int start = so[b], len = so[b + 1] - so[b];
-      for (int q0 = 0; q0 < len; q0 += tile) {
-        AttnWork w{start + q0, std::min(tile, len - q0), start, len, q0, 0, 0, 0};
-        std::memcpy(h + o, &w, sizeof(w));
-        o += 8;
-        ++count;
+      const double item_cost = cost_of(len);
+      const int items = (len + tile - 1) / tile;
+      const int run = item_cost * items > cap ? std::max(1, (int)std::ceil(cap / item_cost)) : items;
+      int c = least();
+      for (int i = 0; i < items; ++i) {
+        if (i % run == 0) c = least();
+        const int q0 = i * tile;
+        per[c].push_back(AttnWork{start + q0, std::min(tile, len - q0), start, len, q0, 0, 0, 0});
+        load[c] += item_cost;
+      }
+    }
+    size_t kmax = 0;
+    for (auto &v : per) kmax = std::max(kmax, v.size());
+    count = 0;
+    if (8 * kmax <= (size_t)n_items + n_items / 2 + 8) {
+      for (size_t k = 0; k < kmax; ++k)
+        for (int c = 0; c < 8; ++c) {
+          const AttnWork w = k < per[c].size() ? per[c][k] : AttnWork{0, 0, 0, 0, 0, 0, 0, 0};
+          std::memcpy(h + o, &w, sizeof(w));
+          o += 8;
+          ++count;
+        }
+    } else {
+      for (int b : order) {
+        const int start = so[b], len = so[b + 1] - so[b];
+        for (int q0 = 0; q0 < len; q0 += tile) {
+          AttnWork w{start + q0, std::min(tile, len - q0), start, len, q0, 0, 0, 0};
+          std::memcpy(h + o, &w, sizeof(w));
+          o += 8;
+          ++count;
+        }
       }
     }
   };
   const size_t o_aw = o;
   int nw = 0, nw_wide = 0;
-  work_list(64, nw);
+  work_list(64, false, nw);
   const size_t o_aw_wide = o;
-  work_list(128, nw_wide);
+  work_list(128, true, nw_wide);
   const size_t o_mw = o;
   for (int b = 0; b < B; ++b) {
     const int first = h[o_mo + b], cnt = h[o_mo + b + 1] - first;

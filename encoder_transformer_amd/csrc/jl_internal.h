@@ -21,6 +21,9 @@ constexpr double kThetaLocal = 10000.0;
 constexpr double kThetaGlobal = 160000.0;
 constexpr float kLnEps = 1e-5f;
 constexpr int kLayerRows = 64;      // rows per work-group of the row-block layer kernel
+// Factor on q (the q rows of every in-projection and the q bias, applied at
+// load): 1 / sqrt(head dim) for the softmax and log2(e) for exp2 scores.
+constexpr float kQScale = (float)(1.4426950408889634 / 8.0);
 
 // A layer is global when its index is a multiple of 3 (layers 0, 3, ..., 21).
 inline bool layer_is_global(int l) { return l % 3 == 0; }

@@ -255,6 +255,40 @@ __device__ inline int vt_swz(int d, int slot) {
   return ((((slot >> 3) ^ (((d >> 4) & 3) << 1)) & 7) << 3) | (slot & 7);
 }
 
+// max of three / two floats with no NaN-quieting copies of the operands (the
+// compiler's fmaxf first canonicalizes every operand that comes from a
+// matrix-core result; scores are never signalling NaNs).
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ inline float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// Maximum over the four 16-lane rows of a wave for each lane position (lanes
+// i, i + 16, i + 32, i + 48): the row-swap permutes pair rows 0-1 and 2-3,
+// then the two halves, without a round trip through LDS.
+__device__ inline float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = max2f(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return max2f(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <typename T> __device__ inline Frag<T> ones_frag();
+template <> __device__ inline Frag<bf16> ones_frag<bf16>() {
+  Frag<bf16> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)1.0f;
+  return f;
+}
+template <> __device__ inline Frag<float> ones_frag<float>() {
+  return Frag<float>{f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
+}
+
 template <typename T>
 __device__ inline void store_vt_pair(T *row, int slot, float a, float b);
 template <>
@@ -273,6 +307,13 @@ __device__ inline void store_vt_pair<float>(float *row, int slot, float a, float
 // NSUB query sub-tiles of 16 per wave, 4 waves: a block covers 64 NSUB
 // queries.  Masking is evaluated only on key tiles that reach past the
 // sequence end or, on local layers, past the window of some query.
+//
+// q arrives pre-scaled by log2(e) / sqrt(64) (the q rows of the projection
+// weights and bias carry the factor, folded in at load), so scores are in the
+// exp2 domain.  Each query keeps a reference maximum m; its score
+// accumulators start at -m, so a probability is one exp2 of the accumulator,
+// and the row sums l run on the matrix cores as a product with a ones
+// fragment, from the same bf16 probabilities the P.V product uses.
 template <typename T, int NSUB>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // LDS row stride (elements): 80 makes the 16-byte operand reads (16 rows x
@@ -282,10 +323,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) T sK[2][64 * KS];
   __shared__ __attribute__((aligned(16))) T sV[2][64 * KS];  // [d][slot]
   const AttnWork w = a.work[blockIdx.x];
+  if (w.n_q <= 0) return;  // padding item of the XCD layout
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 15, g = lane >> 4;
-  const float scale = 0.125f * kLog2e;  // 1/sqrt(64), in the exp2 domain
   const bool local = a.half_window >= 0;
   const int W = a.half_window;
 
@@ -331,15 +372,21 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) store_vt_pair<T>(&sV[buf][(c + e) * KS], slot, frag_get(rv0, e), frag_get(rv1, e));
   };
 
-  float m[NSUB], l[NSUB];
-  f32x4 o[NSUB][4];
+  // per query (lane % 16): the reference maximum m (the accumulators start at
+  // -m), the growth threshold (-inf until the query's first key, then 8),
+  // row sum and output
+  float m[NSUB], thr[NSUB];
+  f32x4 minit[NSUB], lsum[NSUB], o[NSUB][4];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    m[s] = -INFINITY;
-    l[s] = 0.f;
+    m[s] = 0.f;
+    thr[s] = -INFINITY;
+    minit[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lsum[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const Frag<T> ones = ones_frag<T>();
 
   if (n_tiles <= 0) {  // no key (cannot happen for a valid work list): zero output
 #pragma unroll
@@ -369,7 +416,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   for (int t = 0; t < n_tiles; ++t) {
     const int cur = t & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
-    // S^T = K Q^T for each query sub-tile (raw dot products)
+    // S^T = K Q^T - m for each query sub-tile
     f32x4 sc[NSUB][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -377,7 +424,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       const Frag<T> k0 = load_frag(kr), k1 = load_frag(kr + 32);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
-        sc[s][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sc[s][ks] = minit[s];
         mfma(sc[s][ks], k0, fq[s][0]);
         mfma(sc[s][ks], k1, fq[s][1]);
       }
@@ -398,36 +445,36 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      float mt = -INFINITY;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        mt = fmaxf(mt, fmaxf(fmaxf(sc[s][ks][0], sc[s][ks][1]), fmaxf(sc[s][ks][2], sc[s][ks][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      // Lazy rescale: o and l keep the reference m[s] until a tile's maximum
-      // exceeds it by more than 8 (exp2 domain), so p <= 2^8; the ratio o / l
-      // is unchanged.  Most tiles after the first need no rescale at all.
-      const float mt_s = mt * scale;
-      const bool grow = mt_s > m[s] + 8.f;
+      // tile maximum relative to m: 16 values per lane, then across the 4 rows
+      float mt = max2f(max3f(max3f(sc[s][0][0], sc[s][0][1], sc[s][0][2]), max3f(sc[s][0][3], sc[s][1][0], sc[s][1][1]),
+                             max3f(sc[s][1][2], sc[s][1][3], sc[s][2][0])),
+                       max3f(max3f(sc[s][2][1], sc[s][2][2], sc[s][2][3]), max3f(sc[s][3][0], sc[s][3][1], sc[s][3][2]),
+                             sc[s][3][3]));
+      mt = rows_max(mt);
+      // Lazy rescale: m moves only when a tile's maximum exceeds it by more
+      // than 8 (or on the query's first key), so probabilities stay <= 2^8;
+      // the ratio o / l is unchanged.  Most tiles after the first need none.
+      // Before the first key o and l are 0, and alpha is capped so that
+      // 0 * alpha stays 0.
+      const bool grow = mt > thr[s];
       if (__any(grow)) {
-        const float m_new = grow ? mt_s : m[s];
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m[s] - m_new) : 1.f;
-        m[s] = m_new;
-        l[s] *= alpha;
+        const float delta = grow ? mt : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(fminf(-delta, 64.f));
+        lsum[s] *= alpha;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[s][i] *= alpha;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) sc[s][ks] -= delta;
+        m[s] += delta;
+        thr[s] = grow ? 8.f : thr[s];
+        minit[s] = f32x4{-m[s], -m[s], -m[s], -m[s]};
       }
-      const float m_use = (m[s] == -INFINITY) ? 0.f : m[s];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[s][ks][r], scale, -m_use));
-          sc[s][ks][r] = p;
-          l[s] += p;
-        }
+        for (int r = 0; r < 4; ++r) sc[s][ks][r] = __builtin_amdgcn_exp2f(sc[s][ks][r]);
     }
-    // O^T += V^T P^T
+    // O^T += V^T P^T and l += 1 P^T
 #pragma unroll
     for (int kstep = 0; kstep < 2; ++kstep) {
       Frag<T> fp[NSUB];
@@ -440,6 +487,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           pv[4 + r] = sc[s][2 * kstep + 1][r];
         }
         frag_from(fp[s], pv);
+        mfma(lsum[s], ones, fp[s]);
       }
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) {
@@ -454,9 +502,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    float lt = l[s];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = lsum[s][0];  // every row of the ones product holds the query's sum
     const int qi = wave * QW + 16 * s + ql;
     if (qi < w.n_q) {
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
