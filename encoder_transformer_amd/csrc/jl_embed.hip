@@ -16,7 +16,7 @@ __global__ __launch_bounds__(512, 1) void embed_qkv_kernel(EmbedArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sA[RB * kWidth];  // 48 KB: x as bf16
   __shared__ __attribute__((aligned(16))) float sCos[RB * 32];   // 8 KB: RoPE rows of this block
   __shared__ __attribute__((aligned(16))) float sSin[RB * 32];   // 8 KB
-  __shared__ float sRed[NW][RB];
+  __shared__ float sRed[2][NW][RB];
   __shared__ int sPos[RB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;

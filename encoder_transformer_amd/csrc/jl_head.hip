@@ -49,7 +49,7 @@ __global__ __launch_bounds__(512, 1) void head_kernel(HeadArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sA[RB * kWidth];  // 48 KB: o, then u, then u'
   __shared__ __attribute__((aligned(16))) bf16 sH0[RB * 256];    // 32 KB: ReLU chunk buffers,
   __shared__ __attribute__((aligned(16))) bf16 sH1[RB * 256];    // 32 KB: double-buffered
-  __shared__ float sRed[NW][RB];
+  __shared__ float sRed[2][NW][RB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * RB;

@@ -347,8 +347,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     hi = min(w.kv_len, w.q_pos0 + w.n_q + W);
   }
   const int n_tiles = (hi - lo + 63) >> 6;
-  // key tiles [base, base + 64) inside every query's window need no mask
-  const int q_first = w.q_pos0, q_last = w.q_pos0 + w.n_q - 1;
+  // key tiles [base, base + 64) inside every one of a wave's query windows need no mask
+  // this wave's query positions (wave-uniform)
+  const int wq0 = w.q_pos0 + __builtin_amdgcn_readfirstlane(wave) * QW, wq_last = wq0 + QW - 1;
 
   const T *kbase = (const T *)a.k + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
   const T *vbase = (const T *)a.v + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
@@ -430,18 +431,23 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
     }
     const int base = lo + t * 64;
-    const bool need_mask = base + 64 > hi || (local && (base < q_last - W || base + 63 > q_first + W));
+    const bool need_mask = base + 64 > hi || (local && (base < wq_last - W || base + 63 > wq0 + W));
     if (need_mask) {
+      // allowed keys of a lane form one range: its j = 16 ks + r (key
+      // base + 4 g + j) is allowed iff j - jlo <= span, unsigned
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s)
+      for (int s = 0; s < NSUB; ++s) {
+        const int k0 = base + 4 * g;
+        const int klo = local ? max(qpos[s] - W, 0) : 0;
+        const int khi = local ? min(qpos[s] + W, hi - 1) : hi - 1;
+        const int jlo = klo - k0;
+        const unsigned span = (unsigned)(khi - klo);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = base + ks * 16 + 4 * g + r;
-            const bool ok = key < hi && (!local || abs(qpos[s] - key) <= W);
-            if (!ok) sc[s][ks][r] = -INFINITY;
-          }
+          for (int r = 0; r < 4; ++r)
+            if ((unsigned)(16 * ks + r - jlo) > span) sc[s][ks][r] = -INFINITY;
+      }
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {

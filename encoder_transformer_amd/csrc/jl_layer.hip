@@ -78,7 +78,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sH1[RB * 256];    // 32 KB: double-buffered
   __shared__ __attribute__((aligned(16))) float sCos[RB * 32];   // 8 KB: RoPE rows of this block
   __shared__ __attribute__((aligned(16))) float sSin[RB * 32];   // 8 KB
-  __shared__ float sRed[NW][RB];
+  __shared__ float sRed[2][NW][RB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * RB;

@@ -139,12 +139,25 @@ DI void zero(f32x4 (&acc)[4][NT]) {
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Sum over the four 16-lane rows of a wave for each lane position (lanes i,
+// i + 16, i + 32, i + 48) by the row-swap permutes, without an LDS round trip;
+// every lane gets the same (r0 + r1) + (r2 + r3).
+DI float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float p = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Row statistics of the 64 x 384 tile X: wave w holds columns 48w .. 48w+47 as
 // 3 sub-tiles; lane (r16 + 16 g) holds row 16 i + r16, columns 16 j + 4 g + r.
 // Two passes (mean, then the mean of squared deviations), reduced over the 4
-// lane groups and then over the 8 waves through LDS.
-DI void row_stats(const f32x4 (&X)[4][3], float (*sRed)[RB], int lane, int wave,
-                                 float (&mean)[4], float (&rstd)[4]) {
+// lane groups and then over the 8 waves through LDS: sRed[0] holds the
+// partial sums, sRed[1] the partial squared deviations, so one barrier per
+// pass suffices -- a later call cannot overwrite either buffer before every
+// wave has passed the barrier that follows its last read.
+DI void row_stats(const f32x4 (&X)[4][3], float (*sRed)[NW][RB], int lane, int wave, float (&mean)[4],
+                  float (&rstd)[4]) {
   const int r16 = lane & 15, g = lane >> 4;
   float part[4];
 #pragma unroll
@@ -152,13 +165,11 @@ DI void row_stats(const f32x4 (&X)[4][3], float (*sRed)[RB], int lane, int wave,
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < 3; ++j) s += (X[i][j][0] + X[i][j][1]) + (X[i][j][2] + X[i][j][3]);
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    part[i] = s;
+    part[i] = rows_sum(s);
   }
   if (g == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sRed[wave][16 * i + r16] = part[i];
+    for (int i = 0; i < 4; ++i) sRed[0][wave][16 * i + r16] = part[i];
   }
   __syncthreads();
 #pragma unroll
@@ -166,10 +177,9 @@ DI void row_stats(const f32x4 (&X)[4][3], float (*sRed)[RB], int lane, int wave,
     const int row = 16 * i + r16;
     float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) t += sRed[w][row];
+    for (int w = 0; w < NW; ++w) t += sRed[0][w][row];
     mean[i] = t * (1.0f / kWidth);
   }
-  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float s = 0.f;
@@ -180,13 +190,11 @@ DI void row_stats(const f32x4 (&X)[4][3], float (*sRed)[RB], int lane, int wave,
         const float d = X[i][j][r] - mean[i];
         s += d * d;
       }
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    part[i] = s;
+    part[i] = rows_sum(s);
   }
   if (g == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sRed[wave][16 * i + r16] = part[i];
+    for (int i = 0; i < 4; ++i) sRed[1][wave][16 * i + r16] = part[i];
   }
   __syncthreads();
 #pragma unroll
@@ -194,10 +202,9 @@ DI void row_stats(const f32x4 (&X)[4][3], float (*sRed)[RB], int lane, int wave,
     const int row = 16 * i + r16;
     float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) t += sRed[w][row];
+    for (int w = 0; w < NW; ++w) t += sRed[1][w][row];
     rstd[i] = rsqrtf(t * (1.0f / kWidth) + kLnEps);
   }
-  __syncthreads();
 }
 
 // sA = bf16(gain * (X - mean) * rstd [+ shift]), fragment order over the full width.
