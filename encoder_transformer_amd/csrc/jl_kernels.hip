@@ -81,12 +81,16 @@ template <typename T> struct GemmBK;
 template <> struct GemmBK<bf16> { static constexpr int v = 64; };
 template <> struct GemmBK<float> { static constexpr int v = 32; };
 
+// s_waitcnt immediate that waits for at most n outstanding vector memory
+// operations (vmcnt in bits 3:0 and 15:14) and leaves the other counters free.
+constexpr int vm_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
 __device__ inline int xcd_tile(int b, int n_tiles) {
   const int per = n_tiles >> 3, rem = n_tiles & 7, x = b & 7, local = b >> 3;
   return x * per + min(x, rem) + local;
 }
 
-template <typename T, int BM, int BN, int EM>
+template <typename T, int BM, int BN, int EM, int NSTAGE>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int n_tiles) {
   constexpr int BK = GemmBK<T>::v, KS = BK / 32;           // 32-wide k sub-steps per stage
   constexpr int TM = BM / 2, TN = BN / 2;                   // wave tile
@@ -97,8 +101,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   constexpr int A_PER_WAVE = A_BLKS / 4, B_PER_WAVE = B_BLKS / 4;
   static_assert(A_BLKS % 4 == 0 && B_BLKS % 4 == 0, "tile must split over 4 waves");
   static_assert(NT % 4 == 0, "epilogues pair columns within 64-column groups");
-  __shared__ __attribute__((aligned(16))) T sA[2][A_BLKS * BLK];
-  __shared__ __attribute__((aligned(16))) T sB[2][B_BLKS * BLK];
+  // bf16: an NSTAGE-stage pipeline whose loads go straight from memory into
+  // LDS (16 bytes per lane, lane i at block offset 16 i: the fragment order),
+  // so NSTAGE - 1 K-steps are in flight without staging registers (4 stages
+  // for grids that fit the CUs in one round, else 2, which leaves LDS for
+  // more resident work-groups); FP32: two LDS stages filled through registers.
+  // Each bf16 stage buffer is a variable of its own and the K loop is
+  // unrolled over the stages: the compiler then knows which buffer each
+  // in-flight LDS load writes and adds no wait of its own before reading
+  // another.
+  constexpr bool kDma = std::is_same<T, bf16>::value;
+  constexpr int NS = kDma ? NSTAGE : 2;
+  static_assert(NS >= 2 && NS <= 4, "stages");
+  __shared__ __attribute__((aligned(16))) T sA[NS][A_BLKS * BLK];  // FP32 stages
+  __shared__ __attribute__((aligned(16))) T sB[NS][B_BLKS * BLK];
+  __shared__ __attribute__((aligned(16))) T sA0[kDma ? A_BLKS * BLK : 1], sB0[kDma ? B_BLKS * BLK : 1];
+  __shared__ __attribute__((aligned(16))) T sA1[kDma ? A_BLKS * BLK : 1], sB1[kDma ? B_BLKS * BLK : 1];
+  __shared__ __attribute__((aligned(16))) T sA2[kDma && NS > 2 ? A_BLKS * BLK : 1], sB2[kDma && NS > 2 ? B_BLKS * BLK : 1];
+  __shared__ __attribute__((aligned(16))) T sA3[kDma && NS > 3 ? A_BLKS * BLK : 1], sB3[kDma && NS > 3 ? B_BLKS * BLK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -138,26 +158,96 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = g.K / BK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_stage(kt + 1);
+  auto compute = [&](const T *cA, const T *cB) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Frag<T> fa[MT], fb[NT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) fa[i] = load_frag(&sA[cur][((wm * MT + i) * KS + ks) * BLK + lane * FE]);
+      for (int i = 0; i < MT; ++i) fa[i] = load_frag(&cA[((wm * MT + i) * KS + ks) * BLK + lane * FE]);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) fb[j] = load_frag(&sB[cur][((wn * NT + j) * KS + ks) * BLK + lane * FE]);
+      for (int j = 0; j < NT; ++j) fb[j] = load_frag(&cB[((wn * NT + j) * KS + ks) * BLK + lane * FE]);
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j) mfma(acc[i][j], fa[i], fb[j]);
     }
-    if (kt + 1 < KT) store_stage(cur ^ 1);
+  };
+  if constexpr (kDma) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    constexpr int LPS = A_PER_WAVE + B_PER_WAVE;  // loads per stage and wave
+    auto bufA = [&](auto Bc) -> T * {
+      constexpr int B = decltype(Bc)::value;
+      if constexpr (B == 0) return sA0;
+      else if constexpr (B == 1) return sA1;
+      else if constexpr (B == 2) return sA2;
+      else return sA3;
+    };
+    auto bufB = [&](auto Bc) -> T * {
+      constexpr int B = decltype(Bc)::value;
+      if constexpr (B == 0) return sB0;
+      else if constexpr (B == 1) return sB1;
+      else if constexpr (B == 2) return sB2;
+      else return sB3;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // stage kt -> LDS buffer pair (dA, dB), one 1 KB fragment block per load
+    auto issue_stage = [&](int kt, T *dA, T *dB) {
+      const int k0 = kt * BK + lc;
+#pragma unroll
+      for (int i = 0; i < A_PER_WAVE; ++i) {
+        const int q = wave * A_PER_WAVE + i;
+        const int row = min(m0 + (q / KS) * 16 + lr, M - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(Ab + (size_t)row * g.lda + k0 + (q % KS) * 32),
+                                         (lds_void *)&dA[q * BLK], 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < B_PER_WAVE; ++i) {
+        const int q = wave * B_PER_WAVE + i;
+        __builtin_amdgcn_global_load_lds((const void *)(Wb + (size_t)(n0 + (q / KS) * 16 + lr) * g.ldw + k0 + (q % KS) * 32),
+                                         (lds_void *)&dB[q * BLK], 16, 0, 0);
+      }
+    };
+    // K-step kt from buffer B (= kt % NS): wait for this wave's loads of the
+    // step (at most `later` younger steps stay in flight), then a bare
+    // barrier: every wave's loads of the step have landed and every wave is
+    // done reading the previous step's buffer, which the next load refills.
+    auto step = [&](int kt, auto Bc) {
+      constexpr int B = decltype(Bc)::value;
+      const int later = min(NS - 2, KT - 1 - kt);
+      if (later <= 0) __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+      else if (NS == 3 || later == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPS));
+      else __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * LPS));
+      __builtin_amdgcn_s_barrier();
+      using Next = std::integral_constant<int, (B + NS - 1) % NS>;
+      if (kt + NS - 1 < KT) issue_stage(kt + NS - 1, bufA(Next()), bufB(Next()));
+      compute(bufA(Bc), bufB(Bc));
+    };
+    issue_stage(0, sA0, sB0);
+    if constexpr (NS > 2)
+      if (KT > 1) issue_stage(1, sA1, sB1);
+    if constexpr (NS > 3)
+      if (KT > 2) issue_stage(2, bufA(I2()), bufB(I2()));
+    for (int kt = 0; kt < KT; kt += NS) {
+      step(kt, I0());
+      if (kt + 1 < KT) step(kt + 1, I1());
+      if constexpr (NS > 2)
+        if (kt + 2 < KT) step(kt + 2, I2());
+      if constexpr (NS > 3)
+        if (kt + 3 < KT) step(kt + 3, std::integral_constant<int, NS - 1>());
+    }
+  } else {
+    load_stage(0);
+    store_stage(0);
     __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < KT) load_stage(kt + 1);
+      compute(sA[cur], sB[cur]);
+      if (kt + 1 < KT) store_stage(cur ^ 1);
+      __syncthreads();
+    }
   }
 
   // epilogue: acc[i][j][r] = C[row0 + 16i + r][col0 + 16j]
@@ -658,15 +748,15 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, int NS>
 static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
   const int tiles_n = a.N / BN, n_tiles = ((a.M + BM - 1) / BM) * tiles_n;
   switch (emode) {
-    case E_STORE: gemm_kernel<T, BM, BN, E_STORE><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_RESID: gemm_kernel<T, BM, BN, E_RESID><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_GEGLU: gemm_kernel<T, BM, BN, E_GEGLU><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_RELU: gemm_kernel<T, BM, BN, E_RELU><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_GELU_F32: gemm_kernel<T, BM, BN, E_GELU_F32><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_STORE: gemm_kernel<T, BM, BN, E_STORE, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_RESID: gemm_kernel<T, BM, BN, E_RESID, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_GEGLU: gemm_kernel<T, BM, BN, E_GEGLU, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_RELU: gemm_kernel<T, BM, BN, E_RELU, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_GELU_F32: gemm_kernel<T, BM, BN, E_GELU_F32, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -678,12 +768,13 @@ hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t
   if (a.N % 128 != 0 || a.K % 64 != 0) return hipErrorInvalidValue;
   const long nt = a.N / 128;
   if (bf16_mode && emode != E_GELU_F32) {
-    if (((a.M + 255) / 256) * nt >= 256) return gemm_dispatch<bf16, 256, 128>(emode, a, s);
-    if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<bf16, 128, 128>(emode, a, s);
-    return gemm_dispatch<bf16, 64, 128>(emode, a, s);
+    if (((a.M + 255) / 256) * nt >= 256) return gemm_dispatch<bf16, 256, 128, 2>(emode, a, s);
+    if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<bf16, 128, 128, 2>(emode, a, s);
+    if (((a.M + 63) / 64) * nt > 256) return gemm_dispatch<bf16, 64, 128, 2>(emode, a, s);
+    return gemm_dispatch<bf16, 64, 128, 4>(emode, a, s);
   }
-  if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<float, 128, 128>(emode, a, s);
-  return gemm_dispatch<float, 64, 128>(emode, a, s);
+  if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<float, 128, 128, 2>(emode, a, s);
+  return gemm_dispatch<float, 64, 128, 2>(emode, a, s);
 }
 
 hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, const float *shift, int n, void *out,
