@@ -799,6 +799,14 @@ hipError_t attention(bool bf, AttnArgs at, const Plan &pl, bool whole_sequence, 
   return launch_attention(bf, at, whole_sequence ? pl.n_work_wide : pl.n_work, whole_sequence ? 128 : 64, s);
 }
 
+// A = LayerNorm(x; gain, shift) for launch_ln_gemm (a.A: the fallback's bf16/FP32 rows).
+GemmArgs with_ln(GemmArgs a, const float *x, const float *gain, const float *shift) {
+  a.ln_x = x;
+  a.ln_gain = gain;
+  a.ln_shift = shift;
+  return a;
+}
+
 GemmArgs gemm(const void *A, int lda, const void *W, int ldw, const float *bias, void *C, int ldc, int M, int N,
               int K) {
   GemmArgs a{};
@@ -903,18 +911,19 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   for (int l = 0; l < kLayers; ++l) {
     const LayerW &W = m->L[l];
     const bool glob = layer_is_global(l);
-    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, W.attn_norm, nullptr, T, u, s));
-    GemmArgs q = gemm(u, D, W.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D);
+    GemmArgs q = with_ln(gemm(u, D, W.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D), m->x, W.attn_norm, nullptr);
     q.rope_cos = m->rope_cos[glob];
     q.rope_sin = m->rope_sin[glob];
     q.pos = m->pos;
     q.rope_cols = 2 * D;
-    JL_LAUNCH(JL_K_QKV, launch_gemm(bf, E_STORE, q, s));
+    JL_LAUNCH(JL_K_QKV, launch_ln_gemm(bf, E_STORE, q, s));
     at.half_window = glob ? -1 : kHalfWindow;
     JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, attention(bf, at, pl, glob, s));
     JL_LAUNCH(JL_K_OUTPROJ, launch_gemm(bf, E_RESID, gemm(m->o, D, W.Wo, D, nullptr, m->x, D, T, D, D), s));
-    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, W.mlp_norm, nullptr, T, u, s));
-    JL_LAUNCH(JL_K_MLP_IN, launch_gemm(bf, E_GEGLU, gemm(u, D, W.Wi, D, nullptr, m->act, kGeglu, T, 2 * kGeglu, D), s));
+    JL_LAUNCH(JL_K_MLP_IN, launch_ln_gemm(bf, E_GEGLU,
+                                          with_ln(gemm(u, D, W.Wi, D, nullptr, m->act, kGeglu, T, 2 * kGeglu, D),
+                                                  m->x, W.mlp_norm, nullptr),
+                                          s));
     JL_LAUNCH(JL_K_MLP_OUT,
               launch_gemm(bf, E_RESID, gemm(m->act, kGeglu, W.Wout, kGeglu, nullptr, m->x, D, T, D, kGeglu), s));
     if (stop == l + 1) return copy_out(m->x, T);
@@ -931,9 +940,10 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   {
     const HeadW &H = m->H[0];
     if (!row_block) {
-      JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n1_w, H.n1_b, T, u, s));
       JL_LAUNCH(JL_K_HEAD_GEMM,
-                launch_gemm(bf, E_STORE, gemm(u, D, H.in_w, D, H.in_b, m->qkv, 3 * D, T, 3 * D, D), s));
+                launch_ln_gemm(bf, E_STORE,
+                               with_ln(gemm(u, D, H.in_w, D, H.in_b, m->qkv, 3 * D, T, 3 * D, D), m->x, H.n1_w, H.n1_b),
+                               s));
     }
     at.half_window = -1;
     JL_LAUNCH(JL_K_HEAD_ATTN, attention(bf, at, pl, true, s));
@@ -961,9 +971,11 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
       JL_LAUNCH(JL_K_HEAD_LAYER, launch_head_layer(ha, s));
     } else {
       JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->o, D, H.out_w, D, H.out_b, m->x, D, T, D, D), s));
-      JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n2_w, H.n2_b, T, u, s));
       JL_LAUNCH(JL_K_HEAD_GEMM,
-                launch_gemm(bf, E_RELU, gemm(u, D, H.l1_w, D, H.l1_b, m->act, kHeadFfn, T, kHeadFfn, D), s));
+                launch_ln_gemm(bf, E_RELU,
+                               with_ln(gemm(u, D, H.l1_w, D, H.l1_b, m->act, kHeadFfn, T, kHeadFfn, D), m->x, H.n2_w,
+                                       H.n2_b),
+                               s));
       JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID,
                                             gemm(m->act, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, m->x, D, T, D, kHeadFfn),
                                             s));
@@ -975,16 +987,18 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   {
     const HeadW &H = m->H[1];
     if (!row_block) {
-      JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->x, H.n1_w, H.n1_b, T, u, s));
-      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_STORE,
-                                            gemm(u, D, (const char *)H.in_w + (size_t)D * D * es, D, H.in_b + D, kv,
-                                                 2 * D, T, 2 * D, D),
-                                            s));
+      JL_LAUNCH(JL_K_HEAD_GEMM,
+                launch_ln_gemm(bf, E_STORE,
+                               with_ln(gemm(u, D, (const char *)H.in_w + (size_t)D * D * es, D, H.in_b + D, kv, 2 * D,
+                                            T, 2 * D, D),
+                                       m->x, H.n1_w, H.n1_b),
+                               s));
     }
     JL_LAUNCH(JL_K_MISC, launch_gather_rows(m->x, pl.d_mp, M, m->z, s));
     char *um = m->om;  // normalized marker rows, then the marker attention output
-    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->z, H.n1_w, H.n1_b, M, um, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_STORE, gemm(um, D, H.in_w, D, H.in_b, m->qm, D, M, D, D), s));
+    JL_LAUNCH(JL_K_HEAD_GEMM,
+              launch_ln_gemm(bf, E_STORE, with_ln(gemm(um, D, H.in_w, D, H.in_b, m->qm, D, M, D, D), m->z, H.n1_w, H.n1_b),
+                             s));
     AttnArgs mk{};
     mk.q = m->qm;
     mk.q_stride = D;
@@ -997,9 +1011,11 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     mk.half_window = -1;
     JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, mk, pl.B, 64, s));
     JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->om, D, H.out_w, D, H.out_b, m->z, D, M, D, D), s));
-    JL_LAUNCH(JL_K_LN, launch_ln_rows(bf, m->z, H.n2_w, H.n2_b, M, um, s));
     JL_LAUNCH(JL_K_HEAD_GEMM,
-              launch_gemm(bf, E_RELU, gemm(um, D, H.l1_w, D, H.l1_b, m->actm, kHeadFfn, M, kHeadFfn, D), s));
+              launch_ln_gemm(bf, E_RELU,
+                             with_ln(gemm(um, D, H.l1_w, D, H.l1_b, m->actm, kHeadFfn, M, kHeadFfn, D), m->z, H.n2_w,
+                                     H.n2_b),
+                             s));
     JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID,
                                           gemm(m->actm, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, m->z, D, M, D, kHeadFfn),
                                           s));

@@ -44,6 +44,10 @@ struct GemmArgs {
   const float *rope_sin;
   const int *pos;       // [M] position of each row inside its sequence (RoPE)
   int rope_cols;        // columns [0, rope_cols) are rotated (q and k: 768)
+  // LayerNorm fused into the A operand (launch_ln_gemm): A = LN(ln_x) rows
+  const float *ln_x;    // FP32 [M, 384]
+  const float *ln_gain; // nullptr: A = ln_x converted, unnormalized (identity pre-norm)
+  const float *ln_shift;// or nullptr
 };
 
 // One attention work item: up to 64 or 128 queries (the launch's tile size) of
@@ -139,6 +143,10 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
                         const int *seq_offsets, int n_seqs, float *x, int *pos, int *tok_seq,
                         hipStream_t s);
 hipError_t launch_gemm(bool bf16, int emode, const GemmArgs &a, hipStream_t s);
+// A = LayerNorm(ln_x; ln_gain, ln_shift) (K = 384), then launch_gemm's product.
+// bf16 batches small enough for 64-row tiles normalize inside the GEMM's
+// work-groups; otherwise the rows are normalized into a.A first.
+hipError_t launch_ln_gemm(bool bf16, int emode, const GemmArgs &a, hipStream_t s);
 hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, const float *shift, int n, void *out,
                           hipStream_t s);
 hipError_t launch_attention(bool bf16, const AttnArgs &a, int n_work, int queries_per_block, hipStream_t s);

@@ -90,7 +90,7 @@ __device__ inline int xcd_tile(int b, int n_tiles) {
   return x * per + min(x, rem) + local;
 }
 
-template <typename T, int BM, int BN, int EM, int NSTAGE>
+template <typename T, int BM, int BN, int EM, int NSTAGE, bool LNA = false>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int n_tiles) {
   constexpr int BK = GemmBK<T>::v, KS = BK / 32;           // 32-wide k sub-steps per stage
   constexpr int TM = BM / 2, TN = BN / 2;                   // wave tile
@@ -110,15 +110,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   // unrolled over the stages: the compiler then knows which buffer each
   // in-flight LDS load writes and adds no wait of its own before reading
   // another.
+  //
+  // LNA (bf16, BM = 64, K = 384): A = LayerNorm(g.ln_x) rows, normalized by
+  // the work-group itself into an LDS tile that holds all of K; only W
+  // streams through the stages.
   constexpr bool kDma = std::is_same<T, bf16>::value;
   constexpr int NS = kDma ? NSTAGE : 2;
   static_assert(NS >= 2 && NS <= 4, "stages");
-  __shared__ __attribute__((aligned(16))) T sA[NS][A_BLKS * BLK];  // FP32 stages
-  __shared__ __attribute__((aligned(16))) T sB[NS][B_BLKS * BLK];
-  __shared__ __attribute__((aligned(16))) T sA0[kDma ? A_BLKS * BLK : 1], sB0[kDma ? B_BLKS * BLK : 1];
-  __shared__ __attribute__((aligned(16))) T sA1[kDma ? A_BLKS * BLK : 1], sB1[kDma ? B_BLKS * BLK : 1];
-  __shared__ __attribute__((aligned(16))) T sA2[kDma && NS > 2 ? A_BLKS * BLK : 1], sB2[kDma && NS > 2 ? B_BLKS * BLK : 1];
-  __shared__ __attribute__((aligned(16))) T sA3[kDma && NS > 3 ? A_BLKS * BLK : 1], sB3[kDma && NS > 3 ? B_BLKS * BLK : 1];
+  static_assert(!LNA || (kDma && BM == 64), "fused LayerNorm: bf16, 64-row tiles");
+  constexpr int KA = kWidth / 32;  // k sub-steps of the resident A tile
+  constexpr int SA = kDma && !LNA ? A_BLKS * BLK : 1;
+  __shared__ __attribute__((aligned(16))) T sA[kDma ? 1 : NS][A_BLKS * BLK];  // FP32 stages
+  __shared__ __attribute__((aligned(16))) T sB[kDma ? 1 : NS][B_BLKS * BLK];
+  __shared__ __attribute__((aligned(16))) T sAk[LNA ? BM * kWidth : 1];
+  __shared__ __attribute__((aligned(16))) T sA0[SA], sB0[kDma ? B_BLKS * BLK : 1];
+  __shared__ __attribute__((aligned(16))) T sA1[SA], sB1[kDma ? B_BLKS * BLK : 1];
+  __shared__ __attribute__((aligned(16))) T sA2[NS > 2 ? SA : 1], sB2[kDma && NS > 2 ? B_BLKS * BLK : 1];
+  __shared__ __attribute__((aligned(16))) T sA3[NS > 3 ? SA : 1], sB3[kDma && NS > 3 ? B_BLKS * BLK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -158,12 +166,70 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = g.K / BK;
-  auto compute = [&](const T *cA, const T *cB) {
+  // fused LayerNorm: each wave normalizes 16 rows, 8 at a time with all their
+  // loads in flight; lanes 0..47 hold 8 consecutive columns of a row and
+  // write them as one 16-byte run of the fragment-order A tile
+  auto ln_prologue = [&]() {
+    const bool act = lane < kWidth / 8;
+    const bool norm = g.ln_gain != nullptr;
+    f32x4 gm0 = f32x4{0.f, 0.f, 0.f, 0.f}, gm1 = gm0, sh0 = gm0, sh1 = gm0;  // absent shift: + 0
+    if (act && norm) {
+      gm0 = *reinterpret_cast<const f32x4 *>(g.ln_gain + lane * 8);
+      gm1 = *reinterpret_cast<const f32x4 *>(g.ln_gain + lane * 8 + 4);
+      if (g.ln_shift) {
+        sh0 = *reinterpret_cast<const f32x4 *>(g.ln_shift + lane * 8);
+        sh1 = *reinterpret_cast<const f32x4 *>(g.ln_shift + lane * 8 + 4);
+      }
+    }
+    const float gm[8] = {gm0[0], gm0[1], gm0[2], gm0[3], gm1[0], gm1[1], gm1[2], gm1[3]};
+    const float sh[8] = {sh0[0], sh0[1], sh0[2], sh0[3], sh1[0], sh1[1], sh1[2], sh1[3]};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float y[8][8];
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int row = min(m0 + wave * (BM / 4) + half * 8 + rr, M - 1);
+        f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
+        if (act) {
+          const float *xr = g.ln_x + (size_t)row * kWidth + lane * 8;
+          v0 = *reinterpret_cast<const f32x4 *>(xr);
+          v1 = *reinterpret_cast<const f32x4 *>(xr + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[rr][e] = v0[e];
+          y[rr][4 + e] = v1[e];
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const int rl = wave * (BM / 4) + half * 8 + rr;
+        if (norm) {
+          float mean, rstd;
+          row8_stats(y[rr], act, mean, rstd);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[rr][e] = (y[rr][e] - mean) * rstd * gm[e] + sh[e];
+        }
+        if (act) {
+          Frag<T> f;
+          frag_from(f, y[rr]);
+          // (row rl, k = 8 lane): block (rl / 16, lane / 4), lane (rl % 16) + 16 (lane % 4)
+          store_frag(&sAk[((rl >> 4) * KA + (lane >> 2)) * BLK + ((rl & 15) + 16 * (lane & 3)) * FE], f);
+        }
+      }
+    }
+  };
+  // A fragment (row sub-tile i of this wave, k sub-step ks of K-step kt)
+  auto a_frag = [&](const T *cA, int kt, int i, int ks) -> Frag<T> {
+    if constexpr (LNA) return load_frag(&sAk[((wm * MT + i) * KA + kt * KS + ks) * BLK + lane * FE]);
+    else return load_frag(&cA[((wm * MT + i) * KS + ks) * BLK + lane * FE]);
+  };
+  auto compute = [&](const T *cA, const T *cB, int kt) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Frag<T> fa[MT], fb[NT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) fa[i] = load_frag(&cA[((wm * MT + i) * KS + ks) * BLK + lane * FE]);
+      for (int i = 0; i < MT; ++i) fa[i] = a_frag(cA, kt, i, ks);
 #pragma unroll
       for (int j = 0; j < NT; ++j) fb[j] = load_frag(&cB[((wn * NT + j) * KS + ks) * BLK + lane * FE]);
 #pragma unroll
@@ -174,7 +240,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   };
   if constexpr (kDma) {
     typedef __attribute__((address_space(3))) void lds_void;
-    constexpr int LPS = A_PER_WAVE + B_PER_WAVE;  // loads per stage and wave
+    constexpr int LPS = (LNA ? 0 : A_PER_WAVE) + B_PER_WAVE;  // loads per stage and wave
     auto bufA = [&](auto Bc) -> T * {
       constexpr int B = decltype(Bc)::value;
       if constexpr (B == 0) return sA0;
@@ -196,7 +262,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     auto issue_stage = [&](int kt, T *dA, T *dB) {
       const int k0 = kt * BK + lc;
 #pragma unroll
-      for (int i = 0; i < A_PER_WAVE; ++i) {
+      for (int i = 0; i < (LNA ? 0 : A_PER_WAVE); ++i) {
         const int q = wave * A_PER_WAVE + i;
         const int row = min(m0 + (q / KS) * 16 + lr, M - 1);
         __builtin_amdgcn_global_load_lds((const void *)(Ab + (size_t)row * g.lda + k0 + (q % KS) * 32),
@@ -219,16 +285,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
       if (later <= 0) __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
       else if (NS == 3 || later == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPS));
       else __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * LPS));
+      if constexpr (LNA)
+        if (kt == 0) __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the A tile's LDS stores
       __builtin_amdgcn_s_barrier();
       using Next = std::integral_constant<int, (B + NS - 1) % NS>;
       if (kt + NS - 1 < KT) issue_stage(kt + NS - 1, bufA(Next()), bufB(Next()));
-      compute(bufA(Bc), bufB(Bc));
+      compute(bufA(Bc), bufB(Bc), kt);
     };
     issue_stage(0, sA0, sB0);
     if constexpr (NS > 2)
       if (KT > 1) issue_stage(1, sA1, sB1);
     if constexpr (NS > 3)
       if (KT > 2) issue_stage(2, bufA(I2()), bufB(I2()));
+    if constexpr (LNA) ln_prologue();  // the first weight stages are already in flight
     for (int kt = 0; kt < KT; kt += NS) {
       step(kt, I0());
       if (kt + 1 < KT) step(kt + 1, I1());
@@ -244,7 +313,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     for (int kt = 0; kt < KT; ++kt) {
       const int cur = kt & 1;
       if (kt + 1 < KT) load_stage(kt + 1);
-      compute(sA[cur], sB[cur]);
+      compute(sA[cur], sB[cur], kt);
       if (kt + 1 < KT) store_stage(cur ^ 1);
       __syncthreads();
     }
@@ -642,37 +711,40 @@ __global__ __launch_bounds__(256) void final_ln_type_kernel(const float *x, cons
 }
 
 // out[t] = LayerNorm(x[t]; gain, shift) as the GEMM element type; gain == nullptr
-// copies x unchanged (the first layer's identity pre-norm).
+// copies x unchanged (the first layer's identity pre-norm).  One row per wave,
+// lanes 0..47 holding 8 consecutive columns: the arithmetic of the GEMM's
+// fused LayerNorm (row8_stats), so both give identical operands.
 template <typename T>
 __global__ __launch_bounds__(256) void ln_rows_kernel(const float *__restrict__ x, const float *__restrict__ gain,
                                                       const float *__restrict__ shift, int n, T *__restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= n) return;
-  const float *xr = x + (size_t)t * kWidth;
-  float v[6];
+  const bool act = lane < kWidth / 8;
+  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (act) {
+    const float *xr = x + (size_t)t * kWidth + lane * 8;
 #pragma unroll
-  for (int i = 0; i < 6; ++i) v[i] = xr[lane + 64 * i];
-  T *o = out + (size_t)t * kWidth;
-  if (gain == nullptr) {
-#pragma unroll
-    for (int i = 0; i < 6; ++i) o[lane + 64 * i] = to_elem<T>(v[i]);
-    return;
+    for (int e = 0; e < 8; ++e) y[e] = xr[e];
   }
-  float s = 0.f;
+  if (gain != nullptr) {
+    float gm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, sh[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (act) {
 #pragma unroll
-  for (int i = 0; i < 6; ++i) s += v[i];
-  const float mean = wave_sum(s) * (1.0f / kWidth);
-  float q = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        gm[e] = gain[lane * 8 + e];
+        if (shift) sh[e] = shift[lane * 8 + e];  // absent shift: + 0, as in the GEMM's fused LayerNorm
+      }
+    }
+    float mean, rstd;
+    row8_stats(y, act, mean, rstd);
 #pragma unroll
-  for (int i = 0; i < 6; ++i) { const float d = v[i] - mean; q += d * d; }
-  const float rstd = rsqrtf(wave_sum(q) * (1.0f / kWidth) + kLnEps);
+    for (int e = 0; e < 8; ++e) y[e] = (y[e] - mean) * rstd * gm[e] + sh[e];
+  }
+  if (act) {
+    T *o = out + (size_t)t * kWidth + lane * 8;
 #pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const int c = lane + 64 * i;
-    float y = (v[i] - mean) * rstd * gain[c];
-    if (shift) y += shift[c];
-    o[c] = to_elem<T>(y);
+    for (int e = 0; e < 8; ++e) o[e] = to_elem<T>(y[e]);
   }
 }
 
@@ -748,15 +820,21 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BN, int NS>
+template <typename T, int BM, int BN, int NS, bool LNA = false>
 static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
   const int tiles_n = a.N / BN, n_tiles = ((a.M + BM - 1) / BM) * tiles_n;
   switch (emode) {
-    case E_STORE: gemm_kernel<T, BM, BN, E_STORE, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_RESID: gemm_kernel<T, BM, BN, E_RESID, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_GEGLU: gemm_kernel<T, BM, BN, E_GEGLU, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_RELU: gemm_kernel<T, BM, BN, E_RELU, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_GELU_F32: gemm_kernel<T, BM, BN, E_GELU_F32, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_STORE: gemm_kernel<T, BM, BN, E_STORE, NS, LNA><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_GEGLU: gemm_kernel<T, BM, BN, E_GEGLU, NS, LNA><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_RELU: gemm_kernel<T, BM, BN, E_RELU, NS, LNA><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_RESID:
+      if constexpr (LNA) return hipErrorInvalidValue;
+      else gemm_kernel<T, BM, BN, E_RESID, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      break;
+    case E_GELU_F32:
+      if constexpr (LNA) return hipErrorInvalidValue;
+      else gemm_kernel<T, BM, BN, E_GELU_F32, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -775,6 +853,21 @@ hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t
   }
   if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<float, 128, 128, 2>(emode, a, s);
   return gemm_dispatch<float, 64, 128, 2>(emode, a, s);
+}
+
+hipError_t launch_ln_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  if (a.N % 128 != 0 || a.K != kWidth || !a.ln_x) return hipErrorInvalidValue;
+  const long nt = a.N / 128, tiles64 = ((a.M + 63) / 64) * nt;
+  // the GEMM alone would take 64-row tiles: normalize inside it
+  if (bf16_mode && (emode == E_STORE || emode == E_GEGLU || emode == E_RELU) &&
+      ((a.M + 127) / 128) * nt < 256) {
+    if (tiles64 > 256) return gemm_dispatch<bf16, 64, 128, 2, true>(emode, a, s);
+    return gemm_dispatch<bf16, 64, 128, 4, true>(emode, a, s);
+  }
+  hipError_t e = launch_ln_rows(bf16_mode, a.ln_x, a.ln_gain, a.ln_shift, a.M, const_cast<void *>(a.A), s);
+  if (e != hipSuccess) return e;
+  return launch_gemm(bf16_mode, emode, a, s);
 }
 
 hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, const float *shift, int n, void *out,
