@@ -124,6 +124,33 @@ def time_workload(model, batch, steps, warmup, profile_class=None):
     return t, dominant, dom_ms, dom_n, per_class, sampled
 
 
+def serve_timing(model, batch, handles=2, budget=32768, reps=5):
+    """The ragged mix as independent host-side requests through jl_serve:
+    length-sorted micro-batches of at most `budget` tokens on `handles`
+    weight-sharing handles, one stream each; host in, host out (ids uploaded
+    and results downloaded inside the timed region)."""
+    from encoder_transformer_amd import lib
+    req = lib.Requests([batch.sequence(b) for b in range(batch.n_seqs)])
+    hs = [model.share(budget, 4096) for _ in range(handles)]
+    try:
+        lib.serve(hs, req, budget)  # first use: streams, buffers, code paths
+        gc.collect()
+        gc.disable()
+        try:
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                res = lib.serve(hs, req, budget)
+            t = (time.perf_counter() - t0) / reps
+        finally:
+            gc.enable()
+    finally:
+        for h in hs:
+            h.close()
+    return {"ms_per_queue": round(1e3 * t, 3), "requests_per_s": round(req.n / t, 1),
+            "tokens_per_s": round(int(req.id_offsets[-1]) / t, 1), "micro_batches": res.n_batches,
+            "handles": handles, "max_batch_tokens": budget, "host_to_host": True}
+
+
 def cpu_baseline():
     """The oracle on six 1,024-token sequences of the throughput batch."""
     from threadpoolctl import threadpool_info
@@ -207,6 +234,7 @@ def main():
                            "tokens_per_s": round(b.n_tokens * st / tt, 1),
                            "step_mfma_frac": round(fl / (tt / st) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "dominant_kernel": d}
+        extra["ragged256_serve"] = serve_timing(model, synth.make_batch(4))
         result["extra"] = extra
     result["ms_per_call_1x1024"] = result.get("extra", {}).get("1x1024_ms_per_call")
     model.close()

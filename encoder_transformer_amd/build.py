@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjl.so")
-SOURCES = ["jl_kernels.hip", "jl_layer.hip", "jl_head.hip", "jl_embed.hip", "jl_api.cpp", "jl_router.cpp"]
+SOURCES = ["jl_kernels.hip", "jl_layer.hip", "jl_head.hip", "jl_embed.hip", "jl_api.cpp", "jl_router.cpp", "jl_serve.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

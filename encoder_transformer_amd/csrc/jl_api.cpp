@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -113,8 +114,10 @@ struct jl_model {
   int64_t max_tokens = 0, max_markers = 0, max_seqs = 0;
   int64_t row_block_min_tokens = 8192;
 
-  char *warena = nullptr;
+  char *warena = nullptr;  // weights; freed with the last handle that shares them
+  std::shared_ptr<void> warena_owner;
   size_t wbytes = 0;
+  ServeState *serve = nullptr;  // jl_serve's stream and buffers, made on first use
   char *ws = nullptr;
   size_t wsbytes = 0;
 
@@ -320,10 +323,55 @@ extern "C" void jl_free(jl_model *m) {
     (void)hipGraphExecDestroy(g.exec);
     (void)hipGraphDestroy(g.graph);
   }
+  if (m->serve) free_serve_state(m->serve);
   if (m->ws) (void)hipFree(m->ws);
-  if (m->warena) (void)hipFree(m->warena);
+  m->warena_owner.reset();  // frees the weights if no other handle shares them
   delete m;
 }
+
+namespace {
+// Device workspace, metadata ring and pinned staging of a handle, sized by its
+// max_tokens / max_markers (and precision).  On failure the caller frees m.
+int alloc_workspace(jl_model *m) {
+  const uint32_t D = kWidth;
+  const size_t es = m->esize;
+  const size_t T = (size_t)m->max_tokens, Mm = (size_t)m->max_markers, Bm = (size_t)m->max_seqs;
+  // work lists: items plus at most half as many empty ones (and 8 more)
+  m->meta_ints = 2 * (Bm + 1) + Bm + Mm + 12 * (T / 64 + Bm + 8) + 12 * (T / 128 + Bm + 8) + 8 * Bm + 64;
+  size_t off = 0;
+  std::vector<std::pair<void **, size_t>> slots;
+  auto reserve = [&](void **holder, size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    slots.push_back({holder, off});
+    off += bytes;
+  };
+  reserve((void **)&m->x, T * D * 4);
+  reserve((void **)&m->qkv, T * 3 * D * es);
+  reserve((void **)&m->o, T * D * es);
+  reserve((void **)&m->act, T * kHeadFfn * es);
+  reserve((void **)&m->pos, T * 4);
+  reserve((void **)&m->tok_seq, T * 4);
+  reserve((void **)&m->z, Mm * D * 4);
+  reserve((void **)&m->qm, Mm * D * es);
+  reserve((void **)&m->om, Mm * D * es);
+  reserve((void **)&m->actm, Mm * kHeadFfn * es);
+  reserve((void **)&m->sh, Mm * D * 4);
+  reserve((void **)&m->zu, Mm * D * 4);
+  for (int k = 0; k < jl_model::kMetaSlots; ++k) reserve((void **)&m->meta[k], m->meta_ints * 4);
+  reserve((void **)&m->gmeta, m->meta_ints * 4);
+  m->wsbytes = (off + 255) & ~size_t(255);
+  if (hipMalloc((void **)&m->ws, m->wsbytes) != hipSuccess) return fail(JL_ERR_OOM, "cannot allocate the device workspace");
+  for (auto &sl : slots) *sl.first = m->ws + sl.second;
+  for (int k = 0; k < jl_model::kMetaSlots; ++k) {
+    if (hipHostMalloc((void **)&m->host_meta[k], m->meta_ints * 4, hipHostMallocDefault) != hipSuccess)
+      return fail(JL_ERR_OOM, "cannot allocate pinned staging memory");
+    if (hipEventCreateWithFlags(&m->slot_done[k], hipEventDisableTiming) != hipSuccess)
+      return fail(JL_ERR_DEVICE, "cannot create an event");
+  }
+  return JL_OK;
+}
+
+}  // namespace
 
 extern "C" int jl_load_weights(const char *path, int precision, int64_t max_tokens, int64_t max_markers,
                                int device, jl_model **out) {
@@ -535,6 +583,10 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     delete m;
     return fail(JL_ERR_OOM, "cannot allocate device memory for the weights");
   }
+  m->warena_owner = std::shared_ptr<void>(m->warena, [dev = device](void *p) {
+    DeviceGuard g(dev);
+    (void)hipFree(p);
+  });
   auto bail = [&](int code, const std::string &msg) {
     jl_free(m);
     return fail(code, msg);
@@ -545,44 +597,59 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
   m->emb = (const float *)m->warena;
   for (const Pending &pd : pend) *pd.dst = m->warena + emb_bytes + pd.off;
 
-  // workspace
-  const size_t T = (size_t)max_tokens, Mm = (size_t)max_markers, Bm = (size_t)m->max_seqs;
-  // work lists: items plus at most half as many empty ones (and 8 more)
-  m->meta_ints = 2 * (Bm + 1) + Bm + Mm + 12 * (T / 64 + Bm + 8) + 12 * (T / 128 + Bm + 8) + 8 * Bm + 64;
-  size_t off = 0;
-  std::vector<std::pair<void **, size_t>> slots;
-  auto reserve = [&](void **holder, size_t bytes) {
-    off = (off + 255) & ~size_t(255);
-    slots.push_back({holder, off});
-    off += bytes;
-  };
-  reserve((void **)&m->x, T * D * 4);
-  reserve((void **)&m->qkv, T * 3 * D * es);
-  reserve((void **)&m->o, T * D * es);
-  reserve((void **)&m->act, T * kHeadFfn * es);
-  reserve((void **)&m->pos, T * 4);
-  reserve((void **)&m->tok_seq, T * 4);
-  reserve((void **)&m->z, Mm * D * 4);
-  reserve((void **)&m->qm, Mm * D * es);
-  reserve((void **)&m->om, Mm * D * es);
-  reserve((void **)&m->actm, Mm * kHeadFfn * es);
-  reserve((void **)&m->sh, Mm * D * 4);
-  reserve((void **)&m->zu, Mm * D * 4);
-  for (int k = 0; k < jl_model::kMetaSlots; ++k) reserve((void **)&m->meta[k], m->meta_ints * 4);
-  reserve((void **)&m->gmeta, m->meta_ints * 4);
-  m->wsbytes = (off + 255) & ~size_t(255);
-  if (hipMalloc((void **)&m->ws, m->wsbytes) != hipSuccess)
-    return bail(JL_ERR_OOM, "cannot allocate the device workspace");
-  for (auto &sl : slots) *sl.first = m->ws + sl.second;
-  for (int k = 0; k < jl_model::kMetaSlots; ++k) {
-    if (hipHostMalloc((void **)&m->host_meta[k], m->meta_ints * 4, hipHostMallocDefault) != hipSuccess)
-      return bail(JL_ERR_OOM, "cannot allocate pinned staging memory");
-    if (hipEventCreateWithFlags(&m->slot_done[k], hipEventDisableTiming) != hipSuccess)
-      return bail(JL_ERR_DEVICE, "cannot create an event");
+  if (int rc = alloc_workspace(m)) {
+    jl_free(m);
+    return rc;
   }
   *out = m;
   return JL_OK;
 }
+
+extern "C" int jl_share(const jl_model *src, int64_t max_tokens, int64_t max_markers, jl_model **out) {
+  if (!src || !out) return fail(JL_ERR_ARG, "src and out must not be NULL");
+  if (max_tokens < 1 || max_tokens > ((int64_t)1 << 28)) return fail(JL_ERR_ARG, "max_tokens must be in 1..2^28");
+  if (max_markers < 2 || max_markers > ((int64_t)1 << 24)) return fail(JL_ERR_ARG, "max_markers must be in 2..2^24");
+  DeviceGuard dg(src->device);
+  jl_model *m = new jl_model();
+  m->device = src->device;
+  m->precision = src->precision;
+  m->bf16 = src->bf16;
+  m->esize = src->esize;
+  m->max_tokens = max_tokens;
+  m->max_markers = max_markers;
+  m->max_seqs = std::min<int64_t>(max_tokens, max_markers / 2);
+  m->row_block_min_tokens = src->row_block_min_tokens;
+  m->warena = src->warena;
+  m->warena_owner = src->warena_owner;
+  m->wbytes = src->wbytes;
+  m->emb = src->emb;
+  m->emb_norm = src->emb_norm;
+  m->final_norm = src->final_norm;
+  m->type_rows = src->type_rows;
+  for (int l = 0; l < kLayers; ++l) m->L[l] = src->L[l];
+  for (int j = 0; j < 2; ++j) m->H[j] = src->H[j];
+  m->sc_nw = src->sc_nw;
+  m->sc_nb = src->sc_nb;
+  m->sc_w1 = src->sc_w1;
+  m->sc_b1 = src->sc_b1;
+  m->sc_w2 = src->sc_w2;
+  m->sc_b2 = src->sc_b2;
+  for (int k = 0; k < 2; ++k) {
+    m->rope_cos[k] = src->rope_cos[k];
+    m->rope_sin[k] = src->rope_sin[k];
+  }
+  if (int rc = alloc_workspace(m)) {
+    jl_free(m);
+    return rc;
+  }
+  *out = m;
+  return JL_OK;
+}
+
+ServeState *&jl::model_serve_state(jl_model *m) { return m->serve; }
+int jl::model_device(const jl_model *m) { return m->device; }
+int64_t jl::model_max_tokens(const jl_model *m) { return m->max_tokens; }
+int64_t jl::model_max_markers(const jl_model *m) { return m->max_markers; }
 
 extern "C" int jl_set_row_block_min_tokens(jl_model *m, int64_t min_tokens) {
   if (!m) return fail(JL_ERR_ARG, "model handle is NULL");

@@ -167,3 +167,17 @@ hipError_t launch_probs(const float *logits, const int *marker_offsets, const in
 int set_error(int code, const char *msg);
 
 }  // namespace jl
+
+struct jl_model;
+
+namespace jl {
+
+// jl_serve's per-handle stream and buffers (jl_serve.cpp), released by jl_free.
+struct ServeState;
+void free_serve_state(ServeState *st);
+ServeState *&model_serve_state(jl_model *m);
+int model_device(const jl_model *m);
+int64_t model_max_tokens(const jl_model *m);
+int64_t model_max_markers(const jl_model *m);
+
+}  // namespace jl

@@ -88,6 +88,13 @@ def load_library():
     L.jl_set_row_block_min_tokens.argtypes = [vp, i64]
     L.jl_model_info.restype = ctypes.c_int
     L.jl_model_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.c_int]
+    L.jl_share.restype = ctypes.c_int
+    L.jl_share.argtypes = [vp, i64, i64, ctypes.POINTER(vp)]
+    L.jl_serve_plan.restype = ctypes.c_int
+    L.jl_serve_plan.argtypes = [i32, i64p, i64p, i64, i64, i64, _i32p, _i32p, _i32p]
+    L.jl_serve.restype = ctypes.c_int
+    L.jl_serve.argtypes = [ctypes.POINTER(vp), i32, i32, _i32p, i64p, _i32p, i64p, _i32p, i64,
+                           _f32p, _f32p, _f32p, _i32p, _f32p, _i32p]
     _lib = L
     return L
 
@@ -172,20 +179,91 @@ def validate(seq_offsets, mask_positions, qtype, max_tokens: int, max_markers: i
     _check(load_library().jl_validate(_p(so), len(qt), _p(mp), len(mp), _p(qt), max_tokens, max_markers))
 
 
+class Requests:
+    """Independent requests for serve(): each (ids, marker positions inside
+    the request, question type)."""
+
+    def __init__(self, items):
+        items = list(items)
+        self.n = len(items)
+        self.ids = _i32(np.concatenate([np.asarray(i, np.int32) for i, _, _ in items])) if items else _i32([])
+        self.id_offsets = np.ascontiguousarray(np.concatenate([[0], np.cumsum([len(i) for i, _, _ in items])]),
+                                               np.int64)
+        self.mask_positions = (_i32(np.concatenate([np.asarray(m, np.int32) for _, m, _ in items]))
+                               if items else _i32([]))
+        self.mask_offsets = np.ascontiguousarray(np.concatenate([[0], np.cumsum([len(m) for _, m, _ in items])]),
+                                                 np.int64)
+        self.qtype = _i32([q for _, _, q in items])
+
+
+def _i64p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def serve_plan(requests: "Requests", max_batch_tokens: int, max_batch_markers: int, max_batch_seqs: int):
+    """(order, batch_of, n_batches) of jl_serve_plan (host only)."""
+    order = np.zeros(requests.n, np.int32)
+    batch_of = np.zeros(requests.n, np.int32)
+    nb = ctypes.c_int32()
+    _check(load_library().jl_serve_plan(requests.n, _i64p(requests.id_offsets), _i64p(requests.mask_offsets),
+                                        max_batch_tokens, max_batch_markers, max_batch_seqs, _p(order),
+                                        _p(batch_of), ctypes.byref(nb)))
+    return order, batch_of, nb.value
+
+
+class ServeResult:
+    """jl_serve outputs: per marker logits / probs (request order), per request
+    answer, argmax and max probability, and the micro-batch count."""
+
+    def __init__(self, requests, logits, probs, answer, argmax, maxprob, n_batches):
+        self.logits, self.probs, self.answer, self.argmax, self.maxprob = logits, probs, answer, argmax, maxprob
+        self.n_batches = n_batches
+        self._mo = requests.mask_offsets
+
+    def request_logits(self, r: int) -> np.ndarray:
+        return self.logits[self._mo[r]:self._mo[r + 1]]
+
+
+def serve(models, requests: "Requests", max_batch_tokens: int) -> ServeResult:
+    """jl_serve over `models` (handles sharing weights, one stream each)."""
+    L = load_library()
+    hs = (ctypes.c_void_p * len(models))(*[m._h for m in models])
+    M = int(requests.mask_offsets[-1])
+    logits = np.zeros(M, np.float32)
+    probs = np.zeros(M, np.float32)
+    answer = np.zeros(requests.n, np.float32)
+    argmax = np.zeros(requests.n, np.int32)
+    maxprob = np.zeros(requests.n, np.float32)
+    nb = ctypes.c_int32()
+    f = lambda a: a.ctypes.data_as(_f32p)
+    _check(L.jl_serve(hs, len(models), requests.n, _p(requests.ids), _i64p(requests.id_offsets),
+                      _p(requests.mask_positions), _i64p(requests.mask_offsets), _p(requests.qtype),
+                      int(max_batch_tokens), f(logits), f(probs), f(answer), _p(argmax), f(maxprob), ctypes.byref(nb)))
+    return ServeResult(requests, logits, probs, answer, argmax, maxprob, nb.value)
+
+
 class Model:
     """One loaded weight set on one device, with a workspace for `max_tokens` tokens."""
 
-    def __init__(self, weight_path: str, precision: int = BF16, max_tokens: int = 16384,
-                 max_markers: Optional[int] = None, device: int = 0):
+    def __init__(self, weight_path: Optional[str], precision: int = BF16, max_tokens: int = 16384,
+                 max_markers: Optional[int] = None, device: int = 0, _share_from: Optional["Model"] = None):
         self._lib = load_library()
         self.device = device
         self.precision = precision
         self.max_tokens = int(max_tokens)
         self.max_markers = int(max_markers if max_markers is not None else max(2, min(max_tokens, 20 * 512)))
         h = ctypes.c_void_p()
-        _check(self._lib.jl_load_weights(weight_path.encode(), precision, self.max_tokens, self.max_markers,
-                                         device, ctypes.byref(h)))
+        if _share_from is not None:
+            _check(self._lib.jl_share(_share_from._h, self.max_tokens, self.max_markers, ctypes.byref(h)))
+        else:
+            _check(self._lib.jl_load_weights(weight_path.encode(), precision, self.max_tokens, self.max_markers,
+                                             device, ctypes.byref(h)))
         self._h = h
+
+    def share(self, max_tokens: Optional[int] = None, max_markers: Optional[int] = None) -> "Model":
+        """A second handle over these weights with its own workspace (jl_share)."""
+        return Model(None, self.precision, max_tokens or self.max_tokens, max_markers or self.max_markers,
+                     self.device, _share_from=self)
 
     # -- helpers -----------------------------------------------------------
     def _stream(self, stream):

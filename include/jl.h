@@ -217,6 +217,55 @@ int jl_route_with_scorer(jl_score_fn score, void *user, int64_t max_tokens, int6
                          int32_t *pick, float *pick_prob, int32_t *n_final, int32_t *final_idx,
                          float *final_prob, int32_t *calls, int32_t *rounds);
 
+/*
+ * A second handle over the weights of `src`, with a workspace of its own
+ * (max_tokens, max_markers), metadata ring, graph cache and timer.  Handles
+ * that share weights may run jl_forward / jl_probs concurrently on different
+ * streams; the weights stay allocated until the last handle sharing them is
+ * freed with jl_free.  Errors: JL_ERR_ARG (NULL or sizes out of range),
+ * JL_ERR_OOM / JL_ERR_DEVICE.
+ */
+int jl_share(const jl_model *src, int64_t max_tokens, int64_t max_markers, jl_model **out);
+
+/*
+ * Micro-batch plan of a request queue, as jl_serve uses it ("Julia-1 MLX",
+ * Performance: concurrent requests; the serving scenarios of "julia1 - Rust
+ * runtime", Benchmarks).  Host only.  Request r has id_offsets[r+1] -
+ * id_offsets[r] tokens and mask_offsets[r+1] - mask_offsets[r] markers.
+ * Requests are ordered longest first (stable: equal lengths keep their
+ * order) and packed greedily: a micro-batch closes when the next request
+ * would exceed max_batch_tokens, max_batch_markers or max_batch_seqs.
+ * Out: order[i] = the i-th request in execution order, batch_of[r] = its
+ * micro-batch (0-based, non-decreasing along `order`), *n_batches.
+ * Errors: JL_ERR_ARG (bad offsets or limits), JL_ERR_LENGTH (a request larger
+ * than one micro-batch).
+ */
+int jl_serve_plan(int32_t n_requests, const int64_t *id_offsets, const int64_t *mask_offsets,
+                  int64_t max_batch_tokens, int64_t max_batch_markers, int64_t max_batch_seqs,
+                  int32_t *order, int32_t *batch_of, int32_t *n_batches);
+
+/*
+ * Serve n_requests independent requests held in host memory: request r is
+ * ids[id_offsets[r] .. id_offsets[r+1]) with markers mask_positions[
+ * mask_offsets[r] .. mask_offsets[r+1]) (positions inside the request) and
+ * question type qtype[r].  The requests are planned as by jl_serve_plan
+ * (token budget max_batch_tokens, capped by the handles' capacities) and the
+ * micro-batches run round-robin on the n_models handles (1..16, normally
+ * sharing weights through jl_share), each on a stream of its own with its own
+ * device buffers and pinned staging (made on the handle's first jl_serve and
+ * kept until jl_free); each micro-batch is jl_forward + jl_probs.  Outputs
+ * (host, caller-owned): logits and probs [mask_offsets[n_requests]] in request
+ * order; answer, argmax, maxprob [n_requests] as jl_probs defines them;
+ * *n_batches (may be NULL).  Every request is validated as jl_validate
+ * would a batch of that one request before any work starts, so a rejected
+ * call leaves the outputs untouched.  Blocks until every result is in the
+ * output arrays.  Calls that share a handle must not overlap.
+ */
+int jl_serve(jl_model *const *models, int32_t n_models, int32_t n_requests, const int32_t *ids,
+             const int64_t *id_offsets, const int32_t *mask_positions, const int64_t *mask_offsets,
+             const int32_t *qtype, int64_t max_batch_tokens, float *logits, float *probs, float *answer,
+             int32_t *argmax, float *maxprob, int32_t *n_batches);
+
 /* Kernel classes reported by the per-kernel timer. */
 enum jl_kernel_class {
   JL_K_EMBED = 0,      /* embedding gather + LayerNorm (row-block path: also   */

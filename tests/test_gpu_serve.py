@@ -1,0 +1,105 @@
+"""Serving front on the GPU (jl_share, jl_serve): a queue of ragged requests
+served in micro-batches over handles that share the weights, each on its own
+stream, against each request run alone through jl_forward / jl_probs.
+
+Micro-batches below the row-block threshold take the per-GEMM schedule, which
+is batch invariant, so logits and read-offs match bitwise; with larger
+micro-batches (row-block schedule) they match within the bf16 agreement bound
+of the two schedules."""
+import numpy as np
+import pytest
+
+from encoder_transformer_amd import synth
+
+from gpu_common import MAX_MARKERS, device_ids
+
+pytestmark = pytest.mark.gpu
+
+BF16_LOGIT_TIGHT = 3e-3
+
+
+@pytest.fixture(scope="module")
+def models():
+    import torch
+    from encoder_transformer_amd import lib
+    assert torch.cuda.is_available()
+    m = lib.Model(synth.cached_weight_file(), lib.BF16, 20000, MAX_MARKERS)
+    shared = [m.share(), m.share(12000, 2048)]
+    yield m, shared
+    for s in shared:
+        s.close()
+    m.close()
+
+
+def _requests(n, seed):
+    from encoder_transformer_amd import lib
+    b = synth.make_batch(4)
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(b.n_seqs, n, replace=False)
+    items = []
+    for k in pick:
+        ids, marks, qt = b.sequence(int(k))
+        items.append((ids, marks, qt))
+    return lib.Requests(items), items
+
+
+def _alone(m, item):
+    import torch
+    ids, marks, qt = item
+    so = [0, len(ids)]
+    logits = m.forward(device_ids(synth.Batch(np.asarray(ids, np.int32), np.array(so, np.int32),
+                                              np.asarray(marks, np.int32), np.array([qt], np.int32))),
+                       so, marks, [qt])
+    probs, answer, argmax, maxprob = m.probs(logits, so, marks, [qt])
+    torch.cuda.synchronize()
+    return (logits.cpu().numpy(), probs.cpu().numpy(), float(answer.cpu()[0]), int(argmax.cpu()[0]),
+            float(maxprob.cpu()[0]))
+
+
+@pytest.mark.parametrize("n_handles", [1, 3])
+def test_serve_matches_requests_alone(models, n_handles):
+    from encoder_transformer_amd import lib
+    m, shared = models
+    handles = ([m] + shared)[:n_handles]
+    req, items = _requests(40, 5 + n_handles)
+    res = lib.serve(handles, req, max_batch_tokens=6000)
+    assert res.n_batches > n_handles  # several micro-batches per handle
+    for r, item in enumerate(items):
+        lg, pr, ans, am, mp = _alone(m, item)
+        assert np.array_equal(res.request_logits(r), lg), r
+        assert np.array_equal(res.probs[req.mask_offsets[r]:req.mask_offsets[r + 1]], pr), r
+        assert res.answer[r] == np.float32(ans) and res.argmax[r] == am and res.maxprob[r] == np.float32(mp), r
+
+
+def test_serve_row_block_micro_batches(models):
+    from encoder_transformer_amd import lib
+    m, shared = models
+    req, items = _requests(60, 11)
+    res = lib.serve([m, shared[0]], req, max_batch_tokens=20000)  # micro-batches above 8,192 tokens
+    err = max(float(np.max(np.abs(res.request_logits(r) - _alone(m, it)[0]))) for r, it in enumerate(items))
+    print("serve row-block vs alone max |dlogit|", err)
+    assert err <= BF16_LOGIT_TIGHT
+
+
+def test_serve_rejects_before_any_work(models):
+    from encoder_transformer_amd import lib
+    m, _ = models
+    req, items = _requests(6, 3)
+    bad = list(items)
+    ids, marks, _ = bad[4]
+    bad[4] = (ids, marks, 7)  # no such question type
+    breq = lib.Requests(bad)
+    M = int(breq.mask_offsets[-1])
+    import ctypes
+    L = lib.load_library()
+    logits = np.full(M, 7.0, np.float32)
+    hs = (ctypes.c_void_p * 1)(m._h)
+    f = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    i = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    l64 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    other = [np.full(M, 7.0, np.float32), np.full(6, 7.0, np.float32), np.zeros(6, np.int32),
+             np.full(6, 7.0, np.float32)]
+    rc = L.jl_serve(hs, 1, 6, i(breq.ids), l64(breq.id_offsets), i(breq.mask_positions), l64(breq.mask_offsets),
+                    i(breq.qtype), 8192, f(logits), f(other[0]), f(other[1]), i(other[2]), f(other[3]), None)
+    assert rc == lib.ERR_QTYPE and "request 4" in L.jl_last_error().decode()
+    assert np.all(logits == 7.0) and np.all(other[0] == 7.0)
