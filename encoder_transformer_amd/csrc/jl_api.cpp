@@ -858,12 +858,16 @@ struct Launch {
   } while (0)
 
 // Sequence-wide attention takes 128-query work items (two 16-query sub-tiles
-// per wave reuse every K/V fragment read from LDS); the +-64 window takes
+// per wave reuse every K/V fragment read from LDS) when they give at least
+// one work-group per CU; fewer (short batches) leave CUs idle, and the
+// 64-query items, each half the chain, finish sooner.  The +-64 window takes
 // 64-query items: 3 key tiles per item, a shorter chain per work-group than
 // the 4 of a 128-query item (measured no faster).
 hipError_t attention(bool bf, AttnArgs at, const Plan &pl, bool whole_sequence, hipStream_t s) {
-  at.work = whole_sequence ? pl.d_aw_wide : pl.d_aw;
-  return launch_attention(bf, at, whole_sequence ? pl.n_work_wide : pl.n_work, whole_sequence ? 128 : 64, s);
+  constexpr int kCUs = 256;
+  const bool wide = whole_sequence && (long)pl.n_work_wide * kHeads >= kCUs;
+  at.work = wide ? pl.d_aw_wide : pl.d_aw;
+  return launch_attention(bf, at, wide ? pl.n_work_wide : pl.n_work, wide ? 128 : 64, s);
 }
 
 // A = LayerNorm(x; gain, shift) for launch_ln_gemm (a.A: the fallback's bf16/FP32 rows).

@@ -90,7 +90,7 @@ __device__ inline int xcd_tile(int b, int n_tiles) {
   return x * per + min(x, rem) + local;
 }
 
-template <typename T, int BM, int BN, int EM, int NSTAGE, bool LNA = false>
+template <typename T, int BM, int BN, int EM, int NSTAGE, bool LNA = false, int KFIX = 0>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int n_tiles) {
   constexpr int BK = GemmBK<T>::v, KS = BK / 32;           // 32-wide k sub-steps per stage
   constexpr int TM = BM / 2, TN = BN / 2;                   // wave tile
@@ -103,20 +103,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   static_assert(NT % 4 == 0, "epilogues pair columns within 64-column groups");
   // bf16: an NSTAGE-stage pipeline whose loads go straight from memory into
   // LDS (16 bytes per lane, lane i at block offset 16 i: the fragment order),
-  // so NSTAGE - 1 K-steps are in flight without staging registers (4 stages
-  // for grids that fit the CUs in one round, else 2, which leaves LDS for
-  // more resident work-groups); FP32: two LDS stages filled through registers.
+  // without staging registers.  The first NSTAGE K-steps are issued up front
+  // and step kt refills the buffer step kt - 1 read, so NSTAGE - 1 steps stay
+  // in flight; with NSTAGE >= K / BK (6 stages for K = 384, for grids that fit
+  // the CUs in one or two rounds) the whole K arrives in one memory round
+  // trip.  2 stages for larger grids leave LDS for more resident work-groups.
+  // FP32: two LDS stages filled through registers.
   // Each bf16 stage buffer is a variable of its own and the K loop is
   // unrolled over the stages: the compiler then knows which buffer each
   // in-flight LDS load writes and adds no wait of its own before reading
-  // another.
+  // another.  With K fixed at compile time (KFIX; the fused LayerNorm's
+  // K = 384) the K loop unrolls completely and every wait is exact; with a
+  // run-time K the compiler drains all loads once per round of stages.
   //
   // LNA (bf16, BM = 64, K = 384): A = LayerNorm(g.ln_x) rows, normalized by
   // the work-group itself into an LDS tile that holds all of K; only W
-  // streams through the stages.
+  // streams through the stages.  All 6 weight stages are issued first, then
+  // the rows: one memory round trip brings both, and once the rows are in,
+  // every stage has landed.
   constexpr bool kDma = std::is_same<T, bf16>::value;
   constexpr int NS = kDma ? NSTAGE : 2;
-  static_assert(NS >= 2 && NS <= 4, "stages");
+  static_assert(NS >= 2 && NS <= 6, "stages");
   static_assert(!LNA || (kDma && BM == 64), "fused LayerNorm: bf16, 64-row tiles");
   constexpr int KA = kWidth / 32;  // k sub-steps of the resident A tile
   constexpr int SA = kDma && !LNA ? A_BLKS * BLK : 1;
@@ -127,6 +134,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   __shared__ __attribute__((aligned(16))) T sA1[SA], sB1[kDma ? B_BLKS * BLK : 1];
   __shared__ __attribute__((aligned(16))) T sA2[NS > 2 ? SA : 1], sB2[kDma && NS > 2 ? B_BLKS * BLK : 1];
   __shared__ __attribute__((aligned(16))) T sA3[NS > 3 ? SA : 1], sB3[kDma && NS > 3 ? B_BLKS * BLK : 1];
+  __shared__ __attribute__((aligned(16))) T sA4[NS > 4 ? SA : 1], sB4[kDma && NS > 4 ? B_BLKS * BLK : 1];
+  __shared__ __attribute__((aligned(16))) T sA5[NS > 5 ? SA : 1], sB5[kDma && NS > 5 ? B_BLKS * BLK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -165,57 +174,121 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = g.K / BK;
-  // fused LayerNorm: each wave normalizes 16 rows, 8 at a time with all their
-  // loads in flight; lanes 0..47 hold 8 consecutive columns of a row and
-  // write them as one 16-byte run of the fragment-order A tile
-  auto ln_prologue = [&]() {
-    const bool act = lane < kWidth / 8;
-    const bool norm = g.ln_gain != nullptr;
-    f32x4 gm0 = f32x4{0.f, 0.f, 0.f, 0.f}, gm1 = gm0, sh0 = gm0, sh1 = gm0;  // absent shift: + 0
-    if (act && norm) {
-      gm0 = *reinterpret_cast<const f32x4 *>(g.ln_gain + lane * 8);
-      gm1 = *reinterpret_cast<const f32x4 *>(g.ln_gain + lane * 8 + 4);
+  constexpr int KC = LNA ? kWidth : KFIX;  // K when fixed at compile time
+  static_assert(KC % BK == 0, "K steps");
+  const int KT = KC ? KC / BK : g.K / BK;
+  // fused LayerNorm: each wave normalizes 16 rows with all their loads in
+  // flight; lanes 0..47 hold 8 consecutive columns of a row and write them as
+  // one 16-byte run of the fragment-order A tile
+  constexpr int LR = LNA ? BM / 4 : 1;  // rows per wave
+  f32x4 lnx[LR][2], lng[2], lns[2];
+  const bool ln_act = lane < kWidth / 8;
+  // the rows first: a wait the compiler places after the later, branchy
+  // parameter loads then only waits for data the LayerNorm needs next.  The
+  // loads are unconditional (lanes 48..63 re-read lane 47's columns, which
+  // the statistics ignore and nothing stores): a load under a branch would
+  // need a copy at the merge, and with it an early wait.
+  auto ln_load = [&]() {
+    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rr = 0; rr < LR; ++rr) {
+      const int row = min(m0 + wave * LR + rr, M - 1);
+      const float *xr = g.ln_x + (size_t)row * kWidth + min(lane, kWidth / 8 - 1) * 8;
+      lnx[rr][0] = *reinterpret_cast<const f32x4 *>(xr);
+      lnx[rr][1] = *reinterpret_cast<const f32x4 *>(xr + 4);
+    }
+    lng[0] = lng[1] = lns[0] = lns[1] = z;  // absent shift: + 0
+    if (ln_act && g.ln_gain != nullptr) {
+      lng[0] = *reinterpret_cast<const f32x4 *>(g.ln_gain + lane * 8);
+      lng[1] = *reinterpret_cast<const f32x4 *>(g.ln_gain + lane * 8 + 4);
       if (g.ln_shift) {
-        sh0 = *reinterpret_cast<const f32x4 *>(g.ln_shift + lane * 8);
-        sh1 = *reinterpret_cast<const f32x4 *>(g.ln_shift + lane * 8 + 4);
+        lns[0] = *reinterpret_cast<const f32x4 *>(g.ln_shift + lane * 8);
+        lns[1] = *reinterpret_cast<const f32x4 *>(g.ln_shift + lane * 8 + 4);
       }
     }
-    const float gm[8] = {gm0[0], gm0[1], gm0[2], gm0[3], gm1[0], gm1[1], gm1[2], gm1[3]};
-    const float sh[8] = {sh0[0], sh0[1], sh0[2], sh0[3], sh1[0], sh1[1], sh1[2], sh1[3]};
+  };
+  auto ln_finish = [&]() {
+    const bool norm = g.ln_gain != nullptr;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float y[8][8];
+    for (int rr = 0; rr < LR; ++rr) {
+      const int rl = wave * LR + rr;
+      float y[8];
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int row = min(m0 + wave * (BM / 4) + half * 8 + rr, M - 1);
-        f32x4 v0 = f32x4{0.f, 0.f, 0.f, 0.f}, v1 = v0;
-        if (act) {
-          const float *xr = g.ln_x + (size_t)row * kWidth + lane * 8;
-          v0 = *reinterpret_cast<const f32x4 *>(xr);
-          v1 = *reinterpret_cast<const f32x4 *>(xr + 4);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[rr][e] = v0[e];
-          y[rr][4 + e] = v1[e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        y[e] = lnx[rr][0][e];
+        y[4 + e] = lnx[rr][1][e];
       }
+      if (norm) {
+        float mean, rstd;
+        row8_stats(y, ln_act, mean, rstd);
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int rl = wave * (BM / 4) + half * 8 + rr;
-        if (norm) {
-          float mean, rstd;
-          row8_stats(y[rr], act, mean, rstd);
+        for (int e = 0; e < 8; ++e) y[e] = (y[e] - mean) * rstd * lng[e >> 2][e & 3] + lns[e >> 2][e & 3];
+      }
+      if (ln_act) {
+        Frag<T> f;
+        frag_from(f, y);
+        // (row rl, k = 8 lane): block (rl / 16, lane / 4), lane (rl % 16) + 16 (lane % 4)
+        store_frag(&sAk[((rl >> 4) * KA + (lane >> 2)) * BLK + ((rl & 15) + 16 * (lane & 3)) * FE], f);
+      }
+    }
+  };
+  // epilogue coordinates: acc[i][j][r] = C[row0 + 16i + r][col0 + 16j]
+  const int row0 = m0 + wm * TM + (lane >> 4) * 4;
+  const int wcol = n0 + wn * TN;            // first of this wave's TN columns
+  const int col0 = wcol + lr;
+  // Epilogue operands that do not depend on the product (bias, RoPE table
+  // rows, the residual) are all read before the first store: a load that
+  // follows a store to C may alias it, and the compiler would then wait for
+  // every earlier memory operation at each row.  A 64-row tile (kHoist)
+  // reads them before the K loop (the table rows, which need the positions,
+  // after the fused LayerNorm or else at the epilogue), larger tiles one
+  // 16-row group at a time.
+  constexpr bool kHoist = kDma && BM == 64;
+  constexpr int HG = kHoist ? MT : 1;  // row groups held at once
+  const bool has_bias = g.bias != nullptr;
+  const bool rope = EM == E_STORE && g.rope_cos != nullptr;
+  float bias_v[NT];
+  int rpos[HG][4];
+  float rcs[HG][4][4];  // per row: cos and sin of d = lr, then of d = 16 + lr
+  float res[EM == E_RESID ? HG : 1][4][EM == E_RESID ? NT : 1];
+  auto load_bias = [&]() {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[rr][e] = (y[rr][e] - mean) * rstd * gm[e] + sh[e];
-        }
-        if (act) {
-          Frag<T> f;
-          frag_from(f, y[rr]);
-          // (row rl, k = 8 lane): block (rl / 16, lane / 4), lane (rl % 16) + 16 (lane % 4)
-          store_frag(&sAk[((rl >> 4) * KA + (lane >> 2)) * BLK + ((rl & 15) + 16 * (lane & 3)) * FE], f);
-        }
+    for (int j = 0; j < NT; ++j) bias_v[j] = 0.f;
+    if (has_bias) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) bias_v[j] = g.bias[col0 + j * 16];
+    }
+  };
+  auto load_pos = [&](int i, int h) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rpos[h][r] = g.pos[min(row0 + i * 16 + r, M - 1)];
+  };
+  auto load_rope = [&](int h) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int q = rpos[h][r] * 32 + j * 16 + lr;
+        rcs[h][r][2 * j] = g.rope_cos[q];
+        rcs[h][r][2 * j + 1] = g.rope_sin[q];
+      }
+  };
+  auto load_res = [&](int i, int h) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float *C = (const float *)g.C + (size_t)min(row0 + i * 16 + r, M - 1) * g.ldc + col0;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) res[h][r][j] = C[j * 16];
+    }
+  };
+  // the operands a 64-row tile reads before its K loop
+  auto load_hoisted = [&]() {
+    load_bias();
+    if constexpr (kHoist) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        if constexpr (EM == E_RESID) load_res(i, i);
+        if (rope) load_pos(i, i);
       }
     }
   };
@@ -246,18 +319,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
       if constexpr (B == 0) return sA0;
       else if constexpr (B == 1) return sA1;
       else if constexpr (B == 2) return sA2;
-      else return sA3;
+      else if constexpr (B == 3) return sA3;
+      else if constexpr (B == 4) return sA4;
+      else return sA5;
     };
     auto bufB = [&](auto Bc) -> T * {
       constexpr int B = decltype(Bc)::value;
       if constexpr (B == 0) return sB0;
       else if constexpr (B == 1) return sB1;
       else if constexpr (B == 2) return sB2;
-      else return sB3;
+      else if constexpr (B == 3) return sB3;
+      else if constexpr (B == 4) return sB4;
+      else return sB5;
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
     // stage kt -> LDS buffer pair (dA, dB), one 1 KB fragment block per load
     auto issue_stage = [&](int kt, T *dA, T *dB) {
       const int k0 = kt * BK + lc;
@@ -275,38 +355,86 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
                                          (lds_void *)&dB[q * BLK], 16, 0, 0);
       }
     };
+    // wait until at most `later` stages younger than the current one are in
+    // flight (the immediate must be a constant)
+    auto wait_stages = [&](int later) {
+      switch (later) {
+        case 0: __builtin_amdgcn_s_waitcnt(vm_wait_imm(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPS)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * LPS)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * LPS)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(vm_wait_imm(4 * LPS)); break;
+        default: __builtin_amdgcn_s_waitcnt(vm_wait_imm(5 * LPS)); break;
+      }
+    };
     // K-step kt from buffer B (= kt % NS): wait for this wave's loads of the
-    // step (at most `later` younger steps stay in flight), then a bare
-    // barrier: every wave's loads of the step have landed and every wave is
-    // done reading the previous step's buffer, which the next load refills.
+    // step, then a bare barrier: every wave's loads of the step have landed
+    // and every wave is done reading the previous step's buffer, which step
+    // kt (> 0) refills.  Younger stages in flight at the wait: the other
+    // up-front stages (kt = 0), else those issued by steps 1 .. kt - 1.
+    // With every stage in before the LayerNorm (kAllIn), one barrier after
+    // the A tile's LDS stores is all the loop needs.
+    constexpr bool kAllIn = LNA && NS * BK >= kWidth;
     auto step = [&](int kt, auto Bc) {
       constexpr int B = decltype(Bc)::value;
-      const int later = min(NS - 2, KT - 1 - kt);
-      if (later <= 0) __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-      else if (NS == 3 || later == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPS));
-      else __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * LPS));
-      if constexpr (LNA)
-        if (kt == 0) __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the A tile's LDS stores
-      __builtin_amdgcn_s_barrier();
-      using Next = std::integral_constant<int, (B + NS - 1) % NS>;
-      if (kt + NS - 1 < KT) issue_stage(kt + NS - 1, bufA(Next()), bufB(Next()));
+      if constexpr (kAllIn) {
+        if (kt == 0) {
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the A tile's LDS stores
+          __builtin_amdgcn_s_barrier();
+        }
+      } else {
+        wait_stages(kt == 0 ? min(KT, NS) - 1 : min(KT - 1 - kt, NS - 2));
+        if constexpr (LNA)
+          if (kt == 0) __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the A tile's LDS stores
+        __builtin_amdgcn_s_barrier();
+        using Next = std::integral_constant<int, (B + NS - 1) % NS>;
+        if (kt > 0 && kt + NS - 1 < KT) issue_stage(kt + NS - 1, bufA(Next()), bufB(Next()));
+      }
       compute(bufA(Bc), bufB(Bc), kt);
     };
+    // loads older than every stage never hold up a stage wait
+    if constexpr (!LNA) load_hoisted();
     issue_stage(0, sA0, sB0);
+    if (KT > 1) issue_stage(1, sA1, sB1);
     if constexpr (NS > 2)
-      if (KT > 1) issue_stage(1, sA1, sB1);
-    if constexpr (NS > 3)
       if (KT > 2) issue_stage(2, bufA(I2()), bufB(I2()));
-    if constexpr (LNA) ln_prologue();  // the first weight stages are already in flight
-    for (int kt = 0; kt < KT; kt += NS) {
+    if constexpr (NS > 3)
+      if (KT > 3) issue_stage(3, bufA(I3()), bufB(I3()));
+    if constexpr (NS > 4)
+      if (KT > 4) issue_stage(4, bufA(I4()), bufB(I4()));
+    if constexpr (NS > 5)
+      if (KT > 5) issue_stage(5, bufA(I5()), bufB(I5()));
+    if constexpr (LNA) {
+      ln_load();
+      load_hoisted();
+      ln_finish();  // waits for the rows, younger than every stage: all stages have landed
+      if constexpr (kAllIn) {
+        if (rope) {
+#pragma unroll
+          for (int i = 0; i < MT; ++i) load_rope(i);
+        }
+      }
+    }
+    auto round = [&](int kt) {  // steps kt .. kt + NS - 1
       step(kt, I0());
       if (kt + 1 < KT) step(kt + 1, I1());
       if constexpr (NS > 2)
         if (kt + 2 < KT) step(kt + 2, I2());
       if constexpr (NS > 3)
-        if (kt + 3 < KT) step(kt + 3, std::integral_constant<int, NS - 1>());
+        if (kt + 3 < KT) step(kt + 3, I3());
+      if constexpr (NS > 4)
+        if (kt + 4 < KT) step(kt + 4, I4());
+      if constexpr (NS > 5)
+        if (kt + 5 < KT) step(kt + 5, I5());
+    };
+    if constexpr (KC != 0) {
+#pragma unroll
+      for (int kt = 0; kt < KT; kt += NS) round(kt);
+    } else {
+      for (int kt = 0; kt < KT; kt += NS) round(kt);
     }
   } else {
+    load_bias();
     load_stage(0);
     store_stage(0);
     __syncthreads();
@@ -319,12 +447,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     }
   }
 
-  // epilogue: acc[i][j][r] = C[row0 + 16i + r][col0 + 16j]
-  const int row0 = m0 + wm * TM + (lane >> 4) * 4;
-  const int wcol = n0 + wn * TN;            // first of this wave's TN columns
-  const int col0 = wcol + lr;
+  // epilogue, one 16-row group at a time
+  if constexpr (kHoist && !(LNA && NS * BK >= kWidth)) {
+    if (rope) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) load_rope(i);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
+    const int h = kHoist ? i : 0;
+    if constexpr (!kHoist) {
+      if constexpr (EM == E_RESID) load_res(i, 0);
+      if (rope) {
+        load_pos(i, 0);
+        load_rope(0);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = row0 + i * 16 + r;
@@ -341,23 +480,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
         }
         continue;
       }
-      if (g.bias) {
+      if (has_bias) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) v[j] += g.bias[col0 + j * 16];
+        for (int j = 0; j < NT; ++j) v[j] += bias_v[j];
       }
       if (EM == E_STORE) {
-        if (g.rope_cos) {  // each 64-column group is one head: pairs (d, d + 32)
-          const int p = g.pos[row];
+        if (rope) {  // each 64-column group is one head: pairs (d, d + 32)
 #pragma unroll
           for (int hb = 0; hb < NT / 4; ++hb) {
             if (wcol + hb * 64 >= g.rope_cols) break;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-              const int d = j * 16 + lr;
-              const float c = g.rope_cos[p * 32 + d], s = g.rope_sin[p * 32 + d];
+              const float c = rcs[h][r][2 * j], sn = rcs[h][r][2 * j + 1];
               const float lo = v[hb * 4 + j], hi = v[hb * 4 + j + 2];
-              v[hb * 4 + j] = lo * c - hi * s;
-              v[hb * 4 + j + 2] = hi * c + lo * s;
+              v[hb * 4 + j] = lo * c - hi * sn;
+              v[hb * 4 + j + 2] = hi * c + lo * sn;
             }
           }
         }
@@ -367,7 +504,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
       } else if (EM == E_RESID) {
         float *C = (float *)g.C + (size_t)row * g.ldc + col0;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) C[j * 16] += v[j];
+        for (int j = 0; j < NT; ++j) C[j * 16] = res[h][r][j] + v[j];
       } else if (EM == E_RELU) {
         T *C = (T *)g.C + (size_t)row * g.ldc + col0;
 #pragma unroll
@@ -513,15 +650,29 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const T *kbase = (const T *)a.k + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
   const T *vbase = (const T *)a.v + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
   const int last = w.kv_len - 1;
+  // this thread's rows of tile 0 (keys lo + tid / 8 and + 32; values
+  // lo + 2 (tid / 8) and + 1); a full tile t is those rows + 64 t, a
+  // wave-uniform offset, so only the sequence's last tile clamps per row
+  const T *kp0 = kbase + (size_t)(lo + (tid >> 3)) * a.kv_stride;
+  const T *vp0 = vbase + (size_t)(lo + 2 * (tid >> 3)) * a.kv_stride;
+  const size_t r32 = (size_t)32 * a.kv_stride, r1 = (size_t)a.kv_stride;
   Frag<T> rk0, rk1, rv0, rv1;
   auto load_tile = [&](int t) {
     const int base = lo + t * 64;
-    const int k0 = base + (tid >> 3);
-    const int v0 = base + 2 * (tid >> 3);
-    rk0 = load_frag(kbase + (size_t)min(k0, last) * a.kv_stride);
-    rk1 = load_frag(kbase + (size_t)min(k0 + 32, last) * a.kv_stride);
-    rv0 = load_frag(vbase + (size_t)min(v0, last) * a.kv_stride);
-    rv1 = load_frag(vbase + (size_t)min(v0 + 1, last) * a.kv_stride);
+    if (base + 64 <= w.kv_len) {
+      const size_t off = (size_t)(t * 64) * a.kv_stride;
+      rk0 = load_frag(kp0 + off);
+      rk1 = load_frag(kp0 + off + r32);
+      rv0 = load_frag(vp0 + off);
+      rv1 = load_frag(vp0 + off + r1);
+    } else {
+      const int k0 = base + (tid >> 3);
+      const int v0 = base + 2 * (tid >> 3);
+      rk0 = load_frag(kbase + (size_t)min(k0, last) * a.kv_stride);
+      rk1 = load_frag(kbase + (size_t)min(k0 + 32, last) * a.kv_stride);
+      rv0 = load_frag(vbase + (size_t)min(v0, last) * a.kv_stride);
+      rv1 = load_frag(vbase + (size_t)min(v0 + 1, last) * a.kv_stride);
+    }
   };
   auto store_tile = [&](int buf) {
     const int c = (tid & 7) * 8;
@@ -820,19 +971,19 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BN, int NS, bool LNA = false>
+template <typename T, int BM, int BN, int NS, bool LNA = false, int KFIX = 0>
 static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
   const int tiles_n = a.N / BN, n_tiles = ((a.M + BM - 1) / BM) * tiles_n;
   switch (emode) {
-    case E_STORE: gemm_kernel<T, BM, BN, E_STORE, NS, LNA><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_GEGLU: gemm_kernel<T, BM, BN, E_GEGLU, NS, LNA><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_RELU: gemm_kernel<T, BM, BN, E_RELU, NS, LNA><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_STORE: gemm_kernel<T, BM, BN, E_STORE, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_GEGLU: gemm_kernel<T, BM, BN, E_GEGLU, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_RELU: gemm_kernel<T, BM, BN, E_RELU, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
     case E_RESID:
       if constexpr (LNA) return hipErrorInvalidValue;
-      else gemm_kernel<T, BM, BN, E_RESID, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      else gemm_kernel<T, BM, BN, E_RESID, NS, false, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     case E_GELU_F32:
-      if constexpr (LNA) return hipErrorInvalidValue;
+      if constexpr (LNA || KFIX != 0) return hipErrorInvalidValue;
       else gemm_kernel<T, BM, BN, E_GELU_F32, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     default: return hipErrorInvalidValue;
@@ -849,7 +1000,13 @@ hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t
     if (((a.M + 255) / 256) * nt >= 256) return gemm_dispatch<bf16, 256, 128, 2>(emode, a, s);
     if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<bf16, 128, 128, 2>(emode, a, s);
     if (((a.M + 63) / 64) * nt > 256) return gemm_dispatch<bf16, 64, 128, 2>(emode, a, s);
-    return gemm_dispatch<bf16, 64, 128, 4>(emode, a, s);
+    // one round of work-groups: the model's K values get a fully unrolled K loop
+    switch (a.K) {
+      case kWidth: return gemm_dispatch<bf16, 64, 128, 6, false, kWidth>(emode, a, s);
+      case kGeglu: return gemm_dispatch<bf16, 64, 128, 6, false, kGeglu>(emode, a, s);
+      case kHeadFfn: return gemm_dispatch<bf16, 64, 128, 6, false, kHeadFfn>(emode, a, s);
+      default: return gemm_dispatch<bf16, 64, 128, 6>(emode, a, s);
+    }
   }
   if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<float, 128, 128, 2>(emode, a, s);
   return gemm_dispatch<float, 64, 128, 2>(emode, a, s);
@@ -862,8 +1019,12 @@ hipError_t launch_ln_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStrea
   // the GEMM alone would take 64-row tiles: normalize inside it
   if (bf16_mode && (emode == E_STORE || emode == E_GEGLU || emode == E_RELU) &&
       ((a.M + 127) / 128) * nt < 256) {
-    if (tiles64 > 256) return gemm_dispatch<bf16, 64, 128, 2, true>(emode, a, s);
-    return gemm_dispatch<bf16, 64, 128, 4, true>(emode, a, s);
+    // one round of work-groups (1 per CU: 144 KB of LDS): 6 stages of a
+    // 128-column tile, or 3 of a 256-column tile when 128 would need two
+    if (tiles64 <= 256) return gemm_dispatch<bf16, 64, 128, 6, true>(emode, a, s);
+    if (a.N % 256 == 0 && ((a.M + 63) / 64) * (a.N / 256) <= 256)
+      return gemm_dispatch<bf16, 64, 256, 3, true>(emode, a, s);
+    return gemm_dispatch<bf16, 64, 128, 2, true>(emode, a, s);
   }
   hipError_t e = launch_ln_rows(bf16_mode, a.ln_x, a.ln_gain, a.ln_shift, a.M, const_cast<void *>(a.A), s);
   if (e != hipSuccess) return e;
