@@ -62,10 +62,19 @@ __global__ __launch_bounds__(512, 1) void head_kernel(HeadArgs a) {
     const int ngo[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
     wp_start(po, a.Wo, KSD, ngo, 0, lane);
   }
-  for (int c = tid; c < RB * (kWidth / 8); c += 512) {
-    const int r = c / (kWidth / 8), k = (c % (kWidth / 8)) * 8;
-    const int src = min(row0 + r, T - 1);
-    *reinterpret_cast<bf16x8 *>(&sA[afrag(r, k, KSD)]) = ldg8(a.o + (size_t)src * kWidth + k);
+  // attention output rows -> sA (fragment order), all loads of a thread in
+  // flight before its first LDS store
+  constexpr int OL = RB * (kWidth / 8) / 512;
+  bf16x8 ov[OL];
+#pragma unroll
+  for (int q = 0; q < OL; ++q) {
+    const int c = tid + 512 * q, r = c / (kWidth / 8), k = (c % (kWidth / 8)) * 8;
+    ov[q] = ldg8(a.o + (size_t)min(row0 + r, T - 1) * kWidth + k);
+  }
+#pragma unroll
+  for (int q = 0; q < OL; ++q) {
+    const int c = tid + 512 * q, r = c / (kWidth / 8), k = (c % (kWidth / 8)) * 8;
+    *reinterpret_cast<bf16x8 *>(&sA[afrag(r, k, KSD)]) = ov[q];
   }
   __syncthreads();
 

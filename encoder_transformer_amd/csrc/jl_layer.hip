@@ -97,15 +97,24 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
     wp_start(po, a.Wo, KSD, ngo, 0, lane);  // needs nothing: first
   }
 
-  // 1. attention output rows -> sA (fragment order); the RoPE table rows of
-  //    this block's positions -> LDS, for the next layer's q and k
-  for (int c = tid; c < RB * (kWidth / 8); c += 512) {
-    const int r = c / (kWidth / 8), k = (c % (kWidth / 8)) * 8;
-    const int src = min(row0 + r, T - 1);
-    *reinterpret_cast<bf16x8 *>(&sA[afrag(r, k, KSD)]) = ldg8(a.o + (size_t)src * kWidth + k);
+  // 1. attention output rows -> sA (fragment order), all 6 loads of a thread
+  //    in flight before the first LDS store; the position of this thread's
+  //    RoPE row, whose table rows are staged later, away from this phase
+  constexpr int OL = RB * (kWidth / 8) / 512;  // 16-byte loads per thread
+  static_assert(OL * 512 == RB * (kWidth / 8), "o staging");
+  bf16x8 ov[OL];
+#pragma unroll
+  for (int q = 0; q < OL; ++q) {
+    const int c = tid + 512 * q, r = c / (kWidth / 8), k = (c % (kWidth / 8)) * 8;
+    ov[q] = ldg8(a.o + (size_t)min(row0 + r, T - 1) * kWidth + k);
   }
-  if (!kHeadNext && next_layer)
-    stage_rope(sCos, sSin, a.rope_cos_next, a.rope_sin_next, tid, [&](int r) { return a.pos[min(row0 + r, T - 1)]; });
+  const bool rope_next = !kHeadNext && next_layer;
+  const int rope_pos = rope_next ? a.pos[min(row0 + (tid >> 3), T - 1)] : 0;
+#pragma unroll
+  for (int q = 0; q < OL; ++q) {
+    const int c = tid + 512 * q, r = c / (kWidth / 8), k = (c % (kWidth / 8)) * 8;
+    *reinterpret_cast<bf16x8 *>(&sA[afrag(r, k, KSD)]) = ov[q];
+  }
   __syncthreads();
 
   // 2. X = x + o . W_o^T   (wave w: columns 48w .. 48w+47, 3 groups of 16)
@@ -186,8 +195,21 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
     start_wout(po, a, 4, lane, wave);
     __syncthreads();
   }
-  // last W_out
+  // last W_out, with the RoPE table rows of this block's positions (the next
+  // layer's q and k) in flight; they reach LDS after it, and the barriers of
+  // the row statistics below publish them
+  f32x4 rc, rs;
+  if (rope_next) {
+    const int q = (tid & 7) * 4;
+    rc = *reinterpret_cast<const f32x4 *>(a.rope_cos_next + rope_pos * 32 + q);
+    rs = *reinterpret_cast<const f32x4 *>(a.rope_sin_next + rope_pos * 32 + q);
+  }
   wp_run<4>(X, po, sH0, lane, NoNext());
+  if (rope_next) {
+    const int r = tid >> 3, q = (tid & 7) * 4;
+    *reinterpret_cast<f32x4 *>(&sCos[r * 32 + q]) = rc;
+    *reinterpret_cast<f32x4 *>(&sSin[r * 32 + q]) = rs;
+  }
 
   // 5. after the last layer: h = LayerNorm_final(X) + type row, into x (in
   //    head mode also kept in X for the head's first layer); otherwise the
