@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   constexpr int A_BLKS = (BM / 16) * KS, B_BLKS = (BN / 16) * KS;
   constexpr int A_PER_WAVE = A_BLKS / 4, B_PER_WAVE = B_BLKS / 4;
   static_assert(A_BLKS % 4 == 0 && B_BLKS % 4 == 0, "tile must split over 4 waves");
-  static_assert(NT % 4 == 0, "epilogues pair columns within 64-column groups");
+  static_assert(NT % 4 == 0 || EM == E_RESID || EM == E_RELU || EM == E_GELU_F32,
+                "GEGLU and RoPE epilogues pair columns within 64-column groups");
   // bf16: an NSTAGE-stage pipeline whose loads go straight from memory into
   // LDS (16 bytes per lane, lane i at block offset 16 i: the fragment order),
   // without staging registers.  The first NSTAGE K-steps are issued up front
@@ -974,9 +975,16 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
 template <typename T, int BM, int BN, int NS, bool LNA = false, int KFIX = 0>
 static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
   const int tiles_n = a.N / BN, n_tiles = ((a.M + BM - 1) / BM) * tiles_n;
+  constexpr bool pairs = (BN / 32) % 4 == 0;  // 64-column groups per wave: GEGLU and RoPE epilogues
   switch (emode) {
-    case E_STORE: gemm_kernel<T, BM, BN, E_STORE, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
-    case E_GEGLU: gemm_kernel<T, BM, BN, E_GEGLU, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_STORE:
+      if constexpr (!pairs) return hipErrorInvalidValue;
+      else gemm_kernel<T, BM, BN, E_STORE, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      break;
+    case E_GEGLU:
+      if constexpr (!pairs) return hipErrorInvalidValue;
+      else gemm_kernel<T, BM, BN, E_GEGLU, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      break;
     case E_RELU: gemm_kernel<T, BM, BN, E_RELU, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
     case E_RESID:
       if constexpr (LNA) return hipErrorInvalidValue;
@@ -991,7 +999,8 @@ static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile choice: the largest M tile that still gives at least one tile per CU.
+// Tile choice: the largest M tile that still gives at least one tile per CU;
+// grids of at most one tile per CU take the deep pipeline below.
 hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (a.N % 128 != 0 || a.K % 64 != 0) return hipErrorInvalidValue;
@@ -1000,7 +1009,29 @@ hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t
     if (((a.M + 255) / 256) * nt >= 256) return gemm_dispatch<bf16, 256, 128, 2>(emode, a, s);
     if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<bf16, 128, 128, 2>(emode, a, s);
     if (((a.M + 63) / 64) * nt > 256) return gemm_dispatch<bf16, 64, 128, 2>(emode, a, s);
-    // one round of work-groups: the model's K values get a fully unrolled K loop
+    // One round of work-groups: the model's K values get a fully unrolled K
+    // loop.  Such a grid is bound by each work-group's own memory round trip
+    // and by what one CU can take in, so a residual update (N = 384) takes
+    // the smallest tile that still fits the CUs in one round: 32 x 64 moves
+    // (32 + 64) K elements per work-group against 192 K for 64 x 128.
+    if (emode == E_RESID && a.N % 64 == 0) {
+      const long t32 = ((a.M + 31) / 32) * (a.N / 64), t64 = ((a.M + 63) / 64) * (a.N / 64);
+      if (t32 <= 256 || t64 <= 256) {
+        const bool r32 = t32 <= 256;
+        switch (a.K) {
+          case kWidth:
+            return r32 ? gemm_dispatch<bf16, 32, 64, 6, false, kWidth>(emode, a, s)
+                       : gemm_dispatch<bf16, 64, 64, 6, false, kWidth>(emode, a, s);
+          case kGeglu:
+            return r32 ? gemm_dispatch<bf16, 32, 64, 6, false, kGeglu>(emode, a, s)
+                       : gemm_dispatch<bf16, 64, 64, 6, false, kGeglu>(emode, a, s);
+          case kHeadFfn:
+            return r32 ? gemm_dispatch<bf16, 32, 64, 6, false, kHeadFfn>(emode, a, s)
+                       : gemm_dispatch<bf16, 64, 64, 6, false, kHeadFfn>(emode, a, s);
+          default: break;
+        }
+      }
+    }
     switch (a.K) {
       case kWidth: return gemm_dispatch<bf16, 64, 128, 6, false, kWidth>(emode, a, s);
       case kGeglu: return gemm_dispatch<bf16, 64, 128, 6, false, kGeglu>(emode, a, s);
@@ -1009,6 +1040,8 @@ hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t
     }
   }
   if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<float, 128, 128, 2>(emode, a, s);
+  // the FP32 scorer on the marker rows: narrower tiles, twice the work-groups
+  if (emode == E_GELU_F32 && ((a.M + 63) / 64) * (a.N / 64) <= 256) return gemm_dispatch<float, 64, 64, 2>(emode, a, s);
   return gemm_dispatch<float, 64, 128, 2>(emode, a, s);
 }
 

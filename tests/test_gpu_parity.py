@@ -220,6 +220,41 @@ def test_batch_composition_and_order(models, path):
         m.set_row_block_min_tokens(8192)
 
 
+def test_per_gemm_tile_regimes_bitwise(models):
+    """The per-GEMM schedule picks its tiles and pipeline depth from the packed
+    token count T: for the N = 384 residual updates 32 x 64 tiles (up to 42
+    row blocks of 32), 64 x 64 (up to 42 of 64), 6-stage 64 x 128 (up to 85
+    of 64) and the 2-stage tiles of larger grids.  Each output element still
+    sums over K in the same order, so a sequence's logits are bitwise the same
+    in every regime."""
+    def regime(t):
+        if -(-t // 32) * 6 <= 256:
+            return "32x64"
+        if -(-t // 64) * 6 <= 256:
+            return "64x64"
+        return "64x128/6" if -(-t // 64) * 3 <= 256 else "64x128/2"
+
+    m = models["bf16"]
+    base = synth.make_batch(4)
+    lens = np.diff(base.seq_offsets)
+    s0 = int(np.argmax(lens < 1300))
+    others = [b for b in range(base.n_seqs) if b != s0]
+    totals = lens[s0] + np.cumsum(lens[others])
+    m.set_row_block_min_tokens(1 << 62)
+    try:
+        ref = run_logits(m, base.subset([s0]))
+        regimes = {regime(int(lens[s0]))}
+        for target in (2000, 4000, 6200):
+            k = int(np.searchsorted(totals, target)) + 1
+            batch = base.subset([s0] + others[:k])
+            regimes.add(regime(batch.n_tokens))
+            got = run_logits(m, batch)
+            assert np.array_equal(got[:len(ref)], ref), (target, batch.n_tokens)
+        assert len(regimes) == 4, regimes
+    finally:
+        m.set_row_block_min_tokens(8192)
+
+
 def test_row_block_and_per_gemm_paths_agree(models):
     """The two bf16 schedules compute the same function (rounding aside)."""
     m = models["bf16"]
