@@ -74,44 +74,40 @@ __device__ inline float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
-// Sum over the 64 lanes without LDS: butterflies inside each 16-lane row by
-// DPP (xor 1, xor 2 through quad permutes, then the 8- and 16-lane mirrors),
-// then across rows by the row-swap permutes.  Every lane gets the same value,
-// and the summation order is fixed, so any kernel using it reduces a row of
-// data bit-identically.
 template <int CTRL>
 __device__ inline float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
-__device__ inline float wave_sum_lanes(float v) {
+// Sum over each 16-lane row of the wave without LDS: butterflies by DPP (xor
+// 1 and xor 2 through quad permutes, then the 8- and 16-lane mirrors).  Every
+// lane of a row gets the same value and the summation order is fixed, so any
+// kernel using it reduces a row of data bit-identically.
+__device__ inline float row16_sum(float v) {
 #pragma clang fp contract(off)
   v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp<0x141>(v);  // row_half_mirror (8 lanes)
   v += dpp<0x140>(v);  // row_mirror (16 lanes)
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  return v;
 }
 
-// LayerNorm statistics of one 384-wide row held as 8 consecutive values in
-// each of lanes 0..47 (lanes 48..63 pass zeros): two passes, biased
-// variance.  Shared by the LayerNorm kernel and the fused LayerNorm of the
-// GEMM, which therefore produce identical operands.
-__device__ inline void row8_stats(const float (&y)[8], bool act, float &mean, float &rstd) {
+// LayerNorm statistics of one 384-wide row held by a 16-lane row of the
+// wave: lane j holds columns 64 c + 4 j .. 64 c + 4 j + 3 in x[c], c = 0..5.
+// Two passes, biased variance.  Shared by the LayerNorm kernel and the fused
+// LayerNorm of the GEMM, which therefore produce identical operands.
+__device__ inline void ln_row16(const f32x4 (&x)[6], float &mean, float &rstd) {
 #pragma clang fp contract(off)
-  float sum = 0.f;
+  float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sum += y[e];
-  mean = wave_sum_lanes(act ? sum : 0.f) * (1.0f / kWidth);
+  for (int c = 0; c < 6; ++c) s += (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
+  mean = row16_sum(s) * (1.0f / kWidth);
   float q = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float d = y[e] - mean;
-    q += d * d;
+  for (int c = 0; c < 6; ++c) {
+    const float d0 = x[c][0] - mean, d1 = x[c][1] - mean, d2 = x[c][2] - mean, d3 = x[c][3] - mean;
+    q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
   }
-  rstd = rsqrtf(wave_sum_lanes(act ? q : 0.f) * (1.0f / kWidth) + kLnEps);
+  rstd = rsqrtf(row16_sum(q) * (1.0f / kWidth) + kLnEps);
 }
 
 __device__ inline float wave_max(float v) {

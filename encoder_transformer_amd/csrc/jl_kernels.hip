@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
 // rows x 64 contiguous bytes), writes it to LDS linearly and every fragment
 // read is one linear 16-byte read per lane: no bank conflicts either way.
 // LayerNorm, where the model has one, is applied beforehand by
-// ln_rows_kernel, once per row.
+// ln_rows_kernel, once per row, or, when the grid takes 64-row tiles, by the
+// GEMM itself on its rows (the same arithmetic, so the same operands).
 //
 // The grid is 1-D.  Work-groups are dispatched to the 8 XCDs round-robin, so
 // block b is remapped to tile t such that every XCD owns a contiguous run of
@@ -178,58 +179,61 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   constexpr int KC = LNA ? kWidth : KFIX;  // K when fixed at compile time
   static_assert(KC % BK == 0, "K steps");
   const int KT = KC ? KC / BK : g.K / BK;
-  // fused LayerNorm: each wave normalizes 16 rows with all their loads in
-  // flight; lanes 0..47 hold 8 consecutive columns of a row and write them as
-  // one 16-byte run of the fragment-order A tile
-  constexpr int LR = LNA ? BM / 4 : 1;  // rows per wave
-  f32x4 lnx[LR][2], lng[2], lns[2];
-  const bool ln_act = lane < kWidth / 8;
-  // the rows first: a wait the compiler places after the later, branchy
-  // parameter loads then only waits for data the LayerNorm needs next.  The
-  // loads are unconditional (lanes 48..63 re-read lane 47's columns, which
-  // the statistics ignore and nothing stores): a load under a branch would
-  // need a copy at the merge, and with it an early wait.
+  // fused LayerNorm: each wave normalizes 16 rows, 4 at a time, one per
+  // 16-lane row of the wave (lane j: columns 64 c + 4 j .. + 3, c = 0..5),
+  // with all their loads in flight; the gain and shift columns of a lane are
+  // the same in every pass.  The rows are loaded first: a wait the compiler
+  // places after the later, branchy parameter loads then only waits for data
+  // the LayerNorm needs next.
+  constexpr int LP = LNA ? BM / 16 : 1;  // passes of 4 rows per wave
+  const int lj = lane & 15;
+  f32x4 lnx[LP][6], lng[6], lns[6];
   auto ln_load = [&]() {
     const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rr = 0; rr < LR; ++rr) {
-      const int row = min(m0 + wave * LR + rr, M - 1);
-      const float *xr = g.ln_x + (size_t)row * kWidth + min(lane, kWidth / 8 - 1) * 8;
-      lnx[rr][0] = *reinterpret_cast<const f32x4 *>(xr);
-      lnx[rr][1] = *reinterpret_cast<const f32x4 *>(xr + 4);
+    for (int p = 0; p < LP; ++p) {
+      const int row = min(m0 + wave * (BM / 4) + 4 * p + (lane >> 4), M - 1);
+      const float *xr = g.ln_x + (size_t)row * kWidth + 4 * lj;
+#pragma unroll
+      for (int c = 0; c < 6; ++c) lnx[p][c] = *reinterpret_cast<const f32x4 *>(xr + 64 * c);
     }
-    lng[0] = lng[1] = lns[0] = lns[1] = z;  // absent shift: + 0
-    if (ln_act && g.ln_gain != nullptr) {
-      lng[0] = *reinterpret_cast<const f32x4 *>(g.ln_gain + lane * 8);
-      lng[1] = *reinterpret_cast<const f32x4 *>(g.ln_gain + lane * 8 + 4);
+#pragma unroll
+    for (int c = 0; c < 6; ++c) lng[c] = lns[c] = z;  // absent shift: + 0
+    if (g.ln_gain != nullptr) {
+#pragma unroll
+      for (int c = 0; c < 6; ++c) lng[c] = *reinterpret_cast<const f32x4 *>(g.ln_gain + 64 * c + 4 * lj);
       if (g.ln_shift) {
-        lns[0] = *reinterpret_cast<const f32x4 *>(g.ln_shift + lane * 8);
-        lns[1] = *reinterpret_cast<const f32x4 *>(g.ln_shift + lane * 8 + 4);
+#pragma unroll
+        for (int c = 0; c < 6; ++c) lns[c] = *reinterpret_cast<const f32x4 *>(g.ln_shift + 64 * c + 4 * lj);
       }
     }
   };
   auto ln_finish = [&]() {
     const bool norm = g.ln_gain != nullptr;
 #pragma unroll
-    for (int rr = 0; rr < LR; ++rr) {
-      const int rl = wave * LR + rr;
-      float y[8];
+    for (int p = 0; p < LP; ++p) {
+      const int rl = wave * (BM / 4) + 4 * p + (lane >> 4);
+      f32x4 y[6];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        y[e] = lnx[rr][0][e];
-        y[4 + e] = lnx[rr][1][e];
-      }
+      for (int c = 0; c < 6; ++c) y[c] = lnx[p][c];
       if (norm) {
         float mean, rstd;
-        row8_stats(y, ln_act, mean, rstd);
+        ln_row16(lnx[p], mean, rstd);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (y[e] - mean) * rstd * lng[e >> 2][e & 3] + lns[e >> 2][e & 3];
+        for (int c = 0; c < 6; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[c][e] = (y[c][e] - mean) * rstd * lng[c][e] + lns[c][e];
       }
-      if (ln_act) {
-        Frag<T> f;
-        frag_from(f, y);
-        // (row rl, k = 8 lane): block (rl / 16, lane / 4), lane (rl % 16) + 16 (lane % 4)
-        store_frag(&sAk[((rl >> 4) * KA + (lane >> 2)) * BLK + ((rl & 15) + 16 * (lane & 3)) * FE], f);
+#pragma unroll
+      for (int c = 0; c < 6; ++c) {
+        // (row rl, k = 64 c + 4 lj): block (rl / 16, k / 32), lane (rl % 16) + 16 ((k % 32) / 8), element k % 8
+        const int k = 64 * c + 4 * lj;
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)y[c][e];
+        *reinterpret_cast<bf16x4 *>(&sAk[((rl >> 4) * KA + (k >> 5)) * BLK + ((rl & 15) + 16 * ((k & 31) >> 3)) * FE +
+                                         (k & 7)]) = v;
       }
     }
   };
@@ -863,41 +867,37 @@ __global__ __launch_bounds__(256) void final_ln_type_kernel(const float *x, cons
 }
 
 // out[t] = LayerNorm(x[t]; gain, shift) as the GEMM element type; gain == nullptr
-// copies x unchanged (the first layer's identity pre-norm).  One row per wave,
-// lanes 0..47 holding 8 consecutive columns: the arithmetic of the GEMM's
-// fused LayerNorm (row8_stats), so both give identical operands.
+// copies x unchanged (the first layer's identity pre-norm).  One row per
+// 16-lane row of the wave (lane j: columns 64 c + 4 j .. + 3), with the
+// statistics and arithmetic of the GEMM's fused LayerNorm (ln_row16), so both
+// give identical operands.
 template <typename T>
 __global__ __launch_bounds__(256) void ln_rows_kernel(const float *__restrict__ x, const float *__restrict__ gain,
                                                       const float *__restrict__ shift, int n, T *__restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= n) return;
-  const bool act = lane < kWidth / 8;
-  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (act) {
-    const float *xr = x + (size_t)t * kWidth + lane * 8;
+  const int lj = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (t >= n) return;  // whole 16-lane rows leave together
+  f32x4 y[6];
+  const float *xr = x + (size_t)t * kWidth + 4 * lj;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = xr[e];
-  }
+  for (int c = 0; c < 6; ++c) y[c] = *reinterpret_cast<const f32x4 *>(xr + 64 * c);
   if (gain != nullptr) {
-    float gm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, sh[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (act) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        gm[e] = gain[lane * 8 + e];
-        if (shift) sh[e] = shift[lane * 8 + e];  // absent shift: + 0, as in the GEMM's fused LayerNorm
-      }
-    }
     float mean, rstd;
-    row8_stats(y, act, mean, rstd);
+    ln_row16(y, mean, rstd);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = (y[e] - mean) * rstd * gm[e] + sh[e];
-  }
-  if (act) {
-    T *o = out + (size_t)t * kWidth + lane * 8;
+    for (int c = 0; c < 6; ++c) {
+      const f32x4 gm = *reinterpret_cast<const f32x4 *>(gain + 64 * c + 4 * lj);
+      f32x4 sh = f32x4{0.f, 0.f, 0.f, 0.f};  // absent shift: + 0, as in the GEMM's fused LayerNorm
+      if (shift) sh = *reinterpret_cast<const f32x4 *>(shift + 64 * c + 4 * lj);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = to_elem<T>(y[e]);
+      for (int e = 0; e < 4; ++e) y[c][e] = (y[c][e] - mean) * rstd * gm[e] + sh[e];
+    }
   }
+  T *o = out + (size_t)t * kWidth + 4 * lj;
+#pragma unroll
+  for (int c = 0; c < 6; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[64 * c + e] = to_elem<T>(y[c][e]);
 }
 
 __global__ __launch_bounds__(256) void gather_rows_kernel(const float *__restrict__ src,
@@ -1067,8 +1067,8 @@ hipError_t launch_ln_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStrea
 hipError_t launch_ln_rows(bool bf16_out, const float *x, const float *gain, const float *shift, int n, void *out,
                           hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if (bf16_out) ln_rows_kernel<bf16><<<(n + 3) / 4, 256, 0, s>>>(x, gain, shift, n, (bf16 *)out);
-  else ln_rows_kernel<float><<<(n + 3) / 4, 256, 0, s>>>(x, gain, shift, n, (float *)out);
+  if (bf16_out) ln_rows_kernel<bf16><<<(n + 15) / 16, 256, 0, s>>>(x, gain, shift, n, (bf16 *)out);
+  else ln_rows_kernel<float><<<(n + 15) / 16, 256, 0, s>>>(x, gain, shift, n, (float *)out);
   return hipGetLastError();
 }
 
