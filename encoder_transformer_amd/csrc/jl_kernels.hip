@@ -615,7 +615,7 @@ __device__ inline void store_vt_pair<float>(float *row, int slot, float a, float
 // accumulators start at -m, so a probability is one exp2 of the accumulator,
 // and the row sums l run on the matrix cores as a product with a ones
 // fragment, from the same bf16 probabilities the P.V product uses.
-template <typename T, int NSUB>
+template <typename T, int NSUB, bool kPre3 = false>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // LDS row stride (elements): 80 makes the 16-byte operand reads (16 rows x
   // 4 chunks per 16 lanes) conflict-free on gfx950; 72 measured 2-way.
@@ -661,31 +661,34 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const T *kp0 = kbase + (size_t)(lo + (tid >> 3)) * a.kv_stride;
   const T *vp0 = vbase + (size_t)(lo + 2 * (tid >> 3)) * a.kv_stride;
   const size_t r32 = (size_t)32 * a.kv_stride, r1 = (size_t)a.kv_stride;
-  Frag<T> rk0, rk1, rv0, rv1;
-  auto load_tile = [&](int t) {
+  // a tile's K and V rows of this thread, in register slot r: kPre3 keeps
+  // all (at most 3) tiles of a window item in flight from the start
+  constexpr int NR = kPre3 ? 3 : 1;
+  Frag<T> rk0[NR], rk1[NR], rv0[NR], rv1[NR];
+  auto load_tile = [&](int t, int r) {
     const int base = lo + t * 64;
     if (base + 64 <= w.kv_len) {
       const size_t off = (size_t)(t * 64) * a.kv_stride;
-      rk0 = load_frag(kp0 + off);
-      rk1 = load_frag(kp0 + off + r32);
-      rv0 = load_frag(vp0 + off);
-      rv1 = load_frag(vp0 + off + r1);
-    } else {
+      rk0[r] = load_frag(kp0 + off);
+      rk1[r] = load_frag(kp0 + off + r32);
+      rv0[r] = load_frag(vp0 + off);
+      rv1[r] = load_frag(vp0 + off + r1);
+    } else {  // rows past the sequence end (or past the item's keys) read its last row
       const int k0 = base + (tid >> 3);
       const int v0 = base + 2 * (tid >> 3);
-      rk0 = load_frag(kbase + (size_t)min(k0, last) * a.kv_stride);
-      rk1 = load_frag(kbase + (size_t)min(k0 + 32, last) * a.kv_stride);
-      rv0 = load_frag(vbase + (size_t)min(v0, last) * a.kv_stride);
-      rv1 = load_frag(vbase + (size_t)min(v0 + 1, last) * a.kv_stride);
+      rk0[r] = load_frag(kbase + (size_t)min(k0, last) * a.kv_stride);
+      rk1[r] = load_frag(kbase + (size_t)min(k0 + 32, last) * a.kv_stride);
+      rv0[r] = load_frag(vbase + (size_t)min(v0, last) * a.kv_stride);
+      rv1[r] = load_frag(vbase + (size_t)min(v0 + 1, last) * a.kv_stride);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int r) {
     const int c = (tid & 7) * 8;
-    store_frag(&sK[buf][(tid >> 3) * KS + c], rk0);
-    store_frag(&sK[buf][((tid >> 3) + 32) * KS + c], rk1);
+    store_frag(&sK[buf][(tid >> 3) * KS + c], rk0[r]);
+    store_frag(&sK[buf][((tid >> 3) + 32) * KS + c], rk1[r]);
     const int slot = vt_swz(c, vt_slot(2 * (tid >> 3)));  // rows c .. c+7 share d >> 4
 #pragma unroll
-    for (int e = 0; e < 8; ++e) store_vt_pair<T>(&sV[buf][(c + e) * KS], slot, frag_get(rv0, e), frag_get(rv1, e));
+    for (int e = 0; e < 8; ++e) store_vt_pair<T>(&sV[buf][(c + e) * KS], slot, frag_get(rv0[r], e), frag_get(rv1[r], e));
   };
 
   // per query (lane % 16): the reference maximum m (the accumulators start at
@@ -721,17 +724,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // unconditional preamble: the first tile's stores wait for every earlier
   // load (the q fragments), so no wait for them is left inside the loop,
   // where it would also stall on the next tile's prefetch
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0);
+  if constexpr (kPre3) {  // a window item meets at most 3 tiles; beyond n_tiles the loads are clamped and unused
+    load_tile(1, 1);
+    load_tile(2, 2);
+  }
+  store_tile(0, 0);
   // the q fragments must have arrived before the loop: otherwise the
   // compiler places their wait at its first use inside the loop, where it
   // would also stall every iteration on the next tile's prefetch
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) frag_touch(fq[s][0], fq[s][1]);
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+  // one 64-key tile from LDS buffer cur
+  auto tile_step = [&](int t, int cur) {
     // S^T = K Q^T - m for each query sub-tile
     f32x4 sc[NSUB][4];
 #pragma unroll
@@ -818,8 +824,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int s = 0; s < NSUB; ++s) mfma(o[s][ds], vf, fp[s]);
       }
     }
-    if (t + 1 < n_tiles) store_tile(cur ^ 1);
-    __syncthreads();
+  };
+  if constexpr (kPre3) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      if (t < n_tiles) {
+        tile_step(t, t & 1);
+        if (t + 1 < n_tiles) store_tile((t + 1) & 1, t + 1);
+        __syncthreads();
+      }
+    }
+  } else {
+    for (int t = 0; t < n_tiles; ++t) {
+      const int cur = t & 1;
+      if (t + 1 < n_tiles) load_tile(t + 1, 0);
+      tile_step(t, cur);
+      if (t + 1 < n_tiles) store_tile(cur ^ 1, 0);
+      __syncthreads();
+    }
   }
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
@@ -1076,8 +1098,14 @@ hipError_t launch_attention(bool bf16_mode, const AttnArgs &a, int n_work, int q
   if (n_work <= 0) return hipSuccess;
   const dim3 grid(n_work, kHeads);
   if (queries_per_block == 64) {
-    if (bf16_mode) attn_kernel<bf16, 1><<<grid, 256, 0, s>>>(a);
-    else attn_kernel<float, 1><<<grid, 256, 0, s>>>(a);
+    // a window item (64 queries, +-64 keys) meets at most 3 key tiles: all in flight from the start
+    const bool pre3 = a.half_window >= 0 && a.half_window <= kHalfWindow;
+    if (bf16_mode) {
+      if (pre3) attn_kernel<bf16, 1, true><<<grid, 256, 0, s>>>(a);
+      else attn_kernel<bf16, 1><<<grid, 256, 0, s>>>(a);
+    } else {
+      attn_kernel<float, 1><<<grid, 256, 0, s>>>(a);
+    }
   } else if (queries_per_block == 128) {
     if (bf16_mode) attn_kernel<bf16, 2><<<grid, 256, 0, s>>>(a);
     else attn_kernel<float, 2><<<grid, 256, 0, s>>>(a);
