@@ -73,7 +73,7 @@ def class_flops(batch, row_block):
     return f
 
 
-def time_workload(model, batch, steps, warmup, profile_class=None):
+def time_workload(model, batch, steps, warmup, profile_class=None, sample=True):
     import torch
     from encoder_transformer_amd import lib
     ids = torch.from_numpy(np.ascontiguousarray(batch.ids)).to("cuda:0")
@@ -99,9 +99,12 @@ def time_workload(model, batch, steps, warmup, profile_class=None):
     dominant = max(per_class, key=lambda k: per_class[k][0]) if profile_class is None else profile_class
     cls_id = lib.KERNEL_CLASS_NAMES.index(dominant)
     # timed region: the dominant class's launches are bracketed by events in
-    # every PROFILE_EVERY-th step (a sample of the region; the event records
-    # themselves cost the stream a little time)
-    model.profile(1, 0)
+    # every PROFILE_EVERY-th step (a sample of the region; those steps run
+    # eagerly and the event records themselves cost the stream a little time).
+    # sample=False times plain graph replays only (the latency figures).
+    model.profile(1, 0)  # clears the warm-up records
+    if not sample:
+        model.profile(0, 0)  # profiling off: every step replays its graph
     torch.cuda.synchronize()
     # Python's cyclic garbage collector is paused in the timed region (as
     # timeit does): a full collection of this interpreter's heap stalls the
@@ -112,7 +115,8 @@ def time_workload(model, batch, steps, warmup, profile_class=None):
     try:
         t0 = time.perf_counter()
         for i in range(steps):
-            model.profile(2 if i % PROFILE_EVERY == 0 else 0, 1 << cls_id)
+            if sample:
+                model.profile(2 if i % PROFILE_EVERY == 0 else 0, 1 << cls_id)
             step()
         torch.cuda.synchronize()
         t = time.perf_counter() - t0
@@ -120,7 +124,7 @@ def time_workload(model, batch, steps, warmup, profile_class=None):
         gc.enable()
     dom_ms, dom_n = model.profile_read(cls_id)
     model.profile(0, 0)
-    sampled = (steps + PROFILE_EVERY - 1) // PROFILE_EVERY
+    sampled = (steps + PROFILE_EVERY - 1) // PROFILE_EVERY if sample else 0
     return t, dominant, dom_ms, dom_n, per_class, sampled
 
 
@@ -224,11 +228,11 @@ def main():
     if not args.no_extra:
         extra = {}
         b1 = synth.make_batch(1)
-        t1, *_ = time_workload(model, b1, max(args.steps, 20), args.warmup)
+        t1, *_ = time_workload(model, b1, max(args.steps, 20), args.warmup, sample=False)
         extra["1x1024_ms_per_call"] = round(1e3 * t1 / max(args.steps, 20), 4)
         for name, cfg, st in [("16x8192", 3, 5), ("ragged256", 4, 5)]:
             b = synth.make_batch(cfg)
-            tt, d, dms, dn, _, _ = time_workload(model, b, st, 2)
+            tt, d, dms, dn, _, _ = time_workload(model, b, st, 2, sample=False)
             fl = sum(class_flops(b, row_block=b.n_tokens >= ROW_BLOCK_MIN_TOKENS).values())
             extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2),
                            "tokens_per_s": round(b.n_tokens * st / tt, 1),
