@@ -78,6 +78,11 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ 
 // tiles: all N-tiles of an M-block then share one XCD's L2.
 // ---------------------------------------------------------------------------
 
+// The shift of a LayerNorm that has none, for the GEMM's fused LayerNorm:
+// adding + 0 from memory keeps the loads and the arithmetic free of branches
+// and selects (and equals the LayerNorm kernel's + 0).
+__device__ float g_ln_zero_shift[kWidth];
+
 template <typename T> struct GemmBK;
 template <> struct GemmBK<bf16> { static constexpr int v = 64; };
 template <> struct GemmBK<float> { static constexpr int v = 32; };
@@ -86,12 +91,23 @@ template <> struct GemmBK<float> { static constexpr int v = 32; };
 // operations (vmcnt in bits 3:0 and 15:14) and leaves the other counters free.
 constexpr int vm_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
+// 16 bytes per lane from rows at `base` (lane byte offset voff, scalar byte
+// offset soff) straight into LDS: lane i lands at dst + 16 i.  A device
+// function of its own: the GEMM's lambdas are also compiled for the host,
+// which has no buffer resources.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ inline void buffer_load_lds16(const void *base, lds_void *dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000), dst, 16, voff,
+      soff, 0, 0);
+}
+
 __device__ inline int xcd_tile(int b, int n_tiles) {
   const int per = n_tiles >> 3, rem = n_tiles & 7, x = b & 7, local = b >> 3;
   return x * per + min(x, rem) + local;
 }
 
-template <typename T, int BM, int BN, int EM, int NSTAGE, bool LNA = false, int KFIX = 0>
+template <typename T, int BM, int BN, int EM, int NSTAGE, bool LNA = false, int KFIX = 0, bool RF = false>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int n_tiles) {
   constexpr int BK = GemmBK<T>::v, KS = BK / 32;           // 32-wide k sub-steps per stage
   constexpr int TM = BM / 2, TN = BN / 2;                   // wave tile
@@ -120,9 +136,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   //
   // LNA (bf16, BM = 64, K = 384): A = LayerNorm(g.ln_x) rows, normalized by
   // the work-group itself into an LDS tile that holds all of K; only W
-  // streams through the stages.  All 6 weight stages are issued first, then
-  // the rows: one memory round trip brings both, and once the rows are in,
-  // every stage has landed.
+  // streams through the stages.  The rows and the LayerNorm parameters are
+  // loaded first and normalized while the weight stages stream in (RF); an
+  // identity pre-norm (no gain) issues the stages first, then the rows, and
+  // once the rows are in every stage has landed.
   constexpr bool kDma = std::is_same<T, bf16>::value;
   constexpr int NS = kDma ? NSTAGE : 2;
   static_assert(NS >= 2 && NS <= 6, "stages");
@@ -170,15 +187,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     for (int i = 0; i < B_PER_WAVE; ++i) store_frag(&sB[buf][(wave * B_PER_WAVE + i) * BLK + lane * FE], rb[i]);
   };
 
-  f32x4 acc[MT][NT];
+  f32x4 acc[MT][NT];  // zeroed just before the K loop: no registers held through the prologue
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
 
   constexpr int KC = LNA ? kWidth : KFIX;  // K when fixed at compile time
+  // RF (a fused LayerNorm with a gain): the rows are loaded first and
+  // normalized while the weight stages stream in.  Without RF (the identity
+  // pre-norm of the first layer) every weight stage goes first and lands with
+  // the rows (kAllIn below).
+  constexpr bool kRowsFirst = LNA && RF;
+  static_assert(!RF || LNA, "rows first: fused LayerNorm only");
   static_assert(KC % BK == 0, "K steps");
   const int KT = KC ? KC / BK : g.K / BK;
+  constexpr bool kAllIn = LNA && !kRowsFirst && NSTAGE * BK >= kWidth;
+  // rows first with every stage issued up front: the RoPE table rows, which
+  // need the positions, are read right after the LayerNorm, and the stage
+  // waits count them (younger than every stage)
+  constexpr bool kRopeEarly = kRowsFirst && EM == E_STORE && NSTAGE * BK >= kWidth;
   // fused LayerNorm: each wave normalizes 16 rows, 4 at a time, one per
   // 16-lane row of the wave (lane j: columns 64 c + 4 j .. + 3, c = 0..5),
   // with all their loads in flight; the gain and shift columns of a lane are
@@ -197,19 +227,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 #pragma unroll
       for (int c = 0; c < 6; ++c) lnx[p][c] = *reinterpret_cast<const f32x4 *>(xr + 64 * c);
     }
+    if constexpr (kRowsFirst) {
+      // always normalized (the launcher checks the gain); an absent shift is
+      // read as zeros: loads under no branch, so no merge copies and no
+      // early waits
+      const float *sh = g.ln_shift ? g.ln_shift : g_ln_zero_shift;
 #pragma unroll
-    for (int c = 0; c < 6; ++c) lng[c] = lns[c] = z;  // absent shift: + 0
-    if (g.ln_gain != nullptr) {
+      for (int c = 0; c < 6; ++c) {
+        lng[c] = *reinterpret_cast<const f32x4 *>(g.ln_gain + 64 * c + 4 * lj);
+        lns[c] = *reinterpret_cast<const f32x4 *>(sh + 64 * c + 4 * lj);
+      }
+    } else {
 #pragma unroll
-      for (int c = 0; c < 6; ++c) lng[c] = *reinterpret_cast<const f32x4 *>(g.ln_gain + 64 * c + 4 * lj);
-      if (g.ln_shift) {
+      for (int c = 0; c < 6; ++c) lng[c] = lns[c] = z;  // absent shift: + 0
+      if (g.ln_gain != nullptr) {
 #pragma unroll
-        for (int c = 0; c < 6; ++c) lns[c] = *reinterpret_cast<const f32x4 *>(g.ln_shift + 64 * c + 4 * lj);
+        for (int c = 0; c < 6; ++c) lng[c] = *reinterpret_cast<const f32x4 *>(g.ln_gain + 64 * c + 4 * lj);
+        if (g.ln_shift) {
+#pragma unroll
+          for (int c = 0; c < 6; ++c) lns[c] = *reinterpret_cast<const f32x4 *>(g.ln_shift + 64 * c + 4 * lj);
+        }
       }
     }
   };
   auto ln_finish = [&]() {
-    const bool norm = g.ln_gain != nullptr;
+    const bool norm = kRowsFirst || g.ln_gain != nullptr;
 #pragma unroll
     for (int p = 0; p < LP; ++p) {
       const int rl = wave * (BM / 4) + 4 * p + (lane >> 4);
@@ -232,8 +274,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (bf16)y[c][e];
-        *reinterpret_cast<bf16x4 *>(&sAk[((rl >> 4) * KA + (k >> 5)) * BLK + ((rl & 15) + 16 * ((k & 31) >> 3)) * FE +
-                                         (k & 7)]) = v;
+        T *dst = &sAk[((rl >> 4) * KA + (k >> 5)) * BLK + ((rl & 15) + 16 * ((k & 31) >> 3)) * FE + (k & 7)];
+        if constexpr (kRowsFirst) {
+          // the weight stages' LDS-direct loads are still in flight, into
+          // other LDS buffers; a plain store would make the compiler wait
+          // for all of them.  The lgkmcnt(0) before the first barrier of the
+          // K loop completes these stores.
+          typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+          const unsigned a3 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) T *)dst;
+          asm volatile("ds_write_b64 %0, %1" ::"v"(a3), "v"(__builtin_bit_cast(u32x2, v)));
+        } else {
+          *reinterpret_cast<bf16x4 *>(dst) = v;
+        }
       }
     }
   };
@@ -244,29 +296,35 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   // Epilogue operands that do not depend on the product (bias, RoPE table
   // rows, the residual) are all read before the first store: a load that
   // follows a store to C may alias it, and the compiler would then wait for
-  // every earlier memory operation at each row.  A 64-row tile (kHoist)
-  // reads them before the K loop (the table rows, which need the positions,
-  // after the fused LayerNorm or else at the epilogue), larger tiles one
-  // 16-row group at a time.
-  constexpr bool kHoist = kDma && BM == 64;
+  // every earlier memory operation at each row.  A tile of at most 64 rows
+  // (kHoist) reads them before the K loop (the table rows, which need the
+  // positions, after the fused LayerNorm or else at the epilogue), larger
+  // tiles one 16-row group at a time.
+  constexpr bool kHoist = kDma && BM <= 64;
   constexpr int HG = kHoist ? MT : 1;  // row groups held at once
   const bool has_bias = g.bias != nullptr;
   const bool rope = EM == E_STORE && g.rope_cos != nullptr;
+  // the RoPE reads take no branch (a load under a branch makes the compiler
+  // wait for it at the merge, before the weight stages are even issued):
+  // without a table they read zeros at position 0
+  const int *pos_p = rope ? g.pos : (const int *)g_ln_zero_shift;
+  const int pos_step = rope ? 1 : 0;
+  const float *cos_p = rope ? g.rope_cos : g_ln_zero_shift, *sin_p = rope ? g.rope_sin : g_ln_zero_shift;
   float bias_v[NT];
   int rpos[HG][4];
   float rcs[HG][4][4];  // per row: cos and sin of d = lr, then of d = 16 + lr
   float res[EM == E_RESID ? HG : 1][4][EM == E_RESID ? NT : 1];
+  // unconditional loads (without a bias they read the output row, and the
+  // epilogue adds nothing): a load under a branch would need a copy at the
+  // merge, and the copy an early wait
   auto load_bias = [&]() {
+    const float *b = has_bias ? g.bias : (const float *)g.C;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) bias_v[j] = 0.f;
-    if (has_bias) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) bias_v[j] = g.bias[col0 + j * 16];
-    }
+    for (int j = 0; j < NT; ++j) bias_v[j] = b[col0 + j * 16];
   };
   auto load_pos = [&](int i, int h) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rpos[h][r] = g.pos[min(row0 + i * 16 + r, M - 1)];
+    for (int r = 0; r < 4; ++r) rpos[h][r] = pos_p[min(row0 + i * 16 + r, M - 1) * pos_step];
   };
   auto load_rope = [&](int h) {
 #pragma unroll
@@ -274,8 +332,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int q = rpos[h][r] * 32 + j * 16 + lr;
-        rcs[h][r][2 * j] = g.rope_cos[q];
-        rcs[h][r][2 * j + 1] = g.rope_sin[q];
+        rcs[h][r][2 * j] = cos_p[q];
+        rcs[h][r][2 * j + 1] = sin_p[q];
       }
   };
   auto load_res = [&](int i, int h) {
@@ -293,7 +351,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         if constexpr (EM == E_RESID) load_res(i, i);
-        if (rope) load_pos(i, i);
+        if constexpr (EM == E_STORE) load_pos(i, i);
       }
     }
   };
@@ -317,7 +375,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     }
   };
   if constexpr (kDma) {
-    typedef __attribute__((address_space(3))) void lds_void;
     constexpr int LPS = (LNA ? 0 : A_PER_WAVE) + B_PER_WAVE;  // loads per stage and wave
     auto bufA = [&](auto Bc) -> T * {
       constexpr int B = decltype(Bc)::value;
@@ -344,34 +401,53 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     using I4 = std::integral_constant<int, 4>;
     using I5 = std::integral_constant<int, 5>;
     // stage kt -> LDS buffer pair (dA, dB), one 1 KB fragment block per load
+    // Buffer loads into LDS: a lane's byte offset inside the tile's rows is
+    // fixed for all K-steps (one VGPR per fragment block), the K-step's
+    // offset is a scalar, so the stages need no per-load address registers
+    // (reusing one while its load is in flight would make the compiler wait
+    // for that load).  Offsets count from the tile's first row.
+    int voA[LNA ? 1 : A_PER_WAVE], voB[B_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < (LNA ? 0 : A_PER_WAVE); ++i) {
+      const int q = wave * A_PER_WAVE + i;
+      const int row = min(m0 + (q / KS) * 16 + lr, M - 1) - m0;
+      voA[i] = (row * g.lda + lc + (q % KS) * 32) * (int)sizeof(T);
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+      const int q = wave * B_PER_WAVE + i;
+      voB[i] = (((q / KS) * 16 + lr) * g.ldw + lc + (q % KS) * 32) * (int)sizeof(T);
+    }
+    const T *tileA = Ab + (size_t)(LNA ? 0 : m0) * g.lda, *tileB = Wb + (size_t)n0 * g.ldw;
     auto issue_stage = [&](int kt, T *dA, T *dB) {
-      const int k0 = kt * BK + lc;
+      const int so = kt * BK * (int)sizeof(T);
 #pragma unroll
       for (int i = 0; i < (LNA ? 0 : A_PER_WAVE); ++i) {
         const int q = wave * A_PER_WAVE + i;
-        const int row = min(m0 + (q / KS) * 16 + lr, M - 1);
-        __builtin_amdgcn_global_load_lds((const void *)(Ab + (size_t)row * g.lda + k0 + (q % KS) * 32),
-                                         (lds_void *)&dA[q * BLK], 16, 0, 0);
+        buffer_load_lds16(tileA, (lds_void *)&dA[q * BLK], voA[i], so);
       }
 #pragma unroll
       for (int i = 0; i < B_PER_WAVE; ++i) {
         const int q = wave * B_PER_WAVE + i;
-        __builtin_amdgcn_global_load_lds((const void *)(Wb + (size_t)(n0 + (q / KS) * 16 + lr) * g.ldw + k0 + (q % KS) * 32),
-                                         (lds_void *)&dB[q * BLK], 16, 0, 0);
+        buffer_load_lds16(tileB, (lds_void *)&dB[q * BLK], voB[i], so);
       }
     };
     // wait until at most `later` stages younger than the current one are in
-    // flight (the immediate must be a constant)
-    auto wait_stages = [&](int later) {
+    // flight, besides the R loads issued after the last stage (the
+    // immediate must be a constant)
+    auto wait_n = [&](auto Rc, int later) {
+      constexpr int R = decltype(Rc)::value;
       switch (later) {
-        case 0: __builtin_amdgcn_s_waitcnt(vm_wait_imm(0)); break;
-        case 1: __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPS)); break;
-        case 2: __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * LPS)); break;
-        case 3: __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * LPS)); break;
-        case 4: __builtin_amdgcn_s_waitcnt(vm_wait_imm(4 * LPS)); break;
-        default: __builtin_amdgcn_s_waitcnt(vm_wait_imm(5 * LPS)); break;
+        case 0: __builtin_amdgcn_s_waitcnt(vm_wait_imm(R)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPS + R)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * LPS + R)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * LPS + R)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(vm_wait_imm(4 * LPS + R)); break;
+        default: __builtin_amdgcn_s_waitcnt(vm_wait_imm(5 * LPS + R)); break;
       }
     };
+    constexpr int kRopeLoads = MT * 16;  // table reads per lane: 4 rows x 2 halves x (cos, sin)
+    auto wait_stages = [&](int later) { wait_n(std::integral_constant<int, kRopeEarly ? kRopeLoads : 0>(), later); };
     // K-step kt from buffer B (= kt % NS): wait for this wave's loads of the
     // step, then a bare barrier: every wave's loads of the step have landed
     // and every wave is done reading the previous step's buffer, which step
@@ -379,7 +455,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     // up-front stages (kt = 0), else those issued by steps 1 .. kt - 1.
     // With every stage in before the LayerNorm (kAllIn), one barrier after
     // the A tile's LDS stores is all the loop needs.
-    constexpr bool kAllIn = LNA && NS * BK >= kWidth;
     auto step = [&](int kt, auto Bc) {
       constexpr int B = decltype(Bc)::value;
       if constexpr (kAllIn) {
@@ -397,8 +472,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
       }
       compute(bufA(Bc), bufB(Bc), kt);
     };
-    // loads older than every stage never hold up a stage wait
-    if constexpr (!LNA) load_hoisted();
+    // loads older than every stage never hold up a stage wait (the
+    // scheduling barrier keeps the scheduler from sinking them towards their
+    // use, behind the stages)
+    if constexpr (kRowsFirst) {
+      ln_load();
+      load_hoisted();
+    } else if constexpr (!LNA) {
+      load_hoisted();
+    }
+    __builtin_amdgcn_sched_barrier(0);
     issue_stage(0, sA0, sB0);
     if (KT > 1) issue_stage(1, sA1, sB1);
     if constexpr (NS > 2)
@@ -410,16 +493,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     if constexpr (NS > 5)
       if (KT > 5) issue_stage(5, bufA(I5()), bufB(I5()));
     if constexpr (LNA) {
-      ln_load();
-      load_hoisted();
-      ln_finish();  // waits for the rows, younger than every stage: all stages have landed
-      if constexpr (kAllIn) {
-        if (rope) {
+      if constexpr (!kRowsFirst) {
+        ln_load();
+        load_hoisted();
+      }
+      // keep the stage loads ahead of the LayerNorm arithmetic: the scheduler
+      // would otherwise sink them below it, and the weights would only be
+      // requested once the LayerNorm is done
+      __builtin_amdgcn_sched_barrier(0);
+      ln_finish();  // weights first: waits for the rows, younger than every stage
+      if constexpr (EM == E_STORE && (kAllIn || kRopeEarly)) {
+        // rows first: counted by the stage waits (every stage was issued
+        // before); weights first: every stage has landed
 #pragma unroll
-          for (int i = 0; i < MT; ++i) load_rope(i);
-        }
+        for (int i = 0; i < MT; ++i) load_rope(i);
       }
     }
+    zero_acc();
     auto round = [&](int kt) {  // steps kt .. kt + NS - 1
       step(kt, I0());
       if (kt + 1 < KT) step(kt + 1, I1());
@@ -439,6 +529,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
       for (int kt = 0; kt < KT; kt += NS) round(kt);
     }
   } else {
+    zero_acc();
     load_bias();
     load_stage(0);
     store_stage(0);
@@ -453,18 +544,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   }
 
   // epilogue, one 16-row group at a time
-  if constexpr (kHoist && !(LNA && NS * BK >= kWidth)) {
-    if (rope) {
+  if constexpr (EM == E_STORE && kHoist && !kAllIn && !kRopeEarly) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i) load_rope(i);
-    }
+    for (int i = 0; i < MT; ++i) load_rope(i);
   }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int h = kHoist ? i : 0;
     if constexpr (!kHoist) {
       if constexpr (EM == E_RESID) load_res(i, 0);
-      if (rope) {
+      if constexpr (EM == E_STORE) {
         load_pos(i, 0);
         load_rope(0);
       }
@@ -994,26 +1083,29 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BN, int NS, bool LNA = false, int KFIX = 0>
+template <typename T, int BM, int BN, int NS, bool LNA = false, int KFIX = 0, bool RF = false>
 static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
   const int tiles_n = a.N / BN, n_tiles = ((a.M + BM - 1) / BM) * tiles_n;
   constexpr bool pairs = (BN / 32) % 4 == 0;  // 64-column groups per wave: GEGLU and RoPE epilogues
   switch (emode) {
     case E_STORE:
       if constexpr (!pairs) return hipErrorInvalidValue;
-      else gemm_kernel<T, BM, BN, E_STORE, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      else gemm_kernel<T, BM, BN, E_STORE, NS, LNA, KFIX, RF><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     case E_GEGLU:
-      if constexpr (!pairs) return hipErrorInvalidValue;
-      else gemm_kernel<T, BM, BN, E_GEGLU, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      if constexpr (!pairs || (LNA && !RF)) return hipErrorInvalidValue;
+      else gemm_kernel<T, BM, BN, E_GEGLU, NS, LNA, KFIX, RF><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
-    case E_RELU: gemm_kernel<T, BM, BN, E_RELU, NS, LNA, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles); break;
+    case E_RELU:
+      if constexpr (LNA && !RF) return hipErrorInvalidValue;
+      else gemm_kernel<T, BM, BN, E_RELU, NS, LNA, KFIX, RF><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      break;
     case E_RESID:
-      if constexpr (LNA) return hipErrorInvalidValue;
+      if constexpr (LNA || RF) return hipErrorInvalidValue;
       else gemm_kernel<T, BM, BN, E_RESID, NS, false, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     case E_GELU_F32:
-      if constexpr (LNA || KFIX != 0) return hipErrorInvalidValue;
+      if constexpr (LNA || RF || KFIX != 0) return hipErrorInvalidValue;
       else gemm_kernel<T, BM, BN, E_GELU_F32, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     default: return hipErrorInvalidValue;
@@ -1072,14 +1164,21 @@ hipError_t launch_ln_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStrea
   if (a.N % 128 != 0 || a.K != kWidth || !a.ln_x) return hipErrorInvalidValue;
   const long nt = a.N / 128, tiles64 = ((a.M + 63) / 64) * nt;
   // the GEMM alone would take 64-row tiles: normalize inside it
-  if (bf16_mode && (emode == E_STORE || emode == E_GEGLU || emode == E_RELU) &&
+  // (the GEGLU and ReLU products normalize unconditionally inside: they need a gain)
+  if (bf16_mode && (emode == E_STORE || ((emode == E_GEGLU || emode == E_RELU) && a.ln_gain != nullptr)) &&
       ((a.M + 127) / 128) * nt < 256) {
     // one round of work-groups (1 per CU: 144 KB of LDS): 6 stages of a
     // 128-column tile, or 3 of a 256-column tile when 128 would need two
-    if (tiles64 <= 256) return gemm_dispatch<bf16, 64, 128, 6, true>(emode, a, s);
+    // with a gain the rows are loaded (and normalized) ahead of the weights
+    const bool rf = a.ln_gain != nullptr;
+    if (tiles64 <= 256)
+      return rf ? gemm_dispatch<bf16, 64, 128, 6, true, 0, true>(emode, a, s)
+                : gemm_dispatch<bf16, 64, 128, 6, true>(emode, a, s);
     if (a.N % 256 == 0 && ((a.M + 63) / 64) * (a.N / 256) <= 256)
-      return gemm_dispatch<bf16, 64, 256, 3, true>(emode, a, s);
-    return gemm_dispatch<bf16, 64, 128, 2, true>(emode, a, s);
+      return rf ? gemm_dispatch<bf16, 64, 256, 3, true, 0, true>(emode, a, s)
+                : gemm_dispatch<bf16, 64, 256, 3, true>(emode, a, s);
+    return rf ? gemm_dispatch<bf16, 64, 128, 2, true, 0, true>(emode, a, s)
+              : gemm_dispatch<bf16, 64, 128, 2, true>(emode, a, s);
   }
   hipError_t e = launch_ln_rows(bf16_mode, a.ln_x, a.ln_gain, a.ln_shift, a.M, const_cast<void *>(a.A), s);
   if (e != hipSuccess) return e;
