@@ -704,8 +704,17 @@ __device__ inline void store_vt_pair<float>(float *row, int slot, float a, float
 // accumulators start at -m, so a probability is one exp2 of the accumulator,
 // and the row sums l run on the matrix cores as a product with a ones
 // fragment, from the same bf16 probabilities the P.V product uses.
-template <typename T, int NSUB, bool kPre3 = false>
+//
+// PF: key tiles in flight (register slots) on the rolling path, for grids of
+// about one work-group per CU or less, where the registers cost no
+// occupancy.  The marker rows' attention over a long sequence (8,192 keys)
+// gains from it; a 1,024-key item at batch 1 does not, its one wave per SIMD
+// being bound by the chain of each tile's own arithmetic.  The per-query
+// arithmetic is the same for every PF and item size, so results do not
+// depend on the batch.
+template <typename T, int NSUB, bool kPre3 = false, int PF = 1>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+  static_assert(PF >= 1 && (!kPre3 || PF == 1), "prefetch depth");
   // LDS row stride (elements): 80 makes the 16-byte operand reads (16 rows x
   // 4 chunks per 16 lanes) conflict-free on gfx950; 72 measured 2-way.
   constexpr int KS = 80;
@@ -751,25 +760,34 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const T *vp0 = vbase + (size_t)(lo + 2 * (tid >> 3)) * a.kv_stride;
   const size_t r32 = (size_t)32 * a.kv_stride, r1 = (size_t)a.kv_stride;
   // a tile's K and V rows of this thread, in register slot r: kPre3 keeps
-  // all (at most 3) tiles of a window item in flight from the start
-  constexpr int NR = kPre3 ? 3 : 1;
+  // all (at most 3) tiles of a window item in flight from the start, the
+  // rolling path PF tiles (tile t in slot t % PF)
+  constexpr int NR = kPre3 ? 3 : PF;
   Frag<T> rk0[NR], rk1[NR], rv0[NR], rv1[NR];
+  // Only the addresses depend on the branch, the loads take none: a load
+  // under a branch leaves its register to be merged at the join, and the
+  // compiler waits for the load there, not where the data is first used.
   auto load_tile = [&](int t, int r) {
     const int base = lo + t * 64;
+    const T *pk0, *pk1, *pv0, *pv1;
     if (base + 64 <= w.kv_len) {
       const size_t off = (size_t)(t * 64) * a.kv_stride;
-      rk0[r] = load_frag(kp0 + off);
-      rk1[r] = load_frag(kp0 + off + r32);
-      rv0[r] = load_frag(vp0 + off);
-      rv1[r] = load_frag(vp0 + off + r1);
+      pk0 = kp0 + off;
+      pk1 = kp0 + off + r32;
+      pv0 = vp0 + off;
+      pv1 = vp0 + off + r1;
     } else {  // rows past the sequence end (or past the item's keys) read its last row
       const int k0 = base + (tid >> 3);
       const int v0 = base + 2 * (tid >> 3);
-      rk0[r] = load_frag(kbase + (size_t)min(k0, last) * a.kv_stride);
-      rk1[r] = load_frag(kbase + (size_t)min(k0 + 32, last) * a.kv_stride);
-      rv0[r] = load_frag(vbase + (size_t)min(v0, last) * a.kv_stride);
-      rv1[r] = load_frag(vbase + (size_t)min(v0 + 1, last) * a.kv_stride);
+      pk0 = kbase + (size_t)min(k0, last) * a.kv_stride;
+      pk1 = kbase + (size_t)min(k0 + 32, last) * a.kv_stride;
+      pv0 = vbase + (size_t)min(v0, last) * a.kv_stride;
+      pv1 = vbase + (size_t)min(v0 + 1, last) * a.kv_stride;
     }
+    rk0[r] = load_frag(pk0);
+    rk1[r] = load_frag(pk1);
+    rv0[r] = load_frag(pv0);
+    rv1[r] = load_frag(pv1);
   };
   auto store_tile = [&](int buf, int r) {
     const int c = (tid & 7) * 8;
@@ -817,6 +835,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   if constexpr (kPre3) {  // a window item meets at most 3 tiles; beyond n_tiles the loads are clamped and unused
     load_tile(1, 1);
     load_tile(2, 2);
+  } else {
+#pragma unroll
+    for (int r = 1; r < PF; ++r) load_tile(r, r);  // likewise clamped past the last tile
   }
   store_tile(0, 0);
   // the q fragments must have arrived before the loop: otherwise the
@@ -924,12 +945,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
     }
   } else {
-    for (int t = 0; t < n_tiles; ++t) {
-      const int cur = t & 1;
-      if (t + 1 < n_tiles) load_tile(t + 1, 0);
-      tile_step(t, cur);
-      if (t + 1 < n_tiles) store_tile(cur ^ 1, 0);
-      __syncthreads();
+    // slot t % PF: tile t reached LDS at the end of step t - 1 (or before the
+    // loop), so step t refills the slot with tile t + PF (past the last tile:
+    // clamped rows, never stored)
+    for (int t0 = 0; t0 < n_tiles; t0 += PF) {
+#pragma unroll
+      for (int r = 0; r < PF; ++r) {
+        const int t = t0 + r;
+        if (t < n_tiles) {
+          load_tile(t + PF, r);
+          tile_step(t, t & 1);
+          if (t + 1 < n_tiles) store_tile((t + 1) & 1, (r + 1) % PF);
+          __syncthreads();
+        }
+      }
     }
   }
 #pragma unroll
@@ -1197,11 +1226,14 @@ hipError_t launch_attention(bool bf16_mode, const AttnArgs &a, int n_work, int q
   if (n_work <= 0) return hipSuccess;
   const dim3 grid(n_work, kHeads);
   if (queries_per_block == 64) {
-    // a window item (64 queries, +-64 keys) meets at most 3 key tiles: all in flight from the start
+    // a window item (64 queries, +-64 keys) meets at most 3 key tiles: all in
+    // flight from the start.  Whole-sequence 64-query items run on grids of at
+    // most about one work-group per CU (small batches, marker rows): 3 tiles
+    // in flight.
     const bool pre3 = a.half_window >= 0 && a.half_window <= kHalfWindow;
     if (bf16_mode) {
       if (pre3) attn_kernel<bf16, 1, true><<<grid, 256, 0, s>>>(a);
-      else attn_kernel<bf16, 1><<<grid, 256, 0, s>>>(a);
+      else attn_kernel<bf16, 1, false, 3><<<grid, 256, 0, s>>>(a);
     } else {
       attn_kernel<float, 1><<<grid, 256, 0, s>>>(a);
     }
