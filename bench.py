@@ -239,6 +239,16 @@ def main():
                            "step_mfma_frac": round(fl / (tt / st) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "dominant_kernel": d}
         extra["ragged256_serve"] = serve_timing(model, synth.make_batch(4))
+        # FP32 mode (FP32 products and attention), for context against the
+        # FP32 matrix-core peak; the headline is bf16
+        m32 = lib.Model(path, lib.FP32, max_tokens=20_000, max_markers=1024, device=0)
+        m32.set_graph_cache(2)
+        for name, b, st in [("16x1024_fp32", b2, 5), ("1x1024_fp32", b1, 10)]:
+            tt, *_ = time_workload(m32, b, st, 2, sample=False)
+            fl = sum(class_flops(b, row_block=False).values())
+            extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2),
+                           "fp32_peak_frac": round(fl / (tt / st) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+        m32.close()
         result["extra"] = extra
     result["ms_per_call_1x1024"] = result.get("extra", {}).get("1x1024_ms_per_call")
     model.close()
