@@ -142,8 +142,6 @@ def test_logits_small_configs(models, oracle_weights, config, prec):
 @pytest.mark.parametrize("config", [2, 3, 4])
 @pytest.mark.parametrize("prec", ["bf16", "fp32"])
 def test_logits_golden_full_batches(models, config, prec):
-    if prec == "fp32" and config != 2:
-        pytest.skip("FP32 mode is checked at full size on the 16x1024 batch")
     batch, seqs, ref_logits = golden_for(config)
     got = run_logits(models[prec], batch)
     assert got.shape == (batch.n_markers,) and np.all(np.isfinite(got))
