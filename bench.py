@@ -6,8 +6,9 @@ One step = jl_forward + jl_probs over one packed batch already resident in
 HBM (weights loaded, token ids on the device). The headline workload is the
 throughput case: 16 sequences of 1,024 tokens, question types cycling
 choice/score/noul, 2-20 options of 1-48 tokens, bf16. Extra fields report
-the batch-1 latency case (1 x 1,024), the long-context case (16 x 8,192) and
-the ragged serving mix (256 sequences of 64-2,048 tokens).
+the batch-1 latency case (1 x 1,024: mean, per-call percentiles, and host ids
+to host logits), the long-context case (16 x 8,192), the ragged serving mix
+(256 sequences of 64-2,048 tokens) and FP32 mode.
 
 `roofline` covers the kernel class with the most device time in the timed
 region, measured with HIP events bracketing each of its launches on the
@@ -155,6 +156,53 @@ def serve_timing(model, batch, handles=2, budget=32768, reps=5):
             "handles": handles, "max_batch_tokens": budget, "host_to_host": True}
 
 
+def call_distribution(model, batch, calls=200):
+    """Per-call figures at batch 1. Each call (graph replay) is bracketed by
+    HIP events on its stream, which cost the stream a few microseconds; the
+    end-to-end figure runs host ids to host logits (pinned copies on the same
+    stream, then a synchronize), host-side validation included."""
+    import torch
+    so, mp, qt = batch.seq_offsets, batch.mask_positions, batch.qtype
+    ids_h = torch.from_numpy(np.ascontiguousarray(batch.ids)).pin_memory()
+    ids = ids_h.to("cuda:0")
+    logits = torch.empty(batch.n_markers, dtype=torch.float32, device="cuda:0")
+    logits_h = torch.empty(batch.n_markers, dtype=torch.float32).pin_memory()
+    stream = torch.cuda.Stream()
+
+    def call():
+        with torch.cuda.stream(stream):
+            model.forward(ids, so, mp, qt, out=logits)
+            model.probs(logits, so, mp, qt)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    gc.collect()
+    gc.disable()
+    try:
+        for e0, e1 in ev:
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        per = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            with torch.cuda.stream(stream):
+                ids.copy_(ids_h, non_blocking=True)
+                model.forward(ids, so, mp, qt, out=logits)
+                model.probs(logits, so, mp, qt)
+                logits_h.copy_(logits, non_blocking=True)
+            stream.synchronize()
+        e2e = (time.perf_counter() - t0) / calls
+    finally:
+        gc.enable()
+    p10, p50, p90 = np.percentile(per, [10, 50, 90])
+    return {"calls": calls, "event_ms_p10": round(float(p10), 4), "event_ms_p50": round(float(p50), 4),
+            "event_ms_p90": round(float(p90), 4), "host_to_host_ms_per_call": round(1e3 * e2e, 4)}
+
+
 def cpu_baseline():
     """The oracle on six 1,024-token sequences of the throughput batch."""
     from threadpoolctl import threadpool_info
@@ -230,6 +278,7 @@ def main():
         b1 = synth.make_batch(1)
         t1, *_ = time_workload(model, b1, max(args.steps, 20), args.warmup, sample=False)
         extra["1x1024_ms_per_call"] = round(1e3 * t1 / max(args.steps, 20), 4)
+        extra["1x1024_calls"] = call_distribution(model, b1)
         for name, cfg, st in [("16x8192", 3, 5), ("ragged256", 4, 5)]:
             b = synth.make_batch(cfg)
             tt, d, dms, dn, _, _ = time_workload(model, b, st, 2, sample=False)
