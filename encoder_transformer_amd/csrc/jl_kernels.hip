@@ -126,7 +126,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   // in flight; with NSTAGE >= K / BK (6 stages for K = 384, for grids that fit
   // the CUs in one or two rounds) the whole K arrives in one memory round
   // trip.  2 stages for larger grids leave LDS for more resident work-groups.
-  // FP32: two LDS stages filled through registers.
+  // FP32: two LDS stages filled through registers, NSTAGE - 1 K-steps in
+  // flight (register slot kt % (NSTAGE - 1)); one-round grids take 4, so that
+  // a K = 384 product pays 3 memory round trips instead of 12.
   // Each bf16 stage buffer is a variable of its own and the K loop is
   // unrolled over the stages: the compiler then knows which buffer each
   // in-flight LDS load writes and adds no wait of its own before reading
@@ -165,26 +167,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 
   // fragment block q of a tile: row group q / KS, k sub-step q % KS
   const T *Ab = (const T *)g.A, *Wb = (const T *)g.W;
-  Frag<T> ra[A_PER_WAVE], rb[B_PER_WAVE];
-  auto load_stage = [&](int kt) {
-    const int k0 = kt * BK + lc;
+  constexpr int PD = kDma ? 1 : NSTAGE - 1;  // FP32: K-steps in flight through registers
+  Frag<T> ra[PD][A_PER_WAVE], rb[PD][B_PER_WAVE];
+  // K-step kt (clamped to the last: a load past the end is never stored) into register slot r
+  auto load_stage = [&](int kt, int r) {
+    const int k0 = min(kt, (KFIX ? KFIX : g.K) / BK - 1) * BK + lc;
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i) {
       const int q = wave * A_PER_WAVE + i;
       const int row = min(m0 + (q / KS) * 16 + lr, M - 1);
-      ra[i] = load_frag(Ab + (size_t)row * g.lda + k0 + (q % KS) * 32);
+      ra[r][i] = load_frag(Ab + (size_t)row * g.lda + k0 + (q % KS) * 32);
     }
 #pragma unroll
     for (int i = 0; i < B_PER_WAVE; ++i) {
       const int q = wave * B_PER_WAVE + i;
-      rb[i] = load_frag(Wb + (size_t)(n0 + (q / KS) * 16 + lr) * g.ldw + k0 + (q % KS) * 32);
+      rb[r][i] = load_frag(Wb + (size_t)(n0 + (q / KS) * 16 + lr) * g.ldw + k0 + (q % KS) * 32);
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf, int r) {
 #pragma unroll
-    for (int i = 0; i < A_PER_WAVE; ++i) store_frag(&sA[buf][(wave * A_PER_WAVE + i) * BLK + lane * FE], ra[i]);
+    for (int i = 0; i < A_PER_WAVE; ++i) store_frag(&sA[buf][(wave * A_PER_WAVE + i) * BLK + lane * FE], ra[r][i]);
 #pragma unroll
-    for (int i = 0; i < B_PER_WAVE; ++i) store_frag(&sB[buf][(wave * B_PER_WAVE + i) * BLK + lane * FE], rb[i]);
+    for (int i = 0; i < B_PER_WAVE; ++i) store_frag(&sB[buf][(wave * B_PER_WAVE + i) * BLK + lane * FE], rb[r][i]);
   };
 
   f32x4 acc[MT][NT];  // zeroed just before the K loop: no registers held through the prologue
@@ -531,15 +535,35 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   } else {
     zero_acc();
     load_bias();
-    load_stage(0);
-    store_stage(0);
+#pragma unroll
+    for (int r = 0; r < PD; ++r) load_stage(r, r);
+    store_stage(0, 0);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) load_stage(kt + 1);
-      compute(sA[cur], sB[cur], kt);
-      if (kt + 1 < KT) store_stage(cur ^ 1);
+    // step kt, slot r = kt % PD: the slot's K-step reached LDS at the end of
+    // step kt - 1 (or before the loop), so it takes K-step kt + PD
+    auto fstep = [&](int kt, auto Rc) {
+      constexpr int r = decltype(Rc)::value;
+      load_stage(kt + PD, r);
+      compute(sA[kt & 1], sB[kt & 1], kt);
+      if (kt + 1 < KT) store_stage((kt + 1) & 1, (r + 1) % PD);
       __syncthreads();
+    };
+    auto fround = [&](int kt0) {
+      fstep(kt0, std::integral_constant<int, 0>());
+      if constexpr (PD > 1)
+        if (kt0 + 1 < KT) fstep(kt0 + 1, std::integral_constant<int, (PD > 1 ? 1 : 0)>());
+      if constexpr (PD > 2)
+        if (kt0 + 2 < KT) fstep(kt0 + 2, std::integral_constant<int, (PD > 2 ? 2 : 0)>());
+      if constexpr (PD > 3)
+        if (kt0 + 3 < KT) fstep(kt0 + 3, std::integral_constant<int, (PD > 3 ? 3 : 0)>());
+    };
+    // with K fixed at compile time the loop unrolls completely: no slot value
+    // crosses a loop back edge, where the register copies would wait for loads
+    if constexpr (KC != 0) {
+#pragma unroll
+      for (int kt0 = 0; kt0 < KT; kt0 += PD) fround(kt0);
+    } else {
+      for (int kt0 = 0; kt0 < KT; kt0 += PD) fround(kt0);
     }
   }
 
@@ -1134,8 +1158,8 @@ static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
       else gemm_kernel<T, BM, BN, E_RESID, NS, false, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     case E_GELU_F32:
-      if constexpr (LNA || RF || KFIX != 0) return hipErrorInvalidValue;
-      else gemm_kernel<T, BM, BN, E_GELU_F32, NS><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      if constexpr (LNA || RF) return hipErrorInvalidValue;
+      else gemm_kernel<T, BM, BN, E_GELU_F32, NS, false, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -1184,7 +1208,19 @@ hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t
   }
   if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<float, 128, 128, 2>(emode, a, s);
   // the FP32 scorer on the marker rows: narrower tiles, twice the work-groups
-  if (emode == E_GELU_F32 && ((a.M + 63) / 64) * (a.N / 64) <= 256) return gemm_dispatch<float, 64, 64, 2>(emode, a, s);
+  // One round of work-groups with the model's K: 4 K-steps in flight, the K
+  // loop unrolled completely.
+  if (emode == E_GELU_F32 && ((a.M + 63) / 64) * (a.N / 64) <= 256)
+    return a.K == kWidth ? gemm_dispatch<float, 64, 64, 5, false, kWidth>(emode, a, s)
+                         : gemm_dispatch<float, 64, 64, 2>(emode, a, s);
+  if (((a.M + 63) / 64) * nt <= 256) {
+    switch (a.K) {
+      case kWidth: return gemm_dispatch<float, 64, 128, 5, false, kWidth>(emode, a, s);
+      case kGeglu: return gemm_dispatch<float, 64, 128, 5, false, kGeglu>(emode, a, s);
+      case kHeadFfn: return gemm_dispatch<float, 64, 128, 5, false, kHeadFfn>(emode, a, s);
+      default: break;
+    }
+  }
   return gemm_dispatch<float, 64, 128, 2>(emode, a, s);
 }
 
