@@ -301,9 +301,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   // rows, the residual) are all read before the first store: a load that
   // follows a store to C may alias it, and the compiler would then wait for
   // every earlier memory operation at each row.  A tile of at most 64 rows
-  // (kHoist) reads them before the K loop (the table rows, which need the
-  // positions, after the fused LayerNorm or else at the epilogue), larger
-  // tiles one 16-row group at a time.
+  // (kHoist) reads them before the K loop (the RoPE table rows, which need
+  // the positions: right after a fused LayerNorm that has every weight stage
+  // in flight, else before the epilogue), larger tiles one 16-row group at a
+  // time.
   constexpr bool kHoist = kDma && BM <= 64;
   constexpr int HG = kHoist ? MT : 1;  // row groups held at once
   const bool has_bias = g.bias != nullptr;
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
       for (int j = 0; j < NT; ++j) res[h][r][j] = C[j * 16];
     }
   };
-  // the operands a 64-row tile reads before its K loop
+  // the operands a tile of at most 64 rows reads before its K loop
   auto load_hoisted = [&]() {
     load_bias();
     if constexpr (kHoist) {
