@@ -121,6 +121,21 @@ def test_logits_jittered(jit_models, prec):
     assert err <= (FP32_LOGIT_TIGHT if prec == "fp32" else BF16_LOGIT_TIGHT)
 
 
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_logits_random_ragged_batches(models, oracle_weights, seed, prec):
+    """Seeded random packs of 1-6 sequences of 24-300 tokens (question types,
+    option counts and lengths drawn as in the serving mix): every length
+    class against the 64-key tiles, window edges and item boundaries."""
+    from oracle import julia_oracle as jo
+    batch = synth.make_ragged_batch(seed, 1 + seed, 24, 300)
+    ref = jo.forward(oracle_weights, batch)
+    got = run_logits(models[prec], batch)
+    err = float(np.max(np.abs(got - ref)))
+    print(prec, seed, np.diff(batch.seq_offsets).tolist(), "max |dlogit|", err)
+    assert err <= (FP32_LOGIT_TIGHT if prec == "fp32" else BF16_LOGIT_TIGHT)
+
+
 @pytest.mark.parametrize("config", [0, 1])
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
 def test_logits_small_configs(models, oracle_weights, config, prec):
