@@ -8,7 +8,7 @@ throughput case: 16 sequences of 1,024 tokens, question types cycling
 choice/score/noul, 2-20 options of 1-48 tokens, bf16. Extra fields report
 the batch-1 latency case (1 x 1,024: mean, per-call percentiles, and host ids
 to host logits), the long-context case (16 x 8,192), the ragged serving mix
-(256 sequences of 64-2,048 tokens) and FP32 mode.
+(256 sequences of 64-2,048 tokens), FP32 mode and FP8 mode.
 
 `roofline` covers the kernel class with the most device time in the timed
 region, measured with HIP events bracketing each of its launches on the
@@ -298,6 +298,13 @@ def main():
             extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2),
                            "fp32_peak_frac": round(fl / (tt / st) / 1e12 / PEAK_FP32_TFLOPS, 4)}
         m32.close()
+        # FP8 mode (e4m3 QKV and W_i products, per-GEMM schedule), for context
+        m8 = lib.Model(path, lib.FP8, max_tokens=20_000, max_markers=1024, device=0)
+        m8.set_graph_cache(2)
+        for name, b, st in [("16x1024_fp8", b2, 10), ("1x1024_fp8", b1, 20)]:
+            tt, *_ = time_workload(m8, b, st, 2, sample=False)
+            extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2)}
+        m8.close()
         result["extra"] = extra
     result["ms_per_call_1x1024"] = result.get("extra", {}).get("1x1024_ms_per_call")
     model.close()

@@ -61,6 +61,24 @@ uint16_t f32_to_bf16(float f) {  // round to nearest even; NaN stays NaN
   return (uint16_t)(u >> 16);
 }
 
+// OCP e4m3 (1 sign, 4 exponent bits biased by 7, 3 mantissa bits; no
+// infinities, S.1111.111 is NaN, largest finite 448), round to nearest even.
+// Normal codes hold (1 + m/8) 2^(e-7) for e = 1..15, subnormal ones m/8 2^-6;
+// a magnitude that rounds above 448 becomes NaN, as the device conversion does.
+uint8_t f32_to_e4m3(float f) {
+  const uint8_t sign = std::signbit(f) ? 0x80 : 0x00;
+  const float a = std::fabs(f);
+  if (!(a == a)) return sign | 0x7f;
+  if (a < 0x1p-6f) return sign | (uint8_t)std::nearbyint(a * 0x1p9f);  // 8 steps of 2^-9; 8 -> 2^-6 (0x08)
+  int e;
+  std::frexp(a, &e);  // a = f 2^e, f in [0.5, 1): a = (1 + m/8) 2^(e-1)
+  int E = e - 1;
+  int q = (int)std::nearbyint((std::ldexp(a, -E) - 1.0f) * 8.0f);  // exact in FP32
+  if (q == 8) q = 0, ++E;
+  const int code = ((E + 7) << 3) | q;
+  return code > 0x7e ? (uint8_t)(sign | 0x7f) : (uint8_t)(sign | code);
+}
+
 // Matrix-core fragment order of a row-major W [N, K] (rows = output columns):
 // block (gn, s) holds 64 lanes x 8 bf16, lane l element e = W[16 gn + l % 16]
 // [32 s + 8 (l / 16) + e]; blocks are stored gn-major (index gn * K/32 + s), so a
@@ -88,6 +106,9 @@ struct LayerW {
   const float *mlp_norm = nullptr;
   // bf16 fragment-ordered copies for the row-block layer kernel
   const void *pWqkv = nullptr, *pWo = nullptr, *pWi = nullptr, *pWout = nullptr;
+  // JL_FP8: e4m3 codes [N, 384] of the QKV (layers 1-21) and W_i rows and each row's scale
+  const void *Wqkv8 = nullptr, *Wi8 = nullptr;
+  const float *sqkv = nullptr, *si = nullptr;
 };
 struct HeadW {
   const void *in_w = nullptr, *out_w = nullptr, *l1_w = nullptr, *l2_w = nullptr;
@@ -377,7 +398,8 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
                                int device, jl_model **out) {
   if (!path || !out) return fail(JL_ERR_ARG, "path and out must not be NULL");
   *out = nullptr;
-  if (precision != JL_FP32 && precision != JL_BF16) return fail(JL_ERR_ARG, "precision must be JL_FP32 or JL_BF16");
+  if (precision != JL_FP32 && precision != JL_BF16 && precision != JL_FP8)
+    return fail(JL_ERR_ARG, "precision must be JL_FP32, JL_BF16 or JL_FP8");
   if (max_tokens < 1 || max_tokens > (int64_t)1 << 26) return fail(JL_ERR_ARG, "max_tokens must be in 1..2^26");
   if (max_markers < 2 || max_markers > max_tokens) return fail(JL_ERR_ARG, "max_markers must be in 2..max_tokens");
   if (device < 0) return fail(JL_ERR_ARG, "device must be >= 0");
@@ -387,7 +409,8 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
   std::map<std::string, TensorEntry> tab;
   if (int rc = parse_weight_file(path, mf, tab)) return rc;
 
-  const bool bf = precision == JL_BF16;
+  const bool bf = precision != JL_FP32;  // JL_FP8: bf16 operands outside its e4m3 products
+  const bool f8 = precision == JL_FP8;
   const size_t es = bf ? 2 : 4;
   const char *base = (const char *)mf.base;
   auto get = [&](const std::string &name, std::vector<uint32_t> shape, const float **data) -> int {
@@ -430,6 +453,24 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     pend.push_back({dst, off});
   };
 
+  // e4m3 codes of a matrix [rows, cols] (rows through `row_of`), each row
+  // scaled so that its largest magnitude becomes 448, and the row scales
+  auto put_e4m3 = [&](const float *src, size_t rows, size_t cols, const void **dst, const float **scale,
+                      const std::vector<int> *row_of) {
+    const size_t off = ar.add(rows * cols), soff = ar.add(rows * 4);
+    uint8_t *d = (uint8_t *)(ar.buf.data() + off);
+    float *sc = (float *)(ar.buf.data() + soff);
+    for (size_t r = 0; r < rows; ++r) {
+      const float *sr = src + (size_t)(row_of ? (*row_of)[r] : (int)r) * cols;
+      float amax = 0.f;
+      for (size_t c = 0; c < cols; ++c) amax = std::max(amax, std::fabs(sr[c]));
+      const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+      sc[r] = s;
+      for (size_t c = 0; c < cols; ++c) d[r * cols + c] = f32_to_e4m3(sr[c] / s);
+    }
+    pend.push_back({dst, off});
+    pend.push_back({(const void **)scale, soff});
+  };
   auto put_packed = [&](const float *src, int rows, int cols, const void **dst, const std::vector<int> *row_of,
                         const std::vector<float> *row_scale = nullptr) {
     const size_t off = ar.add((size_t)rows * cols * 2);
@@ -490,6 +531,7 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     t = scale_q_rows(t, 3 * D, D);
     put_elem(t, 3 * D, D, &m->L[l].Wqkv, nullptr);
     if (bf) put_packed(t, 3 * D, D, &m->L[l].pWqkv, nullptr);
+    if (f8 && l != 0) put_e4m3(t, 3 * D, D, &m->L[l].Wqkv8, &m->L[l].sqkv, nullptr);
     GET(p + "attn.Wo.weight", D, D);
     put_elem(t, D, D, &m->L[l].Wo, nullptr);
     if (bf) put_packed(t, D, D, &m->L[l].pWo, nullptr);
@@ -497,6 +539,7 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     put_f32(t, D, &m->L[l].mlp_norm);
     GET(p + "mlp.Wi.weight", 2 * kGeglu, D);
     put_elem(t, 2 * kGeglu, D, &m->L[l].Wi, &geglu_rows);
+    if (f8) put_e4m3(t, 2 * kGeglu, D, &m->L[l].Wi8, &m->L[l].si, &geglu_rows);
     if (bf) put_packed(t, 2 * kGeglu, D, &m->L[l].pWi, &geglu_rows, &gate_half);
     GET(p + "mlp.Wo.weight", D, kGeglu);
     put_elem(t, D, kGeglu, &m->L[l].Wout, nullptr);
@@ -908,7 +951,7 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     JL_HIP(hipMemcpyAsync(out, src, rows * D * 4, hipMemcpyDeviceToDevice, s));
     return JL_OK;
   };
-  const bool row_block = bf && T >= m->row_block_min_tokens;
+  const bool row_block = m->precision == JL_BF16 && T >= m->row_block_min_tokens;
   if (row_block) {  // the embedding kernel also computes the first layer's QKV
     EmbedArgs ea{};
     ea.ids = ids;
@@ -982,7 +1025,9 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
   for (int l = 0; l < kLayers; ++l) {
     const LayerW &W = m->L[l];
     const bool glob = layer_is_global(l);
-    GemmArgs q = with_ln(gemm(u, D, W.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D), m->x, W.attn_norm, nullptr);
+    GemmArgs q = with_ln(gemm(u, D, W.Wqkv8 ? W.Wqkv8 : W.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D), m->x,
+                         W.attn_norm, nullptr);
+    q.w_scale = W.sqkv;  // e4m3 products (JL_FP8), else nullptr
     q.rope_cos = m->rope_cos[glob];
     q.rope_sin = m->rope_sin[glob];
     q.pos = m->pos;
@@ -991,10 +1036,10 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     at.half_window = glob ? -1 : kHalfWindow;
     JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, attention(bf, at, pl, glob, s));
     JL_LAUNCH(JL_K_OUTPROJ, launch_gemm(bf, E_RESID, gemm(m->o, D, W.Wo, D, nullptr, m->x, D, T, D, D), s));
-    JL_LAUNCH(JL_K_MLP_IN, launch_ln_gemm(bf, E_GEGLU,
-                                          with_ln(gemm(u, D, W.Wi, D, nullptr, m->act, kGeglu, T, 2 * kGeglu, D),
-                                                  m->x, W.mlp_norm, nullptr),
-                                          s));
+    GemmArgs wi = with_ln(gemm(u, D, W.Wi8 ? W.Wi8 : W.Wi, D, nullptr, m->act, kGeglu, T, 2 * kGeglu, D), m->x,
+                          W.mlp_norm, nullptr);
+    wi.w_scale = W.si;
+    JL_LAUNCH(JL_K_MLP_IN, launch_ln_gemm(bf, E_GEGLU, wi, s));
     JL_LAUNCH(JL_K_MLP_OUT,
               launch_gemm(bf, E_RESID, gemm(m->act, kGeglu, W.Wout, kGeglu, nullptr, m->x, D, T, D, kGeglu), s));
     if (stop == l + 1) return copy_out(m->x, T);
@@ -1102,7 +1147,7 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
 
 // Replay (capturing on first use) the forward pass of this batch shape.
 int forward_graph(jl_model *m, const int32_t *ids, const Plan &pl, float *out, hipStream_t s) {
-  const bool row_block = m->bf16 && pl.T >= m->row_block_min_tokens;
+  const bool row_block = m->precision == JL_BF16 && pl.T >= m->row_block_min_tokens;
   jl_model::GraphEntry *hit = nullptr;
   for (auto &g : m->graphs)
     if (g.T == pl.T && g.B == pl.B && g.M == pl.M && g.n_work == pl.n_work && g.n_work_wide == pl.n_work_wide &&

@@ -110,6 +110,15 @@ __device__ inline void ln_row16(const f32x4 (&x)[6], float &mean, float &rstd) {
   rstd = rsqrtf(row16_sum(q) * (1.0f / kWidth) + kLnEps);
 }
 
+// Maximum over each 16-lane row of the wave (same butterflies as row16_sum).
+__device__ inline float row16_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return v;
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

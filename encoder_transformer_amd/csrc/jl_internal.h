@@ -48,6 +48,9 @@ struct GemmArgs {
   const float *ln_x;    // FP32 [M, 384]
   const float *ln_gain; // nullptr: A = ln_x converted, unnormalized (identity pre-norm)
   const float *ln_shift;// or nullptr
+  // e4m3 products (launch_ln_gemm only): W holds e4m3 codes [N, ldw] and
+  // w_scale[N] each row's scale; nullptr: W is bf16/FP32
+  const float *w_scale;
 };
 
 // One attention work item: up to 64 or 128 queries (the launch's tile size) of

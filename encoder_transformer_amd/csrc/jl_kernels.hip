@@ -107,7 +107,8 @@ __device__ inline int xcd_tile(int b, int n_tiles) {
   return x * per + min(x, rem) + local;
 }
 
-template <typename T, int BM, int BN, int EM, int NSTAGE, bool LNA = false, int KFIX = 0, bool RF = false>
+template <typename T, int BM, int BN, int EM, int NSTAGE, bool LNA = false, int KFIX = 0, bool RF = false,
+          bool F8 = false>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int n_tiles) {
   constexpr int BK = GemmBK<T>::v, KS = BK / 32;           // 32-wide k sub-steps per stage
   constexpr int TM = BM / 2, TN = BN / 2;                   // wave tile
@@ -146,17 +147,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   constexpr int NS = kDma ? NSTAGE : 2;
   static_assert(NS >= 2 && NS <= 6, "stages");
   static_assert(!LNA || (kDma && BM == 64), "fused LayerNorm: bf16, 64-row tiles");
+  // F8: e4m3 operands.  The LayerNorm rows are scaled per row (largest
+  // magnitude -> 448) and converted into an LDS tile of e4m3 codes; W holds
+  // e4m3 codes with a scale per row (w_scale).  Both tiles keep a 16-row
+  // group's codes in 16-byte chunks: byte k % 16 of chunk (k / 16) * 16 + row,
+  // so that a lane's 8 codes of a 32-k step are one 8-byte read, and a weight
+  // stage (64 k of 16 rows, 1 KB) is one 16-byte LDS-direct load per lane.
+  // The products accumulate in FP32 and the epilogue multiplies by both scales.
+  static_assert(!F8 || (LNA && RF && (EM == E_STORE || EM == E_GEGLU)), "e4m3: LayerNorm with a gain, QKV or GEGLU");
+  constexpr int SBE = kDma ? (F8 ? B_BLKS * BLK / 2 : B_BLKS * BLK) : 1;  // stage elements of W
   constexpr int KA = kWidth / 32;  // k sub-steps of the resident A tile
   constexpr int SA = kDma && !LNA ? A_BLKS * BLK : 1;
   __shared__ __attribute__((aligned(16))) T sA[kDma ? 1 : NS][A_BLKS * BLK];  // FP32 stages
   __shared__ __attribute__((aligned(16))) T sB[kDma ? 1 : NS][B_BLKS * BLK];
-  __shared__ __attribute__((aligned(16))) T sAk[LNA ? BM * kWidth : 1];
-  __shared__ __attribute__((aligned(16))) T sA0[SA], sB0[kDma ? B_BLKS * BLK : 1];
-  __shared__ __attribute__((aligned(16))) T sA1[SA], sB1[kDma ? B_BLKS * BLK : 1];
-  __shared__ __attribute__((aligned(16))) T sA2[NS > 2 ? SA : 1], sB2[kDma && NS > 2 ? B_BLKS * BLK : 1];
-  __shared__ __attribute__((aligned(16))) T sA3[NS > 3 ? SA : 1], sB3[kDma && NS > 3 ? B_BLKS * BLK : 1];
-  __shared__ __attribute__((aligned(16))) T sA4[NS > 4 ? SA : 1], sB4[kDma && NS > 4 ? B_BLKS * BLK : 1];
-  __shared__ __attribute__((aligned(16))) T sA5[NS > 5 ? SA : 1], sB5[kDma && NS > 5 ? B_BLKS * BLK : 1];
+  __shared__ __attribute__((aligned(16))) T sAk[LNA && !F8 ? BM * kWidth : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t sA8[F8 ? BM * kWidth : 1];
+  __shared__ float sSa[F8 ? BM : 1];  // e4m3 row scales
+  __shared__ __attribute__((aligned(16))) T sA0[SA], sB0[SBE];
+  __shared__ __attribute__((aligned(16))) T sA1[SA], sB1[SBE];
+  __shared__ __attribute__((aligned(16))) T sA2[NS > 2 ? SA : 1], sB2[NS > 2 ? SBE : 1];
+  __shared__ __attribute__((aligned(16))) T sA3[NS > 3 ? SA : 1], sB3[NS > 3 ? SBE : 1];
+  __shared__ __attribute__((aligned(16))) T sA4[NS > 4 ? SA : 1], sB4[NS > 4 ? SBE : 1];
+  __shared__ __attribute__((aligned(16))) T sA5[NS > 5 ? SA : 1], sB5[NS > 5 ? SBE : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -270,6 +282,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[c][e] = (y[c][e] - mean) * rstd * lng[c][e] + lns[c][e];
       }
+      if constexpr (F8) {
+        float am = 0.f;
+#pragma unroll
+        for (int c = 0; c < 6; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(y[c][e]));
+        am = row16_max(am);
+        const float sc = am > 0.f ? am / 448.0f : 1.0f;
+        const int r16 = rl & 15;
+        uint8_t *grp = &sA8[(rl >> 4) * 16 * kWidth];
+#pragma unroll
+        for (int c = 0; c < 6; ++c) {
+          const int k = 64 * c + 4 * lj;
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[c][0] / sc, y[c][1] / sc, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(y[c][2] / sc, y[c][3] / sc, w, true);
+          const unsigned a3 =
+              (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)&grp[16 * ((k >> 4) * 16 + r16) + (k & 15)];
+          asm volatile("ds_write_b32 %0, %1" ::"v"(a3), "v"(w));
+        }
+        if (lj == 0) {
+          const unsigned a3 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float *)&sSa[rl];
+          asm volatile("ds_write_b32 %0, %1" ::"v"(a3), "v"(__float_as_uint(sc)));
+        }
+        continue;
+      }
 #pragma unroll
       for (int c = 0; c < 6; ++c) {
         // (row rl, k = 64 c + 4 lj): block (rl / 16, k / 32), lane (rl % 16) + 16 ((k % 32) / 8), element k % 8
@@ -316,6 +353,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   const int pos_step = rope ? 1 : 0;
   const float *cos_p = rope ? g.rope_cos : g_ln_zero_shift, *sin_p = rope ? g.rope_sin : g_ln_zero_shift;
   float bias_v[NT];
+  float wsc_v[F8 ? NT : 1];  // e4m3 weight row scales of this lane's columns
   int rpos[HG][4];
   float rcs[HG][4][4];  // per row: cos and sin of d = lr, then of d = 16 + lr
   float res[EM == E_RESID ? HG : 1][4][EM == E_RESID ? NT : 1];
@@ -326,6 +364,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     const float *b = has_bias ? g.bias : (const float *)g.C;
 #pragma unroll
     for (int j = 0; j < NT; ++j) bias_v[j] = b[col0 + j * 16];
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) wsc_v[j] = g.w_scale[col0 + j * 16];
+    }
   };
   auto load_pos = [&](int i, int h) {
 #pragma unroll
@@ -365,6 +407,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     if constexpr (LNA) return load_frag(&sAk[((wm * MT + i) * KA + kt * KS + ks) * BLK + lane * FE]);
     else return load_frag(&cA[((wm * MT + i) * KS + ks) * BLK + lane * FE]);
   };
+  // e4m3 K-step kt: A codes from the resident tile, W codes from stage cB
+  auto compute8 = [&](const T *cB, int kt) {
+    const uint8_t *B8 = (const uint8_t *)cB;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kk = ks * 32 + lc;                 // k inside the stage
+      const int ka = kt * 64 + kk;                 // k inside the row
+      long fa[MT], fb[NT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        fa[i] = *reinterpret_cast<const long *>(&sA8[(wm * MT + i) * 16 * kWidth + 16 * ((ka >> 4) * 16 + lr) + (ka & 15)]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        fb[j] = *reinterpret_cast<const long *>(&B8[(wn * NT + j) * 1024 + 16 * ((kk >> 4) * 16 + lr) + (kk & 15)]);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
   auto compute = [&](const T *cA, const T *cB, int kt) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -380,7 +442,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     }
   };
   if constexpr (kDma) {
-    constexpr int LPS = (LNA ? 0 : A_PER_WAVE) + B_PER_WAVE;  // loads per stage and wave
+    constexpr int LPS = F8 ? BN / 64 : (LNA ? 0 : A_PER_WAVE) + B_PER_WAVE;  // loads per stage and wave
     auto bufA = [&](auto Bc) -> T * {
       constexpr int B = decltype(Bc)::value;
       if constexpr (B == 0) return sA0;
@@ -424,7 +486,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
       voB[i] = (((q / KS) * 16 + lr) * g.ldw + lc + (q % KS) * 32) * (int)sizeof(T);
     }
     const T *tileA = Ab + (size_t)(LNA ? 0 : m0) * g.lda, *tileB = Wb + (size_t)n0 * g.ldw;
+    // F8: 16-row group q of the stage from lane (row lane % 16, k chunk lane / 16)
+    int voB8[F8 ? BN / 64 : 1];
+    const uint8_t *tileB8 = (const uint8_t *)g.W + (size_t)n0 * g.ldw;
+    if constexpr (F8) {
+#pragma unroll
+      for (int i = 0; i < BN / 64; ++i) voB8[i] = ((wave * (BN / 64) + i) * 16 + lr) * g.ldw + (lane >> 4) * 16;
+    }
     auto issue_stage = [&](int kt, T *dA, T *dB) {
+      if constexpr (F8) {
+#pragma unroll
+        for (int i = 0; i < BN / 64; ++i)
+          buffer_load_lds16(tileB8, (lds_void *)((uint8_t *)dB + (wave * (BN / 64) + i) * 1024), voB8[i], kt * 64);
+        return;
+      }
       const int so = kt * BK * (int)sizeof(T);
 #pragma unroll
       for (int i = 0; i < (LNA ? 0 : A_PER_WAVE); ++i) {
@@ -475,7 +550,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
         using Next = std::integral_constant<int, (B + NS - 1) % NS>;
         if (kt > 0 && kt + NS - 1 < KT) issue_stage(kt + NS - 1, bufA(Next()), bufB(Next()));
       }
-      compute(bufA(Bc), bufB(Bc), kt);
+      if constexpr (F8) compute8(bufB(Bc), kt);
+      else compute(bufA(Bc), bufB(Bc), kt);
     };
     // loads older than every stage never hold up a stage wait (the
     // scheduling barrier keeps the scheduler from sinking them towards their
@@ -590,6 +666,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
       float v[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j) v[j] = acc[i][j][r];
+      if constexpr (F8) {
+        const float sa = sSa[row - m0];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) v[j] *= sa * wsc_v[j];
+      }
       if (EM == E_GEGLU) {  // sub-tiles (2p, 2p+1) hold matching GELU and gate columns
         T *C = (T *)g.C + (size_t)row * g.ldc + wcol / 2 + lr;
 #pragma unroll
@@ -1137,29 +1218,29 @@ hipError_t launch_embed(const int32_t *ids, const float *emb, const float *gain,
   return hipGetLastError();
 }
 
-template <typename T, int BM, int BN, int NS, bool LNA = false, int KFIX = 0, bool RF = false>
+template <typename T, int BM, int BN, int NS, bool LNA = false, int KFIX = 0, bool RF = false, bool F8 = false>
 static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
   const int tiles_n = a.N / BN, n_tiles = ((a.M + BM - 1) / BM) * tiles_n;
   constexpr bool pairs = (BN / 32) % 4 == 0;  // 64-column groups per wave: GEGLU and RoPE epilogues
   switch (emode) {
     case E_STORE:
       if constexpr (!pairs) return hipErrorInvalidValue;
-      else gemm_kernel<T, BM, BN, E_STORE, NS, LNA, KFIX, RF><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      else gemm_kernel<T, BM, BN, E_STORE, NS, LNA, KFIX, RF, F8><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     case E_GEGLU:
       if constexpr (!pairs || (LNA && !RF)) return hipErrorInvalidValue;
-      else gemm_kernel<T, BM, BN, E_GEGLU, NS, LNA, KFIX, RF><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
+      else gemm_kernel<T, BM, BN, E_GEGLU, NS, LNA, KFIX, RF, F8><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     case E_RELU:
-      if constexpr (LNA && !RF) return hipErrorInvalidValue;
+      if constexpr ((LNA && !RF) || F8) return hipErrorInvalidValue;
       else gemm_kernel<T, BM, BN, E_RELU, NS, LNA, KFIX, RF><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     case E_RESID:
-      if constexpr (LNA || RF) return hipErrorInvalidValue;
+      if constexpr (LNA || RF || F8) return hipErrorInvalidValue;
       else gemm_kernel<T, BM, BN, E_RESID, NS, false, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     case E_GELU_F32:
-      if constexpr (LNA || RF) return hipErrorInvalidValue;
+      if constexpr (LNA || RF || F8) return hipErrorInvalidValue;
       else gemm_kernel<T, BM, BN, E_GELU_F32, NS, false, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
     default: return hipErrorInvalidValue;
@@ -1229,6 +1310,12 @@ hipError_t launch_ln_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStrea
   if (a.M <= 0) return hipSuccess;
   if (a.N % 128 != 0 || a.K != kWidth || !a.ln_x) return hipErrorInvalidValue;
   const long nt = a.N / 128, tiles64 = ((a.M + 63) / 64) * nt;
+  // e4m3 products: every batch size, 64 x 128 tiles, all 6 weight stages up
+  // front (72 KB of LDS: two work-groups per CU)
+  if (a.w_scale != nullptr) {
+    if (!bf16_mode || a.ln_gain == nullptr || (emode != E_STORE && emode != E_GEGLU)) return hipErrorInvalidValue;
+    return gemm_dispatch<bf16, 64, 128, 6, true, 0, true, true>(emode, a, s);
+  }
   // the GEMM alone would take 64-row tiles: normalize inside it
   // (the GEGLU and ReLU products normalize unconditionally inside: they need a gain)
   if (bf16_mode && (emode == E_STORE || ((emode == E_GEGLU || emode == E_RELU) && a.ln_gain != nullptr)) &&

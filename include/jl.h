@@ -38,10 +38,18 @@ typedef struct jl_model jl_model; /* opaque: weights on the device + workspace *
 
 enum jl_precision {
   JL_FP32 = 0, /* every product in FP32 (FP32 matrix cores)                    */
-  JL_BF16 = 1  /* GEMM and attention operands in bf16 (round to nearest even),  */
+  JL_BF16 = 1, /* GEMM and attention operands in bf16 (round to nearest even),  */
                /* FP32 accumulation; residual stream, LayerNorms, embeddings,   */
                /* RoPE tables, scorer and softmax stay FP32 ("Julia-1 MLX",     */
                /* Performance: the residual carries outliers near 4,000)        */
+  JL_FP8 = 2   /* as JL_BF16, but the encoder's QKV (layers 1-21) and W_i       */
+               /* products take OCP e4m3 operands on the matrix cores: weights  */
+               /* scaled per output row at load (row max -> 448), normalized    */
+               /* activations per token row inside the product, FP32            */
+               /* accumulation, both scales applied to the FP32 result; the     */
+               /* reduced-precision projection mode of "Julia-1 MLX",           */
+               /* Performance (precision), on gfx950's fp8 matrix cores.        */
+               /* Always the per-GEMM schedule                                  */
 };
 
 enum jl_status {

@@ -146,6 +146,40 @@ def attention_band(q: np.ndarray, k: np.ndarray, v: np.ndarray, half_window: int
 # weights
 # ---------------------------------------------------------------------------
 
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest OCP e4m3 value (ties to even).
+
+    e4m3 (the OCP 8-bit floating-point format E4M3): sign, 4 exponent bits
+    with bias 7, 3 mantissa bits; normal values (1 + m/8) 2^(e-7), e = 1..15,
+    subnormal ones (m/8) 2^-6; no infinities, the largest finite value 448.
+    A magnitude that rounds above 448 has no code and becomes NaN.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    out = np.empty_like(a)
+    sub = a < 2.0 ** -6
+    out[sub] = np.round(a[sub] * 2.0 ** 9) * 2.0 ** -9  # np.round: ties to even
+    nz = ~sub
+    e = np.floor(np.log2(a[nz]))
+    step = 2.0 ** (e - 3)  # 8 steps per binade
+    out[nz] = np.round(a[nz] / step) * step
+    out[out > 448.0] = np.nan
+    return np.copysign(out, x).astype(np.float32)
+
+
+def quantize_rows_e4m3(m: np.ndarray) -> np.ndarray:
+    """Per-row e4m3 quantization, returned dequantized (float64).
+
+    Each row, in float32, is divided by its scale s = max |row| / 448 (s = 1
+    for an all-zero row), rounded to e4m3, and multiplied back by s.
+    """
+    m32 = np.asarray(m, dtype=np.float32)
+    amax = np.max(np.abs(m32), axis=1)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = e4m3_round(m32 / s[:, None])
+    return q.astype(np.float64) * s.astype(np.float64)[:, None]
+
+
 class OracleWeights:
     """float64 view of the weights; the embedding table stays float32 and rows are gathered."""
 
@@ -198,16 +232,29 @@ def embed(W: OracleWeights, ids: np.ndarray) -> np.ndarray:
     return layer_norm(W.emb[ids].astype(np.float64), W.emb_norm)
 
 
-def encoder_layer(W: OracleWeights, l: int, x: np.ndarray, half_window: Optional[int] = None) -> np.ndarray:
+def e4m3_weights(P: dict, name: str) -> np.ndarray:
+    """A weight matrix quantized per row to e4m3 (cached beside it)."""
+    if name + "_e4m3" not in P:
+        P[name + "_e4m3"] = quantize_rows_e4m3(P[name])
+    return P[name + "_e4m3"]
+
+
+def encoder_layer(W: OracleWeights, l: int, x: np.ndarray, half_window: Optional[int] = None,
+                  fp8: bool = False) -> np.ndarray:
     """One pre-norm ModernBERT layer: x += Attn(LN x); x += GEGLU-MLP(LN x).
 
     ``half_window`` overrides the local band (used by the window pins).
+    ``fp8``: the QKV product (layers after the first, whose input has no
+    pre-norm) and the W_i product take both operands quantized per row to e4m3.
     """
     P = W.layers[l]
     L = x.shape[0]
     glob = is_global(l)
     u = x if P["attn_norm"] is None else layer_norm(x, P["attn_norm"])
-    qkv = u @ P["Wqkv"].T
+    if fp8 and P["attn_norm"] is not None:
+        qkv = quantize_rows_e4m3(u) @ e4m3_weights(P, "Wqkv").T
+    else:
+        qkv = u @ P["Wqkv"].T
     q = split_heads(qkv[:, :WIDTH])
     k = split_heads(qkv[:, WIDTH:2 * WIDTH])
     v = split_heads(qkv[:, 2 * WIDTH:])
@@ -218,15 +265,18 @@ def encoder_layer(W: OracleWeights, l: int, x: np.ndarray, half_window: Optional
     else:
         o = attention_band(q, k, v, HALF_WINDOW if half_window is None else half_window)
     x = x + o.reshape(L, WIDTH) @ P["Wo"].T
-    ab = layer_norm(x, P["mlp_norm"]) @ P["Wi"].T
+    if fp8:
+        ab = quantize_rows_e4m3(layer_norm(x, P["mlp_norm"])) @ e4m3_weights(P, "Wi").T
+    else:
+        ab = layer_norm(x, P["mlp_norm"]) @ P["Wi"].T
     a, g = ab[:, :GEGLU_HALF], ab[:, GEGLU_HALF:]
     return x + (gelu(a) * g) @ P["Wout"].T
 
 
-def encoder(W: OracleWeights, ids: np.ndarray, n_layers: int = N_LAYERS) -> np.ndarray:
+def encoder(W: OracleWeights, ids: np.ndarray, n_layers: int = N_LAYERS, fp8: bool = False) -> np.ndarray:
     x = embed(W, ids)
     for l in range(n_layers):
-        x = encoder_layer(W, l, x)
+        x = encoder_layer(W, l, x, fp8=fp8)
     return x
 
 
@@ -256,16 +306,17 @@ def score(W: OracleWeights, z: np.ndarray) -> np.ndarray:
     return (t @ S["fc2_w"].T + S["fc2_b"])[:, 0]
 
 
-def forward_sequence(W: OracleWeights, ids: np.ndarray, marks: np.ndarray, qtype: int) -> np.ndarray:
+def forward_sequence(W: OracleWeights, ids: np.ndarray, marks: np.ndarray, qtype: int,
+                     fp8: bool = False) -> np.ndarray:
     """Option logits of one sequence (markers given relative to the sequence)."""
-    x = encoder(W, ids)
+    x = encoder(W, ids, fp8=fp8)
     h = head_input(W, x, qtype)
     h = head_layer(W, 0, h)
     h = head_layer(W, 1, h)
     return score(W, h[marks])
 
 
-def forward(W: OracleWeights, batch, seqs: Optional[Sequence[int]] = None) -> np.ndarray:
+def forward(W: OracleWeights, batch, seqs: Optional[Sequence[int]] = None, fp8: bool = False) -> np.ndarray:
     """Logits of every marker of the packed batch, in marker order.
 
     Sequences never see each other, so each is evaluated on its own.
@@ -274,7 +325,7 @@ def forward(W: OracleWeights, batch, seqs: Optional[Sequence[int]] = None) -> np
     out: List[np.ndarray] = []
     for b in (range(batch.n_seqs) if seqs is None else seqs):
         ids, marks, qt = batch.sequence(b)
-        out.append(forward_sequence(W, ids, marks, qt))
+        out.append(forward_sequence(W, ids, marks, qt, fp8=fp8))
     return np.concatenate(out) if out else np.zeros(0)
 
 

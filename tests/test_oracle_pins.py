@@ -363,3 +363,64 @@ def test_batch_composition_oracle(oracle_weights):
         alone = jo.forward(oracle_weights, batch.subset([b]))
         assert np.array_equal(alone, packed[o:o + sizes[b]])
         o += sizes[b]
+
+
+# ---------------------------------------------------------------------------
+# e4m3 rounding and per-row quantization (the FP8 mode's reference)
+# ---------------------------------------------------------------------------
+
+def test_e4m3_round_matches_torch_float8_e4m3fn():
+    import torch
+    from oracle import julia_oracle as jo
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(100_000).astype(np.float32) * 60,
+                        rng.uniform(-0.03, 0.03, 50_000).astype(np.float32),
+                        np.array([0.0, -0.0, 448.0, -448.0, 2.0 ** -6, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11],
+                                 np.float32)])
+    x = x[np.abs(x) < 464]  # 464 and above round past the largest code
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(jo.e4m3_round(x).view(np.uint32), ref.view(np.uint32))
+
+
+def test_e4m3_round_ties_and_codes():
+    import torch
+    from oracle import julia_oracle as jo
+    # ties go to the even mantissa: 1.0625 lies between 1 (m = 0) and 1.125
+    # (m = 1); 1.1875 between 1.125 and 1.25 (m = 2); 2^-10 between 0 and 2^-9
+    got = jo.e4m3_round(np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 456.0], np.float32))
+    assert np.array_equal(got, np.array([1.0, 1.25, 0.0, 2.0 ** -8, 448.0], np.float32))
+    # 464 is the tie between 448 (m = 6) and 480 (m = 7, the NaN code): even
+    # wins; anything above it has no code
+    assert jo.e4m3_round(np.array([464.0], np.float32))[0] == 448.0
+    assert np.isnan(jo.e4m3_round(np.array([470.0], np.float32))[0])
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    fin = codes[np.isfinite(codes)]
+    assert fin.size == 254 and np.max(fin) == 448.0
+    assert np.array_equal(jo.e4m3_round(fin), fin)  # every code is a fixed point
+
+
+def test_quantize_rows_e4m3():
+    from oracle import julia_oracle as jo
+    rng = np.random.default_rng(6)
+    m = rng.standard_normal((40, 384)) * np.exp(rng.uniform(-6, 6, (40, 1)))
+    m[3] = 0.0
+    dq = jo.quantize_rows_e4m3(m)
+    m32 = m.astype(np.float32).astype(np.float64)
+    s = np.max(np.abs(m32), axis=1) / 448.0
+    s[3] = 1.0
+    q = dq / s[:, None]
+    nz = np.arange(40) != 3
+    assert np.allclose(np.max(np.abs(q[nz]), axis=1), 448.0, rtol=1e-6)  # the row maximum maps to 448
+    assert np.all(dq[3] == 0.0)
+    normal = np.abs(q) >= 2.0 ** -6
+    rel = np.abs(dq - m32)[normal] / np.abs(m32)[normal]
+    assert np.max(rel) <= 2.0 ** -4 * (1 + 1e-6)  # half a step of 3 mantissa bits
+
+
+def test_fp8_forward_is_a_small_perturbation(oracle_weights):
+    from oracle import julia_oracle as jo
+    batch = synth.make_batch(0)
+    ref = jo.forward(oracle_weights, batch)
+    q = jo.forward(oracle_weights, batch, fp8=True)
+    d = np.max(np.abs(q - ref))
+    assert 0.0 < d < 0.05 * np.max(np.abs(ref)) + 1e-3
