@@ -453,8 +453,8 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
     pend.push_back({dst, off});
   };
 
-  // e4m3 codes of a matrix [rows, cols] (rows through `row_of`), each row
-  // scaled so that its largest magnitude becomes 448, and the row scales
+  // e4m3 codes of a matrix [rows, cols] (rows through `row_of`): each row
+  // times 448 / max |row| (in FP32), and the row scales max |row| / 448
   auto put_e4m3 = [&](const float *src, size_t rows, size_t cols, const void **dst, const float **scale,
                       const std::vector<int> *row_of) {
     const size_t off = ar.add(rows * cols), soff = ar.add(rows * 4);
@@ -464,9 +464,9 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
       const float *sr = src + (size_t)(row_of ? (*row_of)[r] : (int)r) * cols;
       float amax = 0.f;
       for (size_t c = 0; c < cols; ++c) amax = std::max(amax, std::fabs(sr[c]));
-      const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-      sc[r] = s;
-      for (size_t c = 0; c < cols; ++c) d[r * cols + c] = f32_to_e4m3(sr[c] / s);
+      const float rc = amax > 0.f ? 448.0f / amax : 1.0f;
+      sc[r] = amax > 0.f ? amax / 448.0f : 1.0f;
+      for (size_t c = 0; c < cols; ++c) d[r * cols + c] = f32_to_e4m3(sr[c] * rc);
     }
     pend.push_back({dst, off});
     pend.push_back({(const void **)scale, soff});

@@ -289,14 +289,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 #pragma unroll
           for (int e = 0; e < 4; ++e) am = fmaxf(am, fabsf(y[c][e]));
         am = row16_max(am);
-        const float sc = am > 0.f ? am / 448.0f : 1.0f;
+        // codes of y 448 / amax, the row's scale amax / 448
+        const float rc = am > 0.f ? 448.0f / am : 1.0f, sc = am > 0.f ? am / 448.0f : 1.0f;
         const int r16 = rl & 15;
         uint8_t *grp = &sA8[(rl >> 4) * 16 * kWidth];
 #pragma unroll
         for (int c = 0; c < 6; ++c) {
           const int k = 64 * c + 4 * lj;
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[c][0] / sc, y[c][1] / sc, 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(y[c][2] / sc, y[c][3] / sc, w, true);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[c][0] * rc, y[c][1] * rc, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(y[c][2] * rc, y[c][3] * rc, w, true);
           const unsigned a3 =
               (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)&grp[16 * ((k >> 4) * 16 + r16) + (k & 15)];
           asm volatile("ds_write_b32 %0, %1" ::"v"(a3), "v"(w));
@@ -1310,10 +1311,13 @@ hipError_t launch_ln_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStrea
   if (a.M <= 0) return hipSuccess;
   if (a.N % 128 != 0 || a.K != kWidth || !a.ln_x) return hipErrorInvalidValue;
   const long nt = a.N / 128, tiles64 = ((a.M + 63) / 64) * nt;
-  // e4m3 products: every batch size, 64 x 128 tiles, all 6 weight stages up
-  // front (72 KB of LDS: two work-groups per CU)
+  // e4m3 products: every batch size, all 6 weight stages up front; 64 x 128
+  // tiles (72 KB of LDS: two work-groups per CU), or 64 x 256 when 128
+  // columns would need a second round and 256 fit the CUs in one
   if (a.w_scale != nullptr) {
     if (!bf16_mode || a.ln_gain == nullptr || (emode != E_STORE && emode != E_GEGLU)) return hipErrorInvalidValue;
+    if (emode == E_GEGLU && tiles64 > 256 && a.N % 256 == 0 && ((a.M + 63) / 64) * (a.N / 256) <= 256)
+      return gemm_dispatch<bf16, 64, 256, 6, true, 0, true, true>(emode, a, s);
     return gemm_dispatch<bf16, 64, 128, 6, true, 0, true, true>(emode, a, s);
   }
   // the GEMM alone would take 64-row tiles: normalize inside it

@@ -170,13 +170,16 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
 def quantize_rows_e4m3(m: np.ndarray) -> np.ndarray:
     """Per-row e4m3 quantization, returned dequantized (float64).
 
-    Each row, in float32, is divided by its scale s = max |row| / 448 (s = 1
-    for an all-zero row), rounded to e4m3, and multiplied back by s.
+    Each row, in float32, is multiplied by r = 448 / max |row| and rounded to
+    e4m3; the codes stand for code * s with the row's scale s = max |row| / 448
+    (r = s = 1 for an all-zero row).
     """
     m32 = np.asarray(m, dtype=np.float32)
     amax = np.max(np.abs(m32), axis=1)
-    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
-    q = e4m3_round(m32 / s[:, None])
+    safe = np.where(amax > 0, amax, np.float32(448.0)).astype(np.float32)
+    r = (np.float32(448.0) / safe).astype(np.float32)
+    s = (safe / np.float32(448.0)).astype(np.float32)
+    q = e4m3_round((m32 * r[:, None]).astype(np.float32))
     return q.astype(np.float64) * s.astype(np.float64)[:, None]
 
 
