@@ -17,7 +17,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjl.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "jl.h")
 
-FP32, BF16, FP8 = 0, 1, 2
+FP32, BF16, FP8 = 0, 1, 2  # jl_precision: FP32 products; bf16 operands; bf16 with e4m3 QKV and W_i products
 OK, ERR_ARG, ERR_OPTIONS, ERR_LENGTH, ERR_QTYPE, ERR_FILE, ERR_DEVICE, ERR_OOM, ERR_CAPACITY = (
     0, -1, -2, -3, -4, -5, -6, -7, -8)
 STATUS_NAMES = {0: "OK", -1: "ARG", -2: "OPTIONS", -3: "LENGTH", -4: "QTYPE", -5: "FILE",
