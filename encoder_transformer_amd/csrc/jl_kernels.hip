@@ -408,25 +408,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
     if constexpr (LNA) return load_frag(&sAk[((wm * MT + i) * KA + kt * KS + ks) * BLK + lane * FE]);
     else return load_frag(&cA[((wm * MT + i) * KS + ks) * BLK + lane * FE]);
   };
-  // e4m3 K-step kt: A codes from the resident tile, W codes from stage cB
-  auto compute8 = [&](const T *cB, int kt) {
-    const uint8_t *B8 = (const uint8_t *)cB;
+  // e4m3 products over 128 k (K-steps kt - 1 and kt, kt odd) on the
+  // 16x16x128 fp8 matrix-core product (unit block scales): lane (row lr,
+  // group g) supplies k = 32 g .. 32 g + 31 of the window, two 16-byte chunks
+  // of each operand; W's first half comes from stage buffer cP, the second
+  // from cB.  The product sums over k, so only the pairing of A and W codes
+  // matters, not their order.
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  typedef int i32x4v __attribute__((ext_vector_type(4)));
+  auto compute8 = [&](const T *cP, const T *cB, int kt) {
+    const int g = lane >> 4;
+    const uint8_t *B8 = (const uint8_t *)((g >> 1) ? cB : cP);
+    const int ca = (kt - 1) * 4 + 2 * g;  // first A chunk of the lane
+    const int cb = (g & 1) * 2;           // first W chunk inside the stage
+    i32x8 fa[MT], fb[NT];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kk = ks * 32 + lc;                 // k inside the stage
-      const int ka = kt * 64 + kk;                 // k inside the row
-      long fa[MT], fb[NT];
+    for (int i = 0; i < MT; ++i) {
+      const uint8_t *a = &sA8[(wm * MT + i) * 16 * kWidth + 16 * (ca * 16 + lr)];
+      const i32x4v lo = *reinterpret_cast<const i32x4v *>(a), hi = *reinterpret_cast<const i32x4v *>(a + 256);
+      fa[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        fa[i] = *reinterpret_cast<const long *>(&sA8[(wm * MT + i) * 16 * kWidth + 16 * ((ka >> 4) * 16 + lr) + (ka & 15)]);
+    for (int j = 0; j < NT; ++j) {
+      const uint8_t *b = &B8[(wn * NT + j) * 1024 + 16 * (cb * 16 + lr)];
+      const i32x4v lo = *reinterpret_cast<const i32x4v *>(b), hi = *reinterpret_cast<const i32x4v *>(b + 256);
+      fb[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        fb[j] = *reinterpret_cast<const long *>(&B8[(wn * NT + j) * 1024 + 16 * ((kk >> 4) * 16 + lr) + (kk & 15)]);
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
   };
   auto compute = [&](const T *cA, const T *cB, int kt) {
 #pragma unroll
@@ -551,8 +563,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
         using Next = std::integral_constant<int, (B + NS - 1) % NS>;
         if (kt > 0 && kt + NS - 1 < KT) issue_stage(kt + NS - 1, bufA(Next()), bufB(Next()));
       }
-      if constexpr (F8) compute8(bufB(Bc), kt);
-      else compute(bufA(Bc), bufB(Bc), kt);
+      if constexpr (F8) {
+        using Prev = std::integral_constant<int, (B + NS - 1) % NS>;
+        if (kt & 1) compute8(bufB(Prev()), bufB(Bc), kt);
+      } else {
+        compute(bufA(Bc), bufB(Bc), kt);
+      }
     };
     // loads older than every stage never hold up a stage wait (the
     // scheduling barrier keeps the scheduler from sinking them towards their
