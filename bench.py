@@ -226,6 +226,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--latency-only", action="store_true",
+                    help="time only the 1 x 1,024 call (graph replays; for a kernel trace of that workload)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (for HBM counter calibration)")
     args = ap.parse_args()
@@ -240,6 +242,13 @@ def main():
     path = synth.cached_weight_file()
     model = lib.Model(path, lib.BF16, max_tokens=300_000, max_markers=4096, device=0)
     model.set_graph_cache(8)  # steps replay captured graphs (profiled steps run eagerly)
+    if args.latency_only:
+        b1 = synth.make_batch(1)
+        t1, *_ = time_workload(model, b1, args.steps, args.warmup, sample=False)
+        print(json.dumps({"metric": "ms per call at 1x1024", "value": round(1e3 * t1 / args.steps, 4), "unit": "ms",
+                          "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}))
+        model.close()
+        return
 
     b2 = synth.make_batch(2)
     t, dom, dom_ms, dom_n, per_class, sampled = time_workload(model, b2, args.steps, args.warmup)
