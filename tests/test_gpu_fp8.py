@@ -54,3 +54,15 @@ def test_fp8_sequence_alone_equals_packed(models8):
     for b in range(batch.n_seqs):
         assert np.array_equal(run_logits(models8["fp8"], batch.subset([b])), packed[sl[b]]), b
 
+
+
+def test_fp8_multi_round_grids(models8, oracle_weights):
+    """4,288 tokens: the e4m3 products run 64 x 128 tiles over several rounds
+    of work-groups (two per CU), beyond the one-round grids of the cases above."""
+    from oracle import julia_oracle as jo
+    batch = synth.make_ragged_batch(300, 3, 1300, 1700)
+    assert ((int(batch.seq_offsets[-1]) + 63) // 64) * (2304 // 128) > 256
+    ref8 = jo.forward(oracle_weights, batch, fp8=True)
+    err = float(np.max(np.abs(run_logits(models8["fp8"], batch) - ref8)))
+    print("max |dlogit| against the e4m3 oracle", err)
+    assert err <= FP8_LOGIT_TIGHT
