@@ -125,6 +125,68 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 
+// Activation buffers of one forward pass (device memory), laid out by
+// layout_workspace:
+//   x [T, 384] FP32 residual stream (the head's h from the final LayerNorm on);
+//   qkv [T, 1152] (head layer 2: keys|values [T, 768]); o [T, 384] attention
+//   output, also the normalized GEMM operand u; act [T, 1536] GEGLU output /
+//   head FFN hidden; pos, tok_seq [T] int32; marker rows z, sh, zu [M, 384]
+//   FP32, qm, om [M, 384], actm [M, 1536] (element type).
+struct Workspace {
+  float *x = nullptr, *z = nullptr, *zu = nullptr, *sh = nullptr;
+  char *qkv = nullptr, *o = nullptr, *act = nullptr, *qm = nullptr, *om = nullptr, *actm = nullptr;
+  int *pos = nullptr, *tok_seq = nullptr;
+};
+
+// Metadata ints of one call for up to T tokens, Mm markers and Bm sequences:
+// offsets, marker counts, types and positions, and work lists of 8-int items
+// (attention items plus at most half as many empty ones, and 8 more).
+constexpr size_t meta_ints_for(size_t T, size_t Mm, size_t Bm) {
+  return 2 * (Bm + 1) + Bm + Mm + 12 * (T / 64 + Bm + 8) + 12 * (T / 128 + Bm + 8) + 8 * Bm + 64;
+}
+
+constexpr size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Bytes of layout_workspace's layout (same pieces, same order).
+constexpr size_t workspace_bytes(size_t T, size_t Mm, size_t es, size_t meta_ints, int n_meta) {
+  const size_t D = kWidth;
+  const size_t parts[12] = {T * D * 4,  T * 3 * D * es, T * D * es,  T * kHeadFfn * es,  T * 4,      T * 4,
+                            Mm * D * 4, Mm * D * es,    Mm * D * es, Mm * kHeadFfn * es, Mm * D * 4, Mm * D * 4};
+  size_t off = 0;
+  for (size_t p : parts) off = align256(off) + p;
+  for (int k = 0; k < n_meta; ++k) off = align256(off) + meta_ints * 4;
+  return align256(off);
+}
+
+// Carve a workspace for T tokens and Mm markers (element size es) and n_meta
+// metadata blocks of meta_ints ints out of `base` (256-byte aligned pieces);
+// with base == nullptr only the size is computed.  Returns the bytes used.
+size_t layout_workspace(char *base, size_t T, size_t Mm, size_t es, size_t meta_ints, Workspace *w, int **meta,
+                        int n_meta) {
+  const size_t D = kWidth;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    char *p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  w->x = (float *)take(T * D * 4);
+  w->qkv = take(T * 3 * D * es);
+  w->o = take(T * D * es);
+  w->act = take(T * kHeadFfn * es);
+  w->pos = (int *)take(T * 4);
+  w->tok_seq = (int *)take(T * 4);
+  w->z = (float *)take(Mm * D * 4);
+  w->qm = take(Mm * D * es);
+  w->om = take(Mm * D * es);
+  w->actm = take(Mm * kHeadFfn * es);
+  w->sh = (float *)take(Mm * D * 4);
+  w->zu = (float *)take(Mm * D * 4);
+  for (int k = 0; k < n_meta; ++k) meta[k] = (int *)take(meta_ints * 4);
+  return align256(off);  // == workspace_bytes(T, Mm, es, meta_ints, n_meta)
+}
+
 }  // namespace
 
 struct jl_model {
@@ -151,9 +213,7 @@ struct jl_model {
   const float *rope_cos[2] = {nullptr, nullptr}, *rope_sin[2] = {nullptr, nullptr};  // [0] local, [1] global
 
   // workspace
-  float *x = nullptr, *z = nullptr, *zu = nullptr, *sh = nullptr;
-  char *qkv = nullptr, *o = nullptr, *act = nullptr, *qm = nullptr, *om = nullptr, *actm = nullptr;
-  int *pos = nullptr, *tok_seq = nullptr;
+  Workspace w;
   // Batch metadata ring: call i uses slot i % kMetaSlots (pinned staging +
   // device copy); slot_done[k] is recorded after the last kernel that reads
   // slot k, so the host may run up to kMetaSlots - 1 calls ahead of the GPU.
@@ -179,6 +239,12 @@ struct jl_model {
   bool slot_pending[kMetaSlots] = {};
   int next_slot = 0;
   size_t meta_ints = 0;
+
+  // Host-side planning buffers, reserved at load for max_tokens / max_seqs
+  // so that planning a call allocates nothing: the longest-first sequence
+  // order and the attention items of each of the 8 XCDs.
+  std::vector<int> plan_order;
+  std::vector<AttnWork> plan_per[8];
 
   // per-kernel timer
   bool prof = false;
@@ -354,35 +420,16 @@ namespace {
 // Device workspace, metadata ring and pinned staging of a handle, sized by its
 // max_tokens / max_markers (and precision).  On failure the caller frees m.
 int alloc_workspace(jl_model *m) {
-  const uint32_t D = kWidth;
-  const size_t es = m->esize;
   const size_t T = (size_t)m->max_tokens, Mm = (size_t)m->max_markers, Bm = (size_t)m->max_seqs;
-  // work lists: items plus at most half as many empty ones (and 8 more)
-  m->meta_ints = 2 * (Bm + 1) + Bm + Mm + 12 * (T / 64 + Bm + 8) + 12 * (T / 128 + Bm + 8) + 8 * Bm + 64;
-  size_t off = 0;
-  std::vector<std::pair<void **, size_t>> slots;
-  auto reserve = [&](void **holder, size_t bytes) {
-    off = (off + 255) & ~size_t(255);
-    slots.push_back({holder, off});
-    off += bytes;
-  };
-  reserve((void **)&m->x, T * D * 4);
-  reserve((void **)&m->qkv, T * 3 * D * es);
-  reserve((void **)&m->o, T * D * es);
-  reserve((void **)&m->act, T * kHeadFfn * es);
-  reserve((void **)&m->pos, T * 4);
-  reserve((void **)&m->tok_seq, T * 4);
-  reserve((void **)&m->z, Mm * D * 4);
-  reserve((void **)&m->qm, Mm * D * es);
-  reserve((void **)&m->om, Mm * D * es);
-  reserve((void **)&m->actm, Mm * kHeadFfn * es);
-  reserve((void **)&m->sh, Mm * D * 4);
-  reserve((void **)&m->zu, Mm * D * 4);
-  for (int k = 0; k < jl_model::kMetaSlots; ++k) reserve((void **)&m->meta[k], m->meta_ints * 4);
-  reserve((void **)&m->gmeta, m->meta_ints * 4);
-  m->wsbytes = (off + 255) & ~size_t(255);
+  m->meta_ints = meta_ints_for(T, Mm, Bm);
+  int *meta[jl_model::kMetaSlots + 1];
+  m->wsbytes = layout_workspace(nullptr, T, Mm, m->esize, m->meta_ints, &m->w, meta, jl_model::kMetaSlots + 1);
   if (hipMalloc((void **)&m->ws, m->wsbytes) != hipSuccess) return fail(JL_ERR_OOM, "cannot allocate the device workspace");
-  for (auto &sl : slots) *sl.first = m->ws + sl.second;
+  layout_workspace(m->ws, T, Mm, m->esize, m->meta_ints, &m->w, meta, jl_model::kMetaSlots + 1);
+  for (int k = 0; k < jl_model::kMetaSlots; ++k) m->meta[k] = meta[k];
+  m->gmeta = meta[jl_model::kMetaSlots];
+  m->plan_order.reserve(Bm);
+  for (auto &v : m->plan_per) v.reserve(T / 64 + Bm + 8);
   for (int k = 0; k < jl_model::kMetaSlots; ++k) {
     if (hipHostMalloc((void **)&m->host_meta[k], m->meta_ints * 4, hipHostMallocDefault) != hipSuccess)
       return fail(JL_ERR_OOM, "cannot allocate pinned staging memory");
@@ -650,8 +697,8 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
 
 extern "C" int jl_share(const jl_model *src, int64_t max_tokens, int64_t max_markers, jl_model **out) {
   if (!src || !out) return fail(JL_ERR_ARG, "src and out must not be NULL");
-  if (max_tokens < 1 || max_tokens > ((int64_t)1 << 28)) return fail(JL_ERR_ARG, "max_tokens must be in 1..2^28");
-  if (max_markers < 2 || max_markers > ((int64_t)1 << 24)) return fail(JL_ERR_ARG, "max_markers must be in 2..2^24");
+  if (max_tokens < 1 || max_tokens > (int64_t)1 << 26) return fail(JL_ERR_ARG, "max_tokens must be in 1..2^26");
+  if (max_markers < 2 || max_markers > max_tokens) return fail(JL_ERR_ARG, "max_markers must be in 2..max_tokens");
   DeviceGuard dg(src->device);
   jl_model *m = new jl_model();
   m->device = src->device;
@@ -724,6 +771,7 @@ struct Plan {
 };
 
 // Build the metadata in pinned memory and enqueue its upload.
+// Allocates nothing: the host-side vectors are the handle's, reserved at load.
 int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, int32_t M, const int32_t *qt,
                 hipStream_t s, Plan &pl, bool to_graph_buffer = false) {
   pl.B = B;
@@ -736,6 +784,21 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
     m->slot_pending[slot] = false;
   }
   pl.slot = slot;
+  // Size of what follows, checked before anything is written: offsets,
+  // marker counts, types and positions, then three lists of 8-int items --
+  // 64- and 128-query attention items (each list at most half again its
+  // item count plus 8 of empty padding) and one marker item per sequence.
+  {
+    size_t items64 = 0, items128 = 0;
+    for (int b = 0; b < B; ++b) {
+      const size_t len = (size_t)(so[b + 1] - so[b]);
+      items64 += (len + 63) / 64;
+      items128 += (len + 127) / 128;
+    }
+    const size_t need = (((size_t)(B + 1) * 2 + B + M + 7) & ~size_t(7)) + 8 * (items64 + items64 / 2 + 8) +
+                        8 * (items128 + items128 / 2 + 8) + 8 * (size_t)B;
+    if (need > m->meta_ints) return fail(JL_ERR_CAPACITY, "batch metadata exceeds the staging buffer");
+  }
   int *h = m->host_meta[slot];
   int *dmeta = to_graph_buffer ? m->gmeta : m->meta[slot];
   size_t o = 0;
@@ -755,10 +818,13 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
   for (int k = 0; k < M; ++k) h[o++] = mp[k];
   o = (o + 7) & ~size_t(7);
   // encoder / head-layer-1 work items, longest sequences first
-  std::vector<int> order(B);
+  std::vector<int> &order = m->plan_order;  // capacity max_seqs >= B (reserved at load)
+  order.resize(B);
   for (int b = 0; b < B; ++b) order[b] = b;
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int a, int b) { return so[a + 1] - so[a] > so[b + 1] - so[b]; });
+  std::sort(order.begin(), order.end(), [&](int a, int b) {  // stable: equal lengths keep their order
+    const int la = so[a + 1] - so[a], lb = so[b + 1] - so[b];
+    return la > lb || (la == lb && a < b);
+  });
   // Work-groups go to the 8 XCDs round-robin by flattened index, and the
   // grid's x extent is a multiple of 8, so item x runs on XCD x % 8 for every
   // head.  Items are laid out per XCD: sequences, longest first, go whole to
@@ -779,7 +845,8 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
       n_items += (len + tile - 1) / tile;
       total += ((len + tile - 1) / tile) * cost_of(len);
     }
-    std::vector<AttnWork> per[8];
+    std::vector<AttnWork> *per = m->plan_per;  // each reserved for every item of a batch
+    for (int c = 0; c < 8; ++c) per[c].clear();
     double load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const double cap = total / 8.0;
     auto least = [&]() {
@@ -802,7 +869,7 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
       }
     }
     size_t kmax = 0;
-    for (auto &v : per) kmax = std::max(kmax, v.size());
+    for (int c = 0; c < 8; ++c) kmax = std::max(kmax, per[c].size());
     count = 0;
     if (8 * kmax <= (size_t)n_items + n_items / 2 + 8) {
       for (size_t k = 0; k < kmax; ++k)
@@ -836,7 +903,6 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
     std::memcpy(h + o, &w, sizeof(w));
     o += 8;
   }
-  if (o > m->meta_ints) return fail(JL_ERR_CAPACITY, "batch metadata exceeds the staging buffer");
   JL_HIP(hipMemcpyAsync(dmeta, h, o * 4, hipMemcpyHostToDevice, s));
   pl.n_work = nw;
   pl.n_work_wide = nw_wide;
@@ -942,11 +1008,12 @@ GemmArgs gemm(const void *A, int lda, const void *W, int ldw, const float *bias,
 //   u   normalized GEMM operand [T, 384] (shares the attention-output buffer o)
 //   qkv [T, 1152]; head layer 2 keeps keys|values there as [T, 768]
 //   act [T, 1152] GEGLU output / [T, 1536] head FFN hidden
-int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float *out, hipStream_t s) {
+int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan &pl, int stop, float *out,
+                hipStream_t s) {
   const bool bf = m->bf16;
   const size_t es = m->esize;
   const int T = pl.T, M = pl.M, D = kWidth;
-  char *u = m->o;
+  char *u = w.o;
   auto copy_out = [&](const float *src, size_t rows) -> int {
     JL_HIP(hipMemcpyAsync(out, src, rows * D * 4, hipMemcpyDeviceToDevice, s));
     return JL_OK;
@@ -959,27 +1026,27 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     ea.gain = m->emb_norm;
     ea.seq_offsets = pl.d_so;
     ea.n_seqs = pl.B;
-    ea.x = m->x;
-    ea.pos = m->pos;
-    ea.tok_seq = m->tok_seq;
+    ea.x = w.x;
+    ea.pos = w.pos;
+    ea.tok_seq = w.tok_seq;
     ea.Wqkv = (const __bf16 *)m->L[0].pWqkv;
     ea.rope_cos = m->rope_cos[layer_is_global(0)];
     ea.rope_sin = m->rope_sin[layer_is_global(0)];
-    ea.qkv_out = (__bf16 *)m->qkv;
+    ea.qkv_out = (__bf16 *)w.qkv;
     ea.T = T;
     JL_LAUNCH(JL_K_EMBED, launch_embed_qkv(ea, s));
   } else {
-    JL_LAUNCH(JL_K_EMBED, launch_embed(ids, m->emb, m->emb_norm, T, pl.d_so, pl.B, m->x, m->pos, m->tok_seq, s));
+    JL_LAUNCH(JL_K_EMBED, launch_embed(ids, m->emb, m->emb_norm, T, pl.d_so, pl.B, w.x, w.pos, w.tok_seq, s));
   }
-  if (stop == 0) return copy_out(m->x, T);
+  if (stop == 0) return copy_out(w.x, T);
 
   AttnArgs at{};
-  at.q = m->qkv;
+  at.q = w.qkv;
   at.q_stride = 3 * D;
-  at.k = m->qkv + D * es;
-  at.v = m->qkv + 2 * D * es;
+  at.k = w.qkv + D * es;
+  at.v = w.qkv + 2 * D * es;
   at.kv_stride = 3 * D;
-  at.o = m->o;
+  at.o = w.o;
   at.o_stride = D;
   at.work = pl.d_aw;
   if (row_block) {
@@ -990,14 +1057,14 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
       JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, attention(bf, at, pl, glob, s));
       LayerArgs la{};
       const LayerW &W = m->L[l];
-      la.x = m->x;
-      la.o = (const __bf16 *)m->o;
+      la.x = w.x;
+      la.o = (const __bf16 *)w.o;
       la.Wo = (const __bf16 *)W.pWo;
       la.mlp_norm = W.mlp_norm;
       la.Wi = (const __bf16 *)W.pWi;
       la.Wout = (const __bf16 *)W.pWout;
-      la.pos = m->pos;
-      la.qkv_out = (__bf16 *)m->qkv;
+      la.pos = w.pos;
+      la.qkv_out = (__bf16 *)w.qkv;
       la.T = T;
       if (l + 1 < kLayers && stop != l + 1) {
         const LayerW &N = m->L[l + 1];
@@ -1009,7 +1076,7 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
         la.final_norm = m->final_norm;
         la.type_rows = m->type_rows;
         la.qtype = pl.d_qt;
-        la.tok_seq = m->tok_seq;
+        la.tok_seq = w.tok_seq;
         if (stop != kLayers + 1) {  // continue into the head's first attention input
           const HeadW &H = m->H[0];
           la.attn_norm_next = H.n1_w;
@@ -1019,46 +1086,46 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
         }
       }
       JL_LAUNCH(JL_K_LAYER, launch_layer(la, s));
-      if (stop == l + 1) return copy_out(m->x, T);
+      if (stop == l + 1) return copy_out(w.x, T);
     }
   } else {
   for (int l = 0; l < kLayers; ++l) {
     const LayerW &W = m->L[l];
     const bool glob = layer_is_global(l);
-    GemmArgs q = with_ln(gemm(u, D, W.Wqkv8 ? W.Wqkv8 : W.Wqkv, D, nullptr, m->qkv, 3 * D, T, 3 * D, D), m->x,
+    GemmArgs q = with_ln(gemm(u, D, W.Wqkv8 ? W.Wqkv8 : W.Wqkv, D, nullptr, w.qkv, 3 * D, T, 3 * D, D), w.x,
                          W.attn_norm, nullptr);
     q.w_scale = W.sqkv;  // e4m3 products (JL_FP8), else nullptr
     q.rope_cos = m->rope_cos[glob];
     q.rope_sin = m->rope_sin[glob];
-    q.pos = m->pos;
+    q.pos = w.pos;
     q.rope_cols = 2 * D;
     JL_LAUNCH(JL_K_QKV, launch_ln_gemm(bf, E_STORE, q, s));
     at.half_window = glob ? -1 : kHalfWindow;
     JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, attention(bf, at, pl, glob, s));
-    JL_LAUNCH(JL_K_OUTPROJ, launch_gemm(bf, E_RESID, gemm(m->o, D, W.Wo, D, nullptr, m->x, D, T, D, D), s));
-    GemmArgs wi = with_ln(gemm(u, D, W.Wi8 ? W.Wi8 : W.Wi, D, nullptr, m->act, kGeglu, T, 2 * kGeglu, D), m->x,
+    JL_LAUNCH(JL_K_OUTPROJ, launch_gemm(bf, E_RESID, gemm(w.o, D, W.Wo, D, nullptr, w.x, D, T, D, D), s));
+    GemmArgs wi = with_ln(gemm(u, D, W.Wi8 ? W.Wi8 : W.Wi, D, nullptr, w.act, kGeglu, T, 2 * kGeglu, D), w.x,
                           W.mlp_norm, nullptr);
     wi.w_scale = W.si;
     JL_LAUNCH(JL_K_MLP_IN, launch_ln_gemm(bf, E_GEGLU, wi, s));
     JL_LAUNCH(JL_K_MLP_OUT,
-              launch_gemm(bf, E_RESID, gemm(m->act, kGeglu, W.Wout, kGeglu, nullptr, m->x, D, T, D, kGeglu), s));
-    if (stop == l + 1) return copy_out(m->x, T);
+              launch_gemm(bf, E_RESID, gemm(w.act, kGeglu, W.Wout, kGeglu, nullptr, w.x, D, T, D, kGeglu), s));
+    if (stop == l + 1) return copy_out(w.x, T);
   }
   // head input: final LayerNorm + type row (in place)
-  JL_LAUNCH(JL_K_MISC, launch_final_ln_type(m->x, m->final_norm, m->type_rows, pl.d_qt, m->tok_seq, T, m->x, s));
+  JL_LAUNCH(JL_K_MISC, launch_final_ln_type(w.x, m->final_norm, m->type_rows, pl.d_qt, w.tok_seq, T, w.x, s));
   }
-  if (stop == 23) return copy_out(m->x, T);
+  if (stop == 23) return copy_out(w.x, T);
 
   // head layer 1 over every token (row-block path: its LayerNorm and
   // in-projection ran in the last encoder layer's kernel; everything after
   // its attention, with the second layer's keys and values, in one kernel)
-  char *kv = m->qkv;  // head layer 2's keys and values, [T, 768]: k then v
+  char *kv = w.qkv;  // head layer 2's keys and values, [T, 768]: k then v
   {
     const HeadW &H = m->H[0];
     if (!row_block) {
       JL_LAUNCH(JL_K_HEAD_GEMM,
                 launch_ln_gemm(bf, E_STORE,
-                               with_ln(gemm(u, D, H.in_w, D, H.in_b, m->qkv, 3 * D, T, 3 * D, D), m->x, H.n1_w, H.n1_b),
+                               with_ln(gemm(u, D, H.in_w, D, H.in_b, w.qkv, 3 * D, T, 3 * D, D), w.x, H.n1_w, H.n1_b),
                                s));
     }
     at.half_window = -1;
@@ -1066,8 +1133,8 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
     if (row_block) {
       const HeadW &N = m->H[1];
       HeadArgs ha{};
-      ha.x = m->x;
-      ha.o = (const __bf16 *)m->o;
+      ha.x = w.x;
+      ha.o = (const __bf16 *)w.o;
       ha.Wo = (const __bf16 *)H.pOut;
       ha.bo = H.out_b;
       ha.n2_w = H.n2_w;
@@ -1086,18 +1153,18 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
       ha.T = T;
       JL_LAUNCH(JL_K_HEAD_LAYER, launch_head_layer(ha, s));
     } else {
-      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->o, D, H.out_w, D, H.out_b, m->x, D, T, D, D), s));
+      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(w.o, D, H.out_w, D, H.out_b, w.x, D, T, D, D), s));
       JL_LAUNCH(JL_K_HEAD_GEMM,
                 launch_ln_gemm(bf, E_RELU,
-                               with_ln(gemm(u, D, H.l1_w, D, H.l1_b, m->act, kHeadFfn, T, kHeadFfn, D), m->x, H.n2_w,
+                               with_ln(gemm(u, D, H.l1_w, D, H.l1_b, w.act, kHeadFfn, T, kHeadFfn, D), w.x, H.n2_w,
                                        H.n2_b),
                                s));
       JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID,
-                                            gemm(m->act, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, m->x, D, T, D, kHeadFfn),
+                                            gemm(w.act, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, w.x, D, T, D, kHeadFfn),
                                             s));
     }
   }
-  if (stop == 24) return copy_out(m->x, T);
+  if (stop == 24) return copy_out(w.x, T);
 
   // head layer 2: keys and values for every token, the rest at marker rows only
   {
@@ -1107,41 +1174,41 @@ int run_forward(jl_model *m, const int32_t *ids, const Plan &pl, int stop, float
                 launch_ln_gemm(bf, E_STORE,
                                with_ln(gemm(u, D, (const char *)H.in_w + (size_t)D * D * es, D, H.in_b + D, kv, 2 * D,
                                             T, 2 * D, D),
-                                       m->x, H.n1_w, H.n1_b),
+                                       w.x, H.n1_w, H.n1_b),
                                s));
     }
-    JL_LAUNCH(JL_K_MISC, launch_gather_rows(m->x, pl.d_mp, M, m->z, s));
-    char *um = m->om;  // normalized marker rows, then the marker attention output
+    JL_LAUNCH(JL_K_MISC, launch_gather_rows(w.x, pl.d_mp, M, w.z, s));
+    char *um = w.om;  // normalized marker rows, then the marker attention output
     JL_LAUNCH(JL_K_HEAD_GEMM,
-              launch_ln_gemm(bf, E_STORE, with_ln(gemm(um, D, H.in_w, D, H.in_b, m->qm, D, M, D, D), m->z, H.n1_w, H.n1_b),
+              launch_ln_gemm(bf, E_STORE, with_ln(gemm(um, D, H.in_w, D, H.in_b, w.qm, D, M, D, D), w.z, H.n1_w, H.n1_b),
                              s));
     AttnArgs mk{};
-    mk.q = m->qm;
+    mk.q = w.qm;
     mk.q_stride = D;
     mk.k = kv;
     mk.v = kv + D * es;
     mk.kv_stride = 2 * D;
-    mk.o = m->om;
+    mk.o = w.om;
     mk.o_stride = D;
     mk.work = pl.d_mw;
     mk.half_window = -1;
     JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, mk, pl.B, 64, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(m->om, D, H.out_w, D, H.out_b, m->z, D, M, D, D), s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(w.om, D, H.out_w, D, H.out_b, w.z, D, M, D, D), s));
     JL_LAUNCH(JL_K_HEAD_GEMM,
               launch_ln_gemm(bf, E_RELU,
-                             with_ln(gemm(um, D, H.l1_w, D, H.l1_b, m->actm, kHeadFfn, M, kHeadFfn, D), m->z, H.n2_w,
+                             with_ln(gemm(um, D, H.l1_w, D, H.l1_b, w.actm, kHeadFfn, M, kHeadFfn, D), w.z, H.n2_w,
                                      H.n2_b),
                              s));
     JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID,
-                                          gemm(m->actm, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, m->z, D, M, D, kHeadFfn),
+                                          gemm(w.actm, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, w.z, D, M, D, kHeadFfn),
                                           s));
   }
-  if (stop == 25) return copy_out(m->z, M);
+  if (stop == 25) return copy_out(w.z, M);
 
   // scorer (FP32 in both modes)
-  JL_LAUNCH(JL_K_MISC, launch_ln_rows(false, m->z, m->sc_nw, m->sc_nb, M, m->zu, s));
-  JL_LAUNCH(JL_K_MISC, launch_gemm(bf, E_GELU_F32, gemm(m->zu, D, m->sc_w1, D, m->sc_b1, m->sh, D, M, D, D), s));
-  JL_LAUNCH(JL_K_MISC, launch_score_dot(m->sh, m->sc_w2, m->sc_b2, M, out, s));
+  JL_LAUNCH(JL_K_MISC, launch_ln_rows(false, w.z, m->sc_nw, m->sc_nb, M, w.zu, s));
+  JL_LAUNCH(JL_K_MISC, launch_gemm(bf, E_GELU_F32, gemm(w.zu, D, m->sc_w1, D, m->sc_b1, w.sh, D, M, D, D), s));
+  JL_LAUNCH(JL_K_MISC, launch_score_dot(w.sh, m->sc_w2, m->sc_b2, M, out, s));
   return JL_OK;
 }
 
@@ -1165,7 +1232,7 @@ int forward_graph(jl_model *m, const int32_t *ids, const Plan &pl, float *out, h
       m->graphs.erase(m->graphs.begin() + lru);
     }
     JL_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-    const int rc = run_forward(m, ids, pl, 26, out, s);
+    const int rc = run_forward(m, m->w, ids, pl, 26, out, s);
     hipGraph_t g = nullptr;
     const hipError_t e = hipStreamEndCapture(s, &g);
     if (rc != JL_OK) {
@@ -1218,7 +1285,7 @@ extern "C" int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *se
   // graphs need a capturable stream and no per-launch timer events
   const bool use_graph = m->graph_cap > 0 && s != nullptr && !m->prof;
   if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl, use_graph)) return rc;
-  if (!use_graph) return finish_plan(m, pl, s, run_forward(m, ids_dev, pl, 26, logits_dev, s));
+  if (!use_graph) return finish_plan(m, pl, s, run_forward(m, m->w, ids_dev, pl, 26, logits_dev, s));
   return finish_plan(m, pl, s, forward_graph(m, ids_dev, pl, logits_dev, s));
 }
 
@@ -1235,7 +1302,7 @@ extern "C" int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_
   hipStream_t s = (hipStream_t)stream;
   Plan pl;
   if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl)) return rc;
-  return finish_plan(m, pl, s, run_forward(m, ids_dev, pl, stage, out_dev, s));
+  return finish_plan(m, pl, s, run_forward(m, m->w, ids_dev, pl, stage, out_dev, s));
 }
 
 extern "C" int jl_probs(jl_model *m, const float *logits_dev, const int32_t *seq_offsets, int32_t n_seqs,

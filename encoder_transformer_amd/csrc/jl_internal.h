@@ -179,6 +179,15 @@ namespace jl {
 struct ServeState;
 void free_serve_state(ServeState *st);
 ServeState *&model_serve_state(jl_model *m);
+// The handle's host-call buffers (made with its serving state on first use,
+// kept until jl_free): device ids [max_tokens] and outputs [2 max_markers +
+// 2 max_seqs] floats, with pinned host copies of each.
+struct HandleBuffers {
+  int32_t *d_ids, *h_ids;
+  float *d_out, *h_out;
+  int64_t max_tokens, max_markers;
+};
+int handle_buffers(jl_model *m, HandleBuffers *out);
 int model_device(const jl_model *m);
 int64_t model_max_tokens(const jl_model *m);
 int64_t model_max_markers(const jl_model *m);

@@ -192,19 +192,15 @@ int route(Scorer score, void *user, int64_t max_tokens, int64_t max_markers, con
   return JL_OK;
 }
 
-// The model as a scorer: ids to the device, jl_forward + jl_probs, probabilities back.
+// The model as a scorer: ids to the device, jl_forward + jl_probs, probabilities
+// back.  The ids and probabilities pass through the handle's pinned staging
+// and device buffers (jl_serve's, made on the handle's first host-side call
+// and kept until jl_free), so routing allocates nothing per call.
 struct ModelScorer {
   jl_model *m;
   hipStream_t s;
   int device;
-  int32_t *ids_dev = nullptr;
-  float *logits_dev = nullptr, *probs_dev = nullptr;
-  size_t cap_tokens = 0, cap_markers = 0;
-  ~ModelScorer() {
-    if (ids_dev) (void)hipFree(ids_dev);
-    if (logits_dev) (void)hipFree(logits_dev);
-    if (probs_dev) (void)hipFree(probs_dev);
-  }
+  jl::HandleBuffers hb;
   static int call(void *self, const int32_t *ids, const int32_t *so, int32_t n_seqs, const int32_t *mp, int32_t M,
                   float *probs) {
     auto &ms = *static_cast<ModelScorer *>(self);
@@ -217,33 +213,22 @@ struct ModelScorer {
     return rc;
   }
   int score(const int32_t *ids, const int32_t *so, int32_t n_seqs, const int32_t *mp, int32_t M, float *probs) {
-    auto &ms = *this;
     const size_t T = (size_t)so[n_seqs];
-    if (T > ms.cap_tokens) {
-      if (ms.ids_dev) (void)hipFree(ms.ids_dev);
-      ms.ids_dev = nullptr;
-      if (hipMalloc(&ms.ids_dev, T * sizeof(int32_t)) != hipSuccess) return jl::set_error(JL_ERR_OOM, "router ids");
-      ms.cap_tokens = T;
-    }
-    if ((size_t)M > ms.cap_markers) {
-      if (ms.logits_dev) (void)hipFree(ms.logits_dev);
-      if (ms.probs_dev) (void)hipFree(ms.probs_dev);
-      ms.logits_dev = ms.probs_dev = nullptr;
-      if (hipMalloc(&ms.logits_dev, M * sizeof(float)) != hipSuccess ||
-          hipMalloc(&ms.probs_dev, M * sizeof(float)) != hipSuccess)
-        return jl::set_error(JL_ERR_OOM, "router outputs");
-      ms.cap_markers = M;
-    }
+    // the router cuts its batches to the handle's capacity
+    if ((int64_t)T > hb.max_tokens || M > hb.max_markers)
+      return jl::set_error(JL_ERR_CAPACITY, "router batch exceeds the handle's capacity");
     std::vector<int32_t> qt(n_seqs, JL_CHOICE);
-    if (hipMemcpyAsync(ms.ids_dev, ids, T * sizeof(int32_t), hipMemcpyHostToDevice, ms.s) != hipSuccess)
+    float *logits_dev = hb.d_out, *probs_dev = hb.d_out + hb.max_markers;
+    std::memcpy(hb.h_ids, ids, T * sizeof(int32_t));
+    if (hipMemcpyAsync(hb.d_ids, hb.h_ids, T * sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess)
       return jl::set_error(JL_ERR_DEVICE, "router ids upload");
-    if (int rc = jl_forward(ms.m, ms.ids_dev, so, n_seqs, mp, M, qt.data(), ms.logits_dev, ms.s)) return rc;
-    if (int rc = jl_probs(ms.m, ms.logits_dev, so, n_seqs, mp, M, qt.data(), ms.probs_dev, nullptr, nullptr, nullptr,
-                          ms.s))
+    if (int rc = jl_forward(m, hb.d_ids, so, n_seqs, mp, M, qt.data(), logits_dev, s)) return rc;
+    if (int rc = jl_probs(m, logits_dev, so, n_seqs, mp, M, qt.data(), probs_dev, nullptr, nullptr, nullptr, s))
       return rc;
-    if (hipMemcpyAsync(probs, ms.probs_dev, M * sizeof(float), hipMemcpyDeviceToHost, ms.s) != hipSuccess ||
-        hipStreamSynchronize(ms.s) != hipSuccess)
+    if (hipMemcpyAsync(hb.h_out, probs_dev, M * sizeof(float), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
       return jl::set_error(JL_ERR_DEVICE, "router probabilities download");
+    std::memcpy(probs, hb.h_out, M * sizeof(float));
     return JL_OK;
   }
 };
@@ -273,7 +258,8 @@ extern "C" int jl_route(jl_model *m, int32_t n_questions, const int32_t *prefix_
   if (!m) return jl::set_error(JL_ERR_ARG, "model handle is NULL");
   int64_t info[4];
   if (int rc = jl_model_info(m, info, 4)) return rc;
-  ModelScorer ms{m, (hipStream_t)stream, (int)info[3]};
+  ModelScorer ms{m, (hipStream_t)stream, (int)info[3], {}};
+  if (int rc = jl::handle_buffers(m, &ms.hb)) return rc;
   const Inputs in{n_questions, prefix_ids, suffix_ids, option_ids, prefix_offsets, suffix_offsets,
                   option_offsets, question_options, mask_id};
   return route(&ModelScorer::call, &ms, info[1], info[2], in, pick, pick_prob, n_final, final_idx, final_prob,

@@ -101,6 +101,14 @@ ServeState *serve_state(jl_model *m, int *rc) {
 
 }  // namespace
 
+int jl::handle_buffers(jl_model *m, HandleBuffers *out) {
+  int rc = JL_OK;
+  ServeState *st = serve_state(m, &rc);
+  if (!st) return rc;
+  *out = HandleBuffers{st->d_ids, st->h_ids, st->d_out, st->h_out, st->max_tokens, st->max_markers};
+  return JL_OK;
+}
+
 extern "C" int jl_serve_plan(int32_t n_requests, const int64_t *id_offsets, const int64_t *mask_offsets,
                              int64_t max_batch_tokens, int64_t max_batch_markers, int64_t max_batch_seqs,
                              int32_t *order, int32_t *batch_of, int32_t *n_batches) {

@@ -77,8 +77,16 @@ enum jl_qtype { JL_CHOICE = 0, JL_SCORE = 1, JL_NOUL = 2 };
  * with tensor names, shapes, offsets and per-tensor checksums, then FP32
  * data) onto `device`, convert it for `precision` and size a workspace for
  * batches of up to `max_tokens` packed tokens and `max_markers` options.
- * Checks every tensor's presence, shape and checksum.  On success *out holds
- * a new handle that the caller releases with jl_free.
+ * The tensors are those of the model the explainer page lays out ("Julia-1:
+ * one score per mask token ...", The decision head: the mmBERT-small encoder,
+ * the type table, two transformer layers with a 1,536-wide feed-forward and
+ * the LayerNorm -> Linear -> GELU -> Linear scorer); the 256,000 x 384
+ * embedding table stays resident in FP32, as do the norms and the head
+ * ("Julia-1 MLX", Performance).  Checks every tensor's presence, shape and
+ * checksum.  path: NUL-terminated, read during the call.  max_tokens in
+ * 1..2^26, max_markers in 2..max_tokens.  On success *out holds a new handle
+ * that the caller releases with jl_free; on error *out is NULL and nothing
+ * stays allocated.  Errors: JL_ERR_ARG, JL_ERR_FILE, JL_ERR_DEVICE, JL_ERR_OOM.
  */
 int jl_load_weights(const char *path, int precision, int64_t max_tokens,
                     int64_t max_markers, int device, jl_model **out);
@@ -88,6 +96,12 @@ void jl_free(jl_model *m);
 
 /*
  * Host-only check of a packed batch; jl_forward and jl_probs call it first.
+ * The limits are the pages' problem statement: each question carries 2 to
+ * 20 options ("Julia-1: one score per mask token ...", Three modes through
+ * one head; more go through the Router), a noul question exactly the two
+ * options [false, true] (same section), and a sequence holds at most 8,192
+ * tokens ("Julia-1 MLX", Performance); an over-long input is refused, never
+ * truncated ("Julia-1 MLX", Quick start).
  *   seq_offsets  [n_seqs+1] cumulative lengths: seq_offsets[0] = 0, strictly
  *                increasing, every length in [1, 8192], total <= max_tokens.
  *   mask_positions [n_markers] absolute packed indices of the <mask> markers,
@@ -103,9 +117,15 @@ int jl_validate(const int32_t *seq_offsets, int32_t n_seqs,
 
 /*
  * Option logits of a packed batch: logits_dev[k] is the score of marker k
- * (FP32, [n_markers]).  ids_dev: int32 token ids [seq_offsets[n_seqs]] on the
- * device; an id outside [0, 256000) makes its whole sequence's logits NaN.
- * Sequences never attend to each other.  Ragged lengths need no padding.
+ * (FP32, [n_markers]), the scorer's output at the hidden state of the k-th
+ * <mask> marker after the encoder, the type row and the two head layers
+ * ("Julia-1: one score per mask token ...", From a state to one decision;
+ * The decision head).  ids_dev: int32 token ids [seq_offsets[n_seqs]] on the
+ * device, caller-owned; an id outside [0, 256000) makes its whole sequence's
+ * logits NaN.  Sequences never attend to each other; ragged lengths need no
+ * padding ("julia1 - Rust runtime for Julia-1", Why it is faster: unpadded
+ * batches).  The other arguments are as jl_validate checks them; errors are
+ * jl_validate's, JL_ERR_ARG for NULL device pointers and JL_ERR_DEVICE.
  */
 int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets,
                int32_t n_seqs, const int32_t *mask_positions, int32_t n_markers,
