@@ -44,6 +44,7 @@ TYPE_WORDS = {0: (1_001, 1_010, 1_003), 1: (1_011, 1_010, 1_003), 2: (1_021, 1_0
 
 CHOICE, SCORE, NOUL = 0, 1, 2
 INIT_STD = 0.02
+WIDE_STD = 0.05   # the "wide" weight set of the parity tests (see make_weights)
 WEIGHT_SEED = 0
 
 
@@ -96,11 +97,14 @@ def weight_spec(vocab: int = VOCAB) -> List[Tuple[str, Tuple[int, ...], str]]:
 
 
 def make_weights(seed: int = WEIGHT_SEED, norm_jitter: bool = False,
-                 vocab: int = VOCAB) -> Dict[str, np.ndarray]:
+                 vocab: int = VOCAB, std: float = INIT_STD) -> Dict[str, np.ndarray]:
     """Draw all weights with NumPy PCG64 (`default_rng(seed)`), float32.
 
     One `standard_normal` call per "normal" tensor, in `weight_spec` order,
-    scaled by 0.02. With ``norm_jitter`` the LayerNorm gains become
+    scaled by ``std`` (0.02, the published init). A larger ``std`` (the
+    "wide" weight set, 0.05) makes attention peaked and spreads the option
+    logits to order one, so that a wrong window, rotation or head step moves
+    the logits far more than bf16 rounding does. With ``norm_jitter`` the LayerNorm gains become
     1 + N(0, 0.1^2) and the shifts N(0, 0.1^2), drawn after all other tensors,
     so that the gain and shift paths are exercised (the published init leaves
     them at 1 and 0, where a wrong gain index would go unnoticed).
@@ -111,7 +115,7 @@ def make_weights(seed: int = WEIGHT_SEED, norm_jitter: bool = False,
     for name, shape, kind in weight_spec(vocab):
         if kind == "normal":
             a = rng.standard_normal(shape, dtype=np.float32)
-            a *= np.float32(INIT_STD)
+            a *= np.float32(std)
         elif kind == "ones":
             a = np.ones(shape, np.float32)
         else:
@@ -181,12 +185,13 @@ def write_weight_file(path: str, weights: Dict[str, np.ndarray]) -> None:
 
 def cached_weight_file(seed: int = WEIGHT_SEED, norm_jitter: bool = False,
                        directory: Optional[str] = None,
-                       weights: Optional[Dict[str, np.ndarray]] = None) -> str:
-    """Path of the weight file for ``seed``, written once per directory."""
+                       weights: Optional[Dict[str, np.ndarray]] = None, std: float = INIT_STD) -> str:
+    """Path of the weight file for (``seed``, ``norm_jitter``, ``std``), written once per directory."""
     directory = directory or os.environ.get("JL_WEIGHT_DIR") or "/tmp"
-    path = os.path.join(directory, "jl_weights_s%d%s.bin" % (seed, "_jit" if norm_jitter else ""))
+    tag = "" if std == INIT_STD else "_std%g" % std
+    path = os.path.join(directory, "jl_weights_s%d%s%s.bin" % (seed, "_jit" if norm_jitter else "", tag))
     if not os.path.exists(path):
-        write_weight_file(path, weights if weights is not None else make_weights(seed, norm_jitter))
+        write_weight_file(path, weights if weights is not None else make_weights(seed, norm_jitter, std=std))
     return path
 
 

@@ -1,36 +1,34 @@
 """GPU parity of the HIP forward pass against the CPU oracle (needs an MI355X).
 
 All calls go through the C ABI (libjl.so) via the ctypes binding.
-* stage parity: hidden states after the embedding, each encoder layer, the
-  head input and both head layers, both precisions, jittered LayerNorm gains;
+* stage parity: hidden states after encoder layers, the head input and both
+  head layers, both precisions and both bf16 schedules, on two weight sets
+  with jittered LayerNorm gains (std 0.02 and 0.05), at per-stage bounds;
 * logits: configurations 0 and 1 against the live oracle, configurations 2-4
   (full batches, the benchmark's launch shapes) against stored oracle logits
-  of sampled sequences (tests/golden/make_oracle_expected.py);
+  of sampled sequences (tests/golden/make_oracle_expected.py) at the tight
+  bounds; the wide weight set (std 0.05, logits of order one) on every
+  configuration, with argmax agreement over the 256-question mix;
+* long sequences: hidden rows at positions up to 8,191 of the 16 x 8,192
+  batch against stored oracle rows, both precisions and both bf16 schedules;
 * read-offs: jl_probs against the oracle's read-offs;
 * invariances: batch composition, sequence order, run-to-run determinism;
 * edge cases: empty batch, 2-token sequences, ragged tails, bad ids, errors.
 """
+import os
+
 import numpy as np
 import pytest
 
 from encoder_transformer_amd import synth
 
-from gpu_common import (BF16_ARGMAX_AGREEMENT, BF16_LOGIT_BOUND, BF16_PROB_BOUND, FP32_LOGIT_BOUND,
-                        MAX_MARKERS, MAX_TOKENS, argmax_report, device_ids, golden, golden_for,
-                        marker_slices, oracle_stages, run_logits, run_stage)
+from gpu_common import (BF16_ARGMAX_AGREEMENT, BF16_LOGIT_BOUND, BF16_PROB_BOUND, FP32_LOGIT_BOUND, GOLDEN,
+                        BF16_LOGIT_TIGHT, FP32_LOGIT_TIGHT, LOGIT_TOL, LONG_TOL, MAX_MARKERS, MAX_TOKENS,
+                        STAGE_TOL, STAGES, argmax_report, device_ids, golden,
+                        golden_for, marker_slices, oracle_stages, run_logits, run_stage, stage_batch,
+                        weight_file, weights_of)
 
 pytestmark = pytest.mark.gpu
-
-# Tighter bounds than the spec ones, from the arithmetic. FP32 products
-# against the float64 oracle drift by ~1e-7 per layer (3e-6 after 24 layers on
-# O(1) hidden values). bf16 operands carry a relative rounding of 2^-9 on every
-# GEMM and attention input; per-layer updates of ~0.1 then add ~3e-4 per layer,
-# 6e-3 after the head (measured). Both bounds leave a 3x or larger margin.
-FP32_HIDDEN_TOL = 1e-4
-BF16_HIDDEN_TOL = 2e-2
-FP32_LOGIT_TIGHT = 1e-5
-BF16_LOGIT_TIGHT = 3e-3
-
 
 @pytest.fixture(scope="module")
 def models():
@@ -46,14 +44,19 @@ def models():
 
 
 @pytest.fixture(scope="module")
-def jit_models():
+def set_models():
+    """bf16 and FP32 handles per weight set, loaded on first use."""
     from encoder_transformer_amd import lib
-    w = synth.make_weights(seed=3, norm_jitter=True)
-    path = synth.cached_weight_file(seed=3, norm_jitter=True, weights=w)
-    m = {"bf16": lib.Model(path, lib.BF16, 20000, 1024), "fp32": lib.Model(path, lib.FP32, 8192, 512), "w": w}
-    yield m
-    m["bf16"].close()
-    m["fp32"].close()
+    cache = {}
+
+    def get(name, prec):
+        if (name, prec) not in cache:
+            cache[(name, prec)] = lib.Model(weight_file(name), lib.BF16 if prec == "bf16" else lib.FP32,
+                                            MAX_TOKENS, MAX_MARKERS)
+        return cache[(name, prec)]
+    yield get
+    for v in cache.values():
+        v.close()
 
 
 def small_ragged():
@@ -61,64 +64,81 @@ def small_ragged():
     return synth.make_ragged_batch(seed=77, n_seqs=3, min_len=70, max_len=200)
 
 
+_STAGE_REF = {}
+
+
+def stage_reference(name):
+    """Oracle hidden states of the stage batch at STAGES (computed once per weight set)."""
+    if name not in _STAGE_REF:
+        from oracle import julia_oracle as jo
+        _STAGE_REF[name] = oracle_stages(jo.OracleWeights(weights_of(name)), stage_batch(), STAGES)
+    return _STAGE_REF[name]
+
+
+def check_stages(errs, name, prec):
+    tol = STAGE_TOL[(name, prec)]
+    print(name, prec, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {s: (e, tol[s]) for s, e in errs.items() if not (np.isfinite(e) and e <= tol[s])}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("name", ["jit02", "jit05"])
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
-def test_stage_parity_jittered(jit_models, prec):
-    from oracle import julia_oracle as jo
-    W = jo.OracleWeights(jit_models["w"])
-    batch = synth.concat([synth.make_batch(0), small_ragged()])
-    stages = [0, 1, 2, 3, 4, 12, 22, 23, 24, 25]
-    ref = oracle_stages(W, batch, stages)
-    tol = FP32_HIDDEN_TOL if prec == "fp32" else BF16_HIDDEN_TOL
+def test_stage_parity(set_models, name, prec):
+    """Hidden states after encoder layers 1-4, 12, 22, the head input and both
+    head layers (per-GEMM schedule: 506 tokens), against the oracle."""
+    batch = stage_batch()
+    ref = stage_reference(name)
     errs = {}
-    for s in stages:
-        got = run_stage(jit_models[prec], batch, s)
+    for s in STAGES:
+        got = run_stage(set_models(name, prec), batch, s)
         assert got.shape == ref[s].shape
         errs[s] = float(np.max(np.abs(got - ref[s])))
-    print(prec, {k: f"{v:.2e}" for k, v in errs.items()})
-    assert all(np.isfinite(v) and v <= tol for v in errs.values()), errs
+    check_stages(errs, name, prec)
 
 
 def rowblock_batch():
-    """Short sequences packed in front of eight 1,024-token ones: over 8,192
-    tokens, so a bf16 forward takes the row-block layer kernel."""
-    return synth.concat([synth.make_batch(0), small_ragged(), synth.make_batch(2).subset(range(8))])
+    """The stage batch packed in front of eight 1,024-token sequences: over
+    8,192 tokens, so a bf16 forward takes the row-block layer kernel."""
+    return synth.concat([stage_batch(), synth.make_batch(2).subset(range(8))])
 
 
-def test_stage_parity_rowblock_path(jit_models):
+@pytest.mark.parametrize("name", ["jit02", "jit05"])
+def test_stage_parity_rowblock_path(set_models, name):
     """Hidden states of the row-block path (bf16, >= 8,192 tokens) against the
-    oracle, on the batch's first four sequences (the oracle runs only those)."""
+    oracle, on the rows of the stage batch at the front (the oracle runs only
+    those), at the stage-parity bounds."""
     from oracle import julia_oracle as jo
-    W = jo.OracleWeights(jit_models["w"])
     batch = rowblock_batch()
     assert batch.n_tokens >= 8192
-    head = batch.subset([0, 1, 2, 3])
-    rows = int(head.seq_offsets[-1])
-    stages = [1, 2, 3, 4, 12, 22, 23, 24, 25]
-    ref = oracle_stages(W, head, stages)
+    head = stage_batch()
+    rows = head.n_tokens
+    ref = stage_reference(name)
+    m = set_models(name, "bf16")
     errs = {}
-    for st in stages:
-        got = run_stage(jit_models["bf16"], batch, st)
+    for st in STAGES:
+        got = run_stage(m, batch, st)
         sub = got[:head.n_markers] if st == 25 else got[:rows]
         errs[st] = float(np.max(np.abs(sub - ref[st])))
-    print("row-block bf16", {k: f"{v:.2e}" for k, v in errs.items()})
-    assert all(np.isfinite(v) and v <= BF16_HIDDEN_TOL for v in errs.values()), errs
-    got = run_logits(jit_models["bf16"], batch)
-    ref_l = jo.forward(W, head)
+    check_stages(errs, name, "bf16")
+    got = run_logits(m, batch)
+    ref_l = jo.forward(jo.OracleWeights(weights_of(name)), head)
     err = float(np.max(np.abs(got[:head.n_markers] - ref_l)))
     print("row-block bf16 max |dlogit|", err)
-    assert err <= BF16_LOGIT_TIGHT
+    assert err <= LOGIT_TOL[(name, "bf16")]
 
 
+@pytest.mark.parametrize("name", ["jit02", "jit05"])
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
-def test_logits_jittered(jit_models, prec):
+def test_logits_stage_batch(set_models, name, prec):
     from oracle import julia_oracle as jo
-    W = jo.OracleWeights(jit_models["w"])
-    batch = small_ragged()
+    W = jo.OracleWeights(weights_of(name))
+    batch = stage_batch()
     ref = jo.forward(W, batch)
-    got = run_logits(jit_models[prec], batch)
+    got = run_logits(set_models(name, prec), batch)
     err = float(np.max(np.abs(got - ref)))
-    print(prec, "max |dlogit|", err)
-    assert err <= (FP32_LOGIT_TIGHT if prec == "fp32" else BF16_LOGIT_TIGHT)
+    print(name, prec, "max |dlogit|", err)
+    assert err <= LOGIT_TOL[(name, prec)]
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -144,7 +164,7 @@ def test_logits_small_configs(models, oracle_weights, config, prec):
     ref = jo.forward(oracle_weights, batch)
     got = run_logits(models[prec], batch)
     err = float(np.max(np.abs(got - ref)))
-    rep = argmax_report(ref, got, batch.seq_offsets, batch.mask_positions, max(err, 1e-7))
+    rep = argmax_report(ref, got, batch.seq_offsets, batch.mask_positions, LOGIT_TOL[("standard", prec)])
     print(prec, config, "max |dlogit|", err, rep)
     if prec == "fp32":
         assert err <= FP32_LOGIT_BOUND and err <= FP32_LOGIT_TIGHT
@@ -154,28 +174,110 @@ def test_logits_small_configs(models, oracle_weights, config, prec):
         assert rep["clear_agree"] == rep["clear"]
 
 
-@pytest.mark.parametrize("config", [2, 3, 4])
-@pytest.mark.parametrize("prec", ["bf16", "fp32"])
-def test_logits_golden_full_batches(models, config, prec):
-    batch, seqs, ref_logits = golden_for(config)
-    got = run_logits(models[prec], batch)
+def compare_golden(got, batch, seqs, ref_logits, name, prec, config):
+    """max |dlogit| over the stored sequences, and argmax agreement: a question
+    is a tie when the oracle's top-2 gap is within twice the logit bound
+    (either answer is then correct); every other question must agree in FP32,
+    >= 99.5% of them in bf16 (the benchmark spec)."""
     assert got.shape == (batch.n_markers,) and np.all(np.isfinite(got))
     sl = marker_slices(batch)
     ref = np.concatenate([np.asarray(r) for r in ref_logits])
     sub = np.concatenate([got[sl[s]] for s in seqs])
     err = float(np.max(np.abs(sub - ref)))
     so = np.concatenate([[0], np.cumsum([len(r) for r in ref_logits])])
-    rep = argmax_report(ref, sub, so, np.arange(len(ref)), max(err, 1e-7))
-    print(prec, config, "sampled seqs", seqs, "max |dlogit|", err, rep)
-    bound = FP32_LOGIT_BOUND if prec == "fp32" else BF16_LOGIT_BOUND
+    bound = LOGIT_TOL[(name, prec)]
+    rep = argmax_report(ref, sub, so, np.arange(len(ref)), bound)
+    print(name, prec, config, "sampled seqs", len(seqs), "max |dlogit|", err, rep)
     assert err <= bound
-    assert rep["clear_agree"] >= BF16_ARGMAX_AGREEMENT * rep["clear"]
+    if prec == "fp32":
+        assert rep["clear_agree"] == rep["clear"]
+    else:
+        assert rep["clear_agree"] >= BF16_ARGMAX_AGREEMENT * rep["clear"]
+    return rep
 
 
-def test_golden_inputs_unchanged():
+@pytest.mark.parametrize("config", [2, 3, 4])
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_logits_golden_full_batches(models, config, prec):
+    """The full batches in the benchmark's launch shapes (published init)
+    against stored oracle logits of sampled sequences, at the tight bounds."""
+    batch, seqs, ref_logits = golden_for(config)
+    compare_golden(run_logits(models[prec], batch), batch, seqs, ref_logits, "standard", prec, config)
+
+
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_logits_golden_wide(set_models, config, prec):
+    """The wide weight set (std 0.05), whose option logits spread to order
+    one: every question of configurations 0-2 and of the 256-sequence mix,
+    two of the 16 x 8,192 batch; argmax agreement is meaningful here."""
+    batch, seqs, ref_logits = golden_for(config, wide=True)
+    rep = compare_golden(run_logits(set_models("wide", prec), batch), batch, seqs, ref_logits, "wide", prec,
+                         config)
+    # FP32: the same argmax on every question, near-ties included.  bf16:
+    # compare_golden requires it on every question whose oracle top-2 gap
+    # exceeds twice the bound; the agreement over all questions is printed
+    # (on the 256-question mix 249 of 256 measured: the 7 others are
+    # near-ties that bf16 rounding reorders)
+    if prec == "fp32":
+        assert rep["agree"] == rep["questions"]
+    print(name, prec, config, "argmax agreement over all questions", rep["agree"], "/", rep["questions"])
+    if config == 4:
+        assert rep["questions"] == 256
+
+
+def long_rows():
+    d = np.load(os.path.join(GOLDEN, "oracle_rows_long.npz"))
+    return {k: d[k] for k in d.files}
+
+
+@pytest.mark.parametrize("name", ["standard", "wide"])
+@pytest.mark.parametrize("path", ["fp32", "bf16-row-block", "bf16-per-gemm"])
+def test_long_sequence_rows(set_models, name, path):
+    """Hidden rows of two 8,192-token sequences of the 16 x 8,192 batch at
+    positions up to 8,191 (RoPE table ends, tile and window edges), run as the
+    whole batch, against stored oracle rows."""
+    import hashlib
+    import torch
+    d = long_rows()
+    batch = synth.make_batch(3)
+    h = hashlib.sha256()
+    for a in (batch.ids, batch.seq_offsets, batch.mask_positions, batch.qtype):
+        h.update(np.ascontiguousarray(a, np.int32).tobytes())
+    assert h.hexdigest().encode() == d["batch_digest"].tobytes()
+    prec = "fp32" if path == "fp32" else "bf16"
+    m = set_models(name, prec)
+    if path == "bf16-per-gemm":
+        m.set_row_block_min_tokens(1 << 62)
+    try:
+        ids = device_ids(batch)
+        pos = d["positions"].astype(np.int64)
+        sl = marker_slices(batch)
+        errs = {}
+        for st in (1, 2, 22, 24, 25):
+            out = m.debug_hidden(ids, batch.seq_offsets, batch.mask_positions, batch.qtype, st)
+            for s in d["seqs"]:
+                s = int(s)
+                rows = pos + int(batch.seq_offsets[s]) if st != 25 else np.arange(sl[s].start, sl[s].stop)
+                got = out[torch.from_numpy(rows).to(out.device)].cpu().numpy().astype(np.float64)
+                ref = d[f"{name}_s{s}_stage{st}"].astype(np.float64)
+                errs[st] = max(errs.get(st, 0.0), float(np.max(np.abs(got - ref))))
+        lg = run_logits(m, batch)
+        errs["logits"] = max(float(np.max(np.abs(lg[sl[int(s)]] - d[f"{name}_s{int(s)}_logits"])))
+                             for s in d["seqs"])
+    finally:
+        m.set_row_block_min_tokens(8192)
+    tol = LONG_TOL[(name, prec)]
+    print(name, path, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: (e, tol[k]) for k, e in errs.items() if not (np.isfinite(e) and e <= tol[k])}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("wide", [False, True])
+def test_golden_inputs_unchanged(wide):
     """The stored oracle logits belong to today's generator output."""
     import hashlib
-    g = golden()
+    g = golden(wide)
     for c, entry in g["configs"].items():
         b = synth.make_batch(int(c))
         h = hashlib.sha256()
