@@ -441,7 +441,7 @@ int alloc_workspace(jl_model *m) {
 
 }  // namespace
 
-extern "C" int jl_load_weights(const char *path, int precision, int64_t max_tokens, int64_t max_markers,
+static int jl_load_weights_impl(const char *path, int precision, int64_t max_tokens, int64_t max_markers,
                                int device, jl_model **out) {
   if (!path || !out) return fail(JL_ERR_ARG, "path and out must not be NULL");
   *out = nullptr;
@@ -695,7 +695,12 @@ extern "C" int jl_load_weights(const char *path, int precision, int64_t max_toke
   return JL_OK;
 }
 
-extern "C" int jl_share(const jl_model *src, int64_t max_tokens, int64_t max_markers, jl_model **out) {
+extern "C" int jl_load_weights(const char *path, int precision, int64_t max_tokens, int64_t max_markers,
+                               int device, jl_model **out) {
+  JL_CATCH_ALL(jl_load_weights_impl(path, precision, max_tokens, max_markers, device, out));
+}
+
+static int jl_share_impl(const jl_model *src, int64_t max_tokens, int64_t max_markers, jl_model **out) {
   if (!src || !out) return fail(JL_ERR_ARG, "src and out must not be NULL");
   if (max_tokens < 1 || max_tokens > (int64_t)1 << 26) return fail(JL_ERR_ARG, "max_tokens must be in 1..2^26");
   if (max_markers < 2 || max_markers > max_tokens) return fail(JL_ERR_ARG, "max_markers must be in 2..max_tokens");
@@ -734,6 +739,10 @@ extern "C" int jl_share(const jl_model *src, int64_t max_tokens, int64_t max_mar
   }
   *out = m;
   return JL_OK;
+}
+
+extern "C" int jl_share(const jl_model *src, int64_t max_tokens, int64_t max_markers, jl_model **out) {
+  JL_CATCH_ALL(jl_share_impl(src, max_tokens, max_markers, out));
 }
 
 ServeState *&jl::model_serve_state(jl_model *m) { return m->serve; }

@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <exception>
+#include <new>
+
 namespace jl {
 
 // Model shape (mmBERT-small encoder + Julia-1 decision head).
@@ -168,6 +171,17 @@ hipError_t launch_probs(const float *logits, const int *marker_offsets, const in
 
 // Sets the calling thread's jl_last_error() message; returns `code`.
 int set_error(int code, const char *msg);
+
+// Body of an extern "C" entry point that uses C++ containers: no exception
+// crosses the C ABI (an allocation failure becomes JL_ERR_OOM).
+#define JL_CATCH_ALL(call)                                                  \
+  try {                                                                     \
+    return call;                                                            \
+  } catch (const std::bad_alloc &) {                                        \
+    return ::jl::set_error(JL_ERR_OOM, "host memory exhausted");            \
+  } catch (const std::exception &e_) {                                      \
+    return ::jl::set_error(JL_ERR_ARG, e_.what());                          \
+  }
 
 }  // namespace jl
 

@@ -235,7 +235,7 @@ struct ModelScorer {
 
 }  // namespace
 
-extern "C" int jl_route_with_scorer(jl_score_fn score, void *user, int64_t max_tokens, int64_t max_markers,
+static int jl_route_with_scorer_impl(jl_score_fn score, void *user, int64_t max_tokens, int64_t max_markers,
                                     int32_t n_questions, const int32_t *prefix_ids, const int64_t *prefix_offsets,
                                     const int32_t *suffix_ids, const int64_t *suffix_offsets,
                                     const int32_t *option_ids, const int64_t *option_offsets,
@@ -250,7 +250,19 @@ extern "C" int jl_route_with_scorer(jl_score_fn score, void *user, int64_t max_t
                rounds);
 }
 
-extern "C" int jl_route(jl_model *m, int32_t n_questions, const int32_t *prefix_ids, const int64_t *prefix_offsets,
+extern "C" int jl_route_with_scorer(jl_score_fn score, void *user, int64_t max_tokens, int64_t max_markers,
+                                    int32_t n_questions, const int32_t *prefix_ids, const int64_t *prefix_offsets,
+                                    const int32_t *suffix_ids, const int64_t *suffix_offsets,
+                                    const int32_t *option_ids, const int64_t *option_offsets,
+                                    const int32_t *question_options, int32_t mask_id, int32_t *pick,
+                                    float *pick_prob, int32_t *n_final, int32_t *final_idx, float *final_prob,
+                                    int32_t *calls, int32_t *rounds) {
+  JL_CATCH_ALL(jl_route_with_scorer_impl(score, user, max_tokens, max_markers, n_questions, prefix_ids, prefix_offsets, suffix_ids,
+               suffix_offsets, option_ids, option_offsets, question_options, mask_id, pick, pick_prob, n_final,
+               final_idx, final_prob, calls, rounds));
+}
+
+static int jl_route_impl(jl_model *m, int32_t n_questions, const int32_t *prefix_ids, const int64_t *prefix_offsets,
                         const int32_t *suffix_ids, const int64_t *suffix_offsets, const int32_t *option_ids,
                         const int64_t *option_offsets, const int32_t *question_options, int32_t mask_id,
                         int32_t *pick, float *pick_prob, int32_t *n_final, int32_t *final_idx, float *final_prob,
@@ -264,4 +276,13 @@ extern "C" int jl_route(jl_model *m, int32_t n_questions, const int32_t *prefix_
                   option_offsets, question_options, mask_id};
   return route(&ModelScorer::call, &ms, info[1], info[2], in, pick, pick_prob, n_final, final_idx, final_prob,
                calls, rounds);
+}
+
+extern "C" int jl_route(jl_model *m, int32_t n_questions, const int32_t *prefix_ids, const int64_t *prefix_offsets,
+                        const int32_t *suffix_ids, const int64_t *suffix_offsets, const int32_t *option_ids,
+                        const int64_t *option_offsets, const int32_t *question_options, int32_t mask_id,
+                        int32_t *pick, float *pick_prob, int32_t *n_final, int32_t *final_idx, float *final_prob,
+                        int32_t *calls, int32_t *rounds, void *stream) {
+  JL_CATCH_ALL(jl_route_impl(m, n_questions, prefix_ids, prefix_offsets, suffix_ids, suffix_offsets, option_ids, option_offsets,
+               question_options, mask_id, pick, pick_prob, n_final, final_idx, final_prob, calls, rounds, stream));
 }

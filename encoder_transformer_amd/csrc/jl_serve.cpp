@@ -109,7 +109,7 @@ int jl::handle_buffers(jl_model *m, HandleBuffers *out) {
   return JL_OK;
 }
 
-extern "C" int jl_serve_plan(int32_t n_requests, const int64_t *id_offsets, const int64_t *mask_offsets,
+static int jl_serve_plan_impl(int32_t n_requests, const int64_t *id_offsets, const int64_t *mask_offsets,
                              int64_t max_batch_tokens, int64_t max_batch_markers, int64_t max_batch_seqs,
                              int32_t *order, int32_t *batch_of, int32_t *n_batches) {
   if (n_requests < 0 || (n_requests > 0 && (!id_offsets || !mask_offsets || !order || !batch_of)) || !n_batches)
@@ -145,7 +145,14 @@ extern "C" int jl_serve_plan(int32_t n_requests, const int64_t *id_offsets, cons
   return JL_OK;
 }
 
-extern "C" int jl_serve(jl_model *const *models, int32_t n_models, int32_t n_requests, const int32_t *ids,
+extern "C" int jl_serve_plan(int32_t n_requests, const int64_t *id_offsets, const int64_t *mask_offsets,
+                             int64_t max_batch_tokens, int64_t max_batch_markers, int64_t max_batch_seqs,
+                             int32_t *order, int32_t *batch_of, int32_t *n_batches) {
+  JL_CATCH_ALL(jl_serve_plan_impl(n_requests, id_offsets, mask_offsets, max_batch_tokens, max_batch_markers, max_batch_seqs, order,
+               batch_of, n_batches));
+}
+
+static int jl_serve_impl(jl_model *const *models, int32_t n_models, int32_t n_requests, const int32_t *ids,
                         const int64_t *id_offsets, const int32_t *mask_positions, const int64_t *mask_offsets,
                         const int32_t *qtype, int64_t max_batch_tokens, float *logits, float *probs, float *answer,
                         int32_t *argmax, float *maxprob, int32_t *n_batches) {
@@ -264,4 +271,12 @@ extern "C" int jl_serve(jl_model *const *models, int32_t n_models, int32_t n_req
   if (prev >= 0) (void)hipSetDevice(prev);
   if (rc == JL_OK && n_batches) *n_batches = nb;
   return rc;
+}
+
+extern "C" int jl_serve(jl_model *const *models, int32_t n_models, int32_t n_requests, const int32_t *ids,
+                        const int64_t *id_offsets, const int32_t *mask_positions, const int64_t *mask_offsets,
+                        const int32_t *qtype, int64_t max_batch_tokens, float *logits, float *probs, float *answer,
+                        int32_t *argmax, float *maxprob, int32_t *n_batches) {
+  JL_CATCH_ALL(jl_serve_impl(models, n_models, n_requests, ids, id_offsets, mask_positions, mask_offsets, qtype, max_batch_tokens,
+               logits, probs, answer, argmax, maxprob, n_batches));
 }

@@ -150,29 +150,33 @@ def tensor_checksum(a: np.ndarray) -> int:
     return total % (1 << 64)
 
 
-def write_weight_file(path: str, weights: Dict[str, np.ndarray]) -> None:
-    names = [n for n, _, _ in weight_spec(weights["embeddings.tok_embeddings.weight"].shape[0])]
+def weight_file_header(tensors: Sequence[Tuple[str, Tuple[int, ...], int]]) -> Tuple[bytes, List[int], int]:
+    """Header bytes of a weight file holding `tensors` ((name, shape,
+    checksum) in file order), each tensor's data offset and the file size."""
     hdr_size = 16
-    for n in names:
-        hdr_size += 2 + len(n.encode()) + 1 + 4 * weights[n].ndim + 16
+    for n, shape, _ in tensors:
+        hdr_size += 2 + len(n.encode()) + 1 + 4 * len(shape) + 16
     off = (hdr_size + _ALIGN - 1) // _ALIGN * _ALIGN
     layout = []
-    for n in names:
-        a = weights[n]
+    for _, shape, _ in tensors:
         layout.append(off)
-        off += a.size * 4
+        off += int(np.prod(shape)) * 4
         off = (off + _ALIGN - 1) // _ALIGN * _ALIGN
-    total = off
     hdr = bytearray()
     hdr += WEIGHT_FILE_MAGIC
-    hdr += struct.pack("<III", WEIGHT_FILE_VERSION, len(names), hdr_size)
-    for n, o in zip(names, layout):
-        a = weights[n]
+    hdr += struct.pack("<III", WEIGHT_FILE_VERSION, len(tensors), hdr_size)
+    for (n, shape, checksum), o in zip(tensors, layout):
         nb = n.encode()
-        hdr += struct.pack("<H", len(nb)) + nb + struct.pack("<B", a.ndim)
-        hdr += struct.pack("<" + "I" * a.ndim, *a.shape)
-        hdr += struct.pack("<QQ", o, tensor_checksum(a))
+        hdr += struct.pack("<H", len(nb)) + nb + struct.pack("<B", len(shape))
+        hdr += struct.pack("<" + "I" * len(shape), *shape)
+        hdr += struct.pack("<QQ", o, checksum)
     assert len(hdr) == hdr_size
+    return bytes(hdr), layout, off
+
+
+def write_weight_file(path: str, weights: Dict[str, np.ndarray]) -> None:
+    names = [n for n, _, _ in weight_spec(weights["embeddings.tok_embeddings.weight"].shape[0])]
+    hdr, layout, total = weight_file_header([(n, weights[n].shape, tensor_checksum(weights[n])) for n in names])
     tmp = path + ".tmp%d" % os.getpid()
     with open(tmp, "wb") as f:
         f.write(hdr)

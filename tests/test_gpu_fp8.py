@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from encoder_transformer_amd import synth
-from gpu_common import marker_slices, run_logits
+from gpu_common import marker_slices, run_logits, run_stage, stage_batch, weight_file, weights_of
 
 pytestmark = pytest.mark.gpu
 
@@ -66,3 +66,59 @@ def test_fp8_multi_round_grids(models8, oracle_weights):
     err = float(np.max(np.abs(run_logits(models8["fp8"], batch) - ref8)))
     print("max |dlogit| against the e4m3 oracle", err)
     assert err <= FP8_LOGIT_TIGHT
+
+
+@pytest.fixture(scope="module")
+def jit8():
+    from encoder_transformer_amd import lib
+    m = {name: lib.Model(weight_file(name), lib.FP8, 20000, 1024) for name in ("jit02", "jit05")}
+    yield m
+    for v in m.values():
+        v.close()
+
+
+@pytest.mark.parametrize("name", ["jit02", "jit05"])
+def test_fp8_stages_follow_the_e4m3_products(jit8, name):
+    """Hidden states after the first four layers (the stage batch, jittered
+    weights at std 0.02 and 0.05): the e4m3 rounding moves the oracle's
+    states by 13x the bf16 mode's error there (1.6e-2 against 1.2e-3 after
+    layer 1 at std 0.02), so the FP8 mode must stay within a quarter of that
+    gap of the oracle's e4m3 forward -- not near its exact forward, and not
+    off by a scale.  Further on, bf16-level differences ahead of each
+    quantization flip a few e4m3 codes (steps of 2^-3) and the flips
+    compound: after 22 layers at std 0.05 the logits are 0.064 from the e4m3
+    oracle and 0.056 from the exact one, which are 0.086 apart."""
+    from oracle import julia_oracle as jo
+    W = jo.OracleWeights(weights_of(name))
+    batch = stage_batch()
+    per8, per = {s: [] for s in (1, 2, 3, 4)}, {s: [] for s in (1, 2, 3, 4)}
+    for b in range(batch.n_seqs):
+        ids, _, _ = batch.sequence(b)
+        x8 = x = jo.embed(W, ids)
+        for l in range(4):
+            x8 = jo.encoder_layer(W, l, x8, fp8=True)
+            x = jo.encoder_layer(W, l, x)
+            per8[l + 1].append(x8)
+            per[l + 1].append(x)
+    # Measured at std 0.02: 0.18-0.20 of the gap from the e4m3 oracle and
+    # 0.99-1.01 of it from the exact one.  At std 0.05 the bf16 attention
+    # ahead of layer 0's W_i already leaves differences of ~2e-2 in its
+    # input, which flip some e4m3 codes, and the flips compound: 0.35, 0.47,
+    # 0.54, 0.51 of the gap after layers 1-4 (0.98-1.06 from the exact one);
+    # there the e4m3 oracle is matched after layer 1 only, and the exact
+    # oracle must be missed at every stage.
+    frac = {"jit02": 0.3, "jit05": 0.5}[name]
+    check_upto = {"jit02": 4, "jit05": 1}[name]  # stages up to this one held to frac
+    rows = []
+    for st in (1, 2, 3, 4):
+        ref8, ref = np.concatenate(per8[st]), np.concatenate(per[st])
+        got = run_stage(jit8[name], batch, st)
+        e8 = float(np.max(np.abs(got - ref8)))
+        ex = float(np.max(np.abs(got - ref)))
+        gap = float(np.max(np.abs(ref8 - ref)))
+        print(name, "stage", st, "max |d| vs e4m3 oracle", e8, "vs exact oracle", ex, "e4m3 gap", gap)
+        rows.append((st, e8, ex, gap))
+    for st, e8, ex, gap in rows:
+        assert ex >= 0.75 * gap, (st, e8, ex, gap)  # not the exact products
+        if st <= check_upto:
+            assert e8 <= frac * gap, (st, e8, ex, gap)  # the e4m3 products, scaled as the oracle scales them

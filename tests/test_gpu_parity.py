@@ -221,7 +221,7 @@ def test_logits_golden_wide(set_models, config, prec):
     # near-ties that bf16 rounding reorders)
     if prec == "fp32":
         assert rep["agree"] == rep["questions"]
-    print(name, prec, config, "argmax agreement over all questions", rep["agree"], "/", rep["questions"])
+    print("wide", prec, config, "argmax agreement over all questions", rep["agree"], "/", rep["questions"])
     if config == 4:
         assert rep["questions"] == 256
 

@@ -103,3 +103,47 @@ def test_serve_rejects_before_any_work(models):
                     i(breq.qtype), 8192, f(logits), f(other[0]), f(other[1]), i(other[2]), f(other[3]), None)
     assert rc == lib.ERR_QTYPE and "request 4" in L.jl_last_error().decode()
     assert np.all(logits == 7.0) and np.all(other[0] == 7.0)
+
+
+@pytest.mark.parametrize("name", ["standard", "wide"])
+def test_serve_against_the_oracle(name):
+    """jl_serve on the requests of the 256-sequence ragged mix against the
+    oracle: logits against the stored oracle logits (wide weights: all 256
+    requests, logits of order one; published init: the 8 stored ones), the
+    probabilities and answers against the oracle's read-offs of those logits.
+    Micro-batches of up to 32,768 tokens on two handles, so both schedules run."""
+    from encoder_transformer_amd import lib
+    from gpu_common import BF16_PROB_BOUND, LOGIT_TOL, golden_for, weight_file
+    from oracle import julia_oracle as jo
+    batch, seqs, ref_logits = golden_for(4, wide=name == "wide")
+    items = [batch.sequence(b) for b in seqs]
+    req = lib.Requests(items)
+    m = lib.Model(weight_file(name), lib.BF16, 32768, 4096)
+    h2 = m.share()
+    try:
+        res = lib.serve([m, h2], req, max_batch_tokens=32768)
+    finally:
+        h2.close()
+        m.close()
+    bound = LOGIT_TOL[(name, "bf16")]
+    worst = {"logit": 0.0, "prob": 0.0}
+    for r, (ids, marks, qt) in enumerate(items):
+        ref = np.asarray(ref_logits[r])
+        got = res.request_logits(r)
+        worst["logit"] = max(worst["logit"], float(np.max(np.abs(got - ref))))
+        ro = jo.read_offs(ref, np.array([0, len(ids)]), np.asarray(marks), np.array([qt]))
+        dp = float(np.max(np.abs(res.probs[req.mask_offsets[r]:req.mask_offsets[r + 1]] - ro["probs"])))
+        worst["prob"] = max(worst["prob"], dp)
+        n = len(marks)
+        if qt == 1:  # expected index: sum_i i * dp_i
+            assert abs(res.answer[r] - ro["answer"][0]) <= dp * n * (n - 1) / 2 + 1e-6, r
+        elif qt == 2:  # p(true)
+            assert abs(res.answer[r] - ro["answer"][0]) <= dp + 1e-6, r
+        srt = np.sort(ref)[::-1]
+        if srt[0] - srt[1] > 2 * bound:  # a clear question: the same argmax (and the choice answer)
+            assert res.argmax[r] == ro["argmax"][0], r
+            if qt == 0:
+                assert res.answer[r] == ro["answer"][0], r
+    print(name, "serve vs oracle", worst, "micro-batches", res.n_batches)
+    assert worst["logit"] <= bound
+    assert worst["prob"] <= BF16_PROB_BOUND
