@@ -17,6 +17,7 @@
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -246,7 +247,8 @@ struct jl_model {
   std::vector<int> plan_order;
   std::vector<AttnWork> plan_per[8];
 
-  // per-kernel timer
+  // per-kernel timer (suspended inside jl_forward_static, which records no events)
+  bool prof_suspended = false;
   bool prof = false;
   uint32_t prof_mask = 0;
   std::vector<ProfRec> prof_rec;
@@ -436,6 +438,40 @@ int alloc_workspace(jl_model *m) {
     if (hipEventCreateWithFlags(&m->slot_done[k], hipEventDisableTiming) != hipSuccess)
       return fail(JL_ERR_DEVICE, "cannot create an event");
   }
+  return JL_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// Largest batch of jl_forward_static: 2,048 tokens and 256 markers (so at
+// most 128 sequences), in any precision; its workspace (FP32 mode: 31.3 MB)
+// lives in `scratch`, one copy per GPU, held until the process ends.
+constexpr int64_t kStaticMaxTokens = 2048, kStaticMaxMarkers = 256, kStaticMaxSeqs = kStaticMaxMarkers / 2;
+constexpr size_t kStaticMetaInts = meta_ints_for(kStaticMaxTokens, kStaticMaxMarkers, kStaticMaxSeqs);
+constexpr size_t kScratchBytes = workspace_bytes(kStaticMaxTokens, kStaticMaxMarkers, 4, kStaticMetaInts, 1);
+static_assert(kScratchBytes <= ((size_t)32 << 20), "static workspace above 32 MiB");
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// The array's device address on each GPU (hipGetSymbolAddress, taken once
+// per device at the first jl_load_weights there, with that device current).
+// In host code `scratch` names a host-side stand-in, never device memory:
+// only these addresses are passed to kernels and copies.
+std::mutex g_scratch_mu;
+void *g_scratch_dev[64] = {};
+
+int scratch_init(int device) {
+  if (device >= 64) return fail(JL_ERR_DEVICE, "device index above 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_dev[device]) return JL_OK;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != device) return fail(JL_ERR_DEVICE, "scratch: device not current");
+  void *p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return fail(JL_ERR_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+  g_scratch_dev[device] = p;
   return JL_OK;
 }
 
@@ -666,6 +702,10 @@ static int jl_load_weights_impl(const char *path, int precision, int64_t max_tok
     return fail(JL_ERR_DEVICE, "no HIP device " + std::to_string(device));
   }
   DeviceGuard dg(device);
+  if (int rc = scratch_init(device)) {
+    delete m;
+    return rc;
+  }
   const size_t emb_bytes = (size_t)kVocab * D * 4;
   const size_t rest = (ar.buf.size() + 255) & ~size_t(255);
   m->wbytes = emb_bytes + rest;
@@ -780,9 +820,11 @@ struct Plan {
 };
 
 // Build the metadata in pinned memory and enqueue its upload.
-// Allocates nothing: the host-side vectors are the handle's, reserved at load.
+// `dmeta_override`: device block to upload to instead of the handle's own
+// (the allocation-free entry point's, in its static scratch).  Allocates
+// nothing: the host-side vectors are the handle's, reserved at load.
 int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, int32_t M, const int32_t *qt,
-                hipStream_t s, Plan &pl, bool to_graph_buffer = false) {
+                hipStream_t s, Plan &pl, bool to_graph_buffer = false, int *dmeta_override = nullptr) {
   pl.B = B;
   pl.M = M;
   pl.T = so[B];
@@ -809,7 +851,7 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
     if (need > m->meta_ints) return fail(JL_ERR_CAPACITY, "batch metadata exceeds the staging buffer");
   }
   int *h = m->host_meta[slot];
-  int *dmeta = to_graph_buffer ? m->gmeta : m->meta[slot];
+  int *dmeta = dmeta_override ? dmeta_override : to_graph_buffer ? m->gmeta : m->meta[slot];
   size_t o = 0;
   const size_t o_so = o;
   for (int b = 0; b <= B; ++b) h[o++] = so[b];
@@ -951,7 +993,7 @@ struct Launch {
   int cls;
   hipEvent_t a = nullptr;
   Launch(jl_model *m_, hipStream_t s_, int c) : m(m_), s(s_), cls(c) {
-    if (m->prof && (m->prof_mask >> c & 1u)) {
+    if (m->prof && !m->prof_suspended && (m->prof_mask >> c & 1u)) {
       a = prof_event(m);
       if (a) (void)hipEventRecord(a, s);
     }
@@ -1296,6 +1338,38 @@ extern "C" int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *se
   if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl, use_graph)) return rc;
   if (!use_graph) return finish_plan(m, pl, s, run_forward(m, m->w, ids_dev, pl, 26, logits_dev, s));
   return finish_plan(m, pl, s, forward_graph(m, ids_dev, pl, logits_dev, s));
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free forward: the workspace in a static device array
+// ---------------------------------------------------------------------------
+
+extern "C" int jl_forward_static(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
+                                 const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype,
+                                 float *logits_dev, void *stream) {
+  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  const int64_t max_t = std::min(m->max_tokens, kStaticMaxTokens), max_m = std::min(m->max_markers, kStaticMaxMarkers);
+  if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, max_t, max_m)) {
+    if (rc == JL_ERR_CAPACITY)
+      g_err = "jl_forward_static takes at most " + std::to_string(max_t) + " tokens and " + std::to_string(max_m) +
+              " markers (static workspace of 2,048 tokens / 256 markers, and the handle's capacity): " + g_err;
+    return rc;
+  }
+  if (n_seqs == 0) return JL_OK;
+  if (!ids_dev || !logits_dev) return fail(JL_ERR_ARG, "ids_dev and logits_dev must not be NULL");
+  char *base = m->device < 64 ? (char *)g_scratch_dev[m->device] : nullptr;
+  if (!base) return fail(JL_ERR_DEVICE, "no static workspace on this device");
+  DeviceGuard dg(m->device);
+  Workspace w;
+  int *dmeta = nullptr;
+  layout_workspace(base, kStaticMaxTokens, kStaticMaxMarkers, m->esize, kStaticMetaInts, &w, &dmeta, 1);
+  hipStream_t s = (hipStream_t)stream;
+  Plan pl;
+  if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl, false, dmeta)) return rc;
+  m->prof_suspended = true;  // timer events would have to be created on demand
+  const int rc = run_forward(m, w, ids_dev, pl, 26, logits_dev, s);
+  m->prof_suspended = false;
+  return finish_plan(m, pl, s, rc);
 }
 
 extern "C" int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,

@@ -67,6 +67,8 @@ def load_library():
     L.jl_validate.argtypes = [_i32p, i32, _i32p, i32, _i32p, i64, i64]
     L.jl_forward.restype = ctypes.c_int
     L.jl_forward.argtypes = [vp, vp, _i32p, i32, _i32p, i32, _i32p, vp, vp]
+    L.jl_forward_static.restype = ctypes.c_int
+    L.jl_forward_static.argtypes = [vp, vp, _i32p, i32, _i32p, i32, _i32p, vp, vp]
     L.jl_probs.restype = ctypes.c_int
     L.jl_probs.argtypes = [vp, vp, _i32p, i32, _i32p, i32, _i32p, vp, vp, vp, vp, vp]
     L.jl_debug_hidden.restype = ctypes.c_int
@@ -301,6 +303,14 @@ class Model:
             out = torch.empty(len(mp), dtype=torch.float32, device=f"cuda:{self.device}")
         _check(self._lib.jl_forward(self._h, ctypes.c_void_p(ids.data_ptr()), _p(so), len(qt), _p(mp), len(mp),
                                     _p(qt), ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
+        return out
+
+    def forward_static(self, ids, seq_offsets, mask_positions, qtype, out, stream=None):
+        """jl_forward_static: the forward pass on the library's static workspace
+        (no allocation; at most 2,048 tokens and 256 markers)."""
+        so, mp, qt = self._meta(seq_offsets, mask_positions, qtype)
+        _check(self._lib.jl_forward_static(self._h, ctypes.c_void_p(ids.data_ptr()), _p(so), len(qt), _p(mp),
+                                           len(mp), _p(qt), ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
         return out
 
     def probs(self, logits, seq_offsets, mask_positions, qtype, stream=None):

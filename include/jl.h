@@ -132,6 +132,25 @@ int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets,
                const int32_t *qtype, float *logits_dev, void *stream);
 
 /*
+ * jl_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and result as jl_forward, bitwise, with the activation
+ * workspace and the batch metadata in the library's static device array
+ * (30.4 MiB, one per GPU, taken at the first jl_load_weights on that GPU and
+ * held until the process ends) instead of the handle's workspace.  Allocates
+ * nothing, on the device or the host, and records no timer events.
+ * Limits: at most 2,048 tokens and 256 markers (and the handle's own
+ * capacity); larger batches are rejected with JL_ERR_CAPACITY before
+ * anything is enqueued.  Every call on one GPU shares the array, which keeps
+ * the previous call's contents (nothing in it needs to start at zero): calls
+ * that overlap on one GPU, from any handle or stream, race -- order them.
+ * Arguments and other errors as jl_forward; no graph replay.
+ */
+int jl_forward_static(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets,
+                      int32_t n_seqs, const int32_t *mask_positions, int32_t n_markers,
+                      const int32_t *qtype, float *logits_dev, void *stream);
+
+/*
  * Softmax across each question's options (temperature 1) and the answers of
  * the three modes ("Julia-1: one score per mask token ...", Three modes
  * through one head):
