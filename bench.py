@@ -35,6 +35,14 @@ ROW_BLOCK_MIN_TOKENS = 8192  # bf16 batches this large use the row-block layer k
 PROFILE_EVERY = 4
 
 
+def call_alg_bytes(batch):
+    """Algorithmic HBM bytes of one forward + read-off: every bf16 GEMM weight
+    once (encoder 22 x 3,833,856 B; head layers 2 x 3,538,944 B), the FP32
+    norms, biases, type table and scorer (709,636 B), each token's FP32
+    embedding row and id, each marker's logit and probability."""
+    return 22 * 3_833_856 + 2 * 3_538_944 + 709_636 + batch.n_tokens * (1536 + 4) + batch.n_markers * 8
+
+
 def band_pairs(L, w=64):
     p = np.arange(L)
     return int(np.sum(np.minimum(L - 1, p + w) - np.maximum(0, p - w) + 1))
@@ -244,6 +252,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--latency-only", action="store_true",
                     help="time only the 1 x 1,024 call (graph replays; for a kernel trace of that workload)")
+    ap.add_argument("--only", choices=["16x8192", "ragged256"],
+                    help="time only this workload (graph replays; for profiles of that workload)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (for HBM counter calibration)")
     args = ap.parse_args()
@@ -266,6 +276,17 @@ def main():
         print(json.dumps({"metric": "ms per call at 1x1024", "value": round(1e3 * t1 / args.steps, 4), "unit": "ms",
                           "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
                           "calls": 1 + max(1, args.warmup) + args.steps}))
+        return
+
+    if args.only:
+        b = synth.make_batch({"16x8192": 3, "ragged256": 4}[args.only])
+        tt, d, *_ = time_workload(model, b, args.steps, args.warmup, sample=False)
+        fl = sum(class_flops(b, row_block=b.n_tokens >= ROW_BLOCK_MIN_TOKENS).values())
+        model.close()
+        print(json.dumps({"metric": f"decisions/s at {args.only}", "value": round(b.n_seqs * args.steps / tt, 2),
+                          "unit": "decisions/s", "ms_per_step": round(1e3 * tt / args.steps, 3),
+                          "step_mfma_frac": round(fl / (tt / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}))
         return
 
     b2 = synth.make_batch(2)
@@ -306,6 +327,18 @@ def main():
         t1, *_ = time_workload(model, b1, max(args.steps, 20), args.warmup, sample=False)
         extra["1x1024_ms_per_call"] = round(1e3 * t1 / max(args.steps, 20), 4)
         extra["1x1024_calls"] = call_distribution(model, b1)
+        # HBM rate of the call: algorithmic bytes, and the counter bytes
+        # (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of its committed summary
+        call_s = t1 / max(args.steps, 20)
+        alg = call_alg_bytes(b1)
+        ctr = profiling.read_call_traffic(os.path.join(ROOT, "profiles"))
+        extra["1x1024_hbm"] = {
+            "alg_bytes": alg, "alg_GBps": round(alg / call_s / 1e9, 1),
+            "alg_frac": round(alg / call_s / 1e9 / HBM_GBPS, 4),
+            "counter_bytes": None if ctr is None else round(ctr),
+            "counter_GBps": None if ctr is None else round(ctr / call_s / 1e9, 1),
+            "counter_frac": None if ctr is None else round(ctr / call_s / 1e9 / HBM_GBPS, 4),
+            "peak_GBps": HBM_GBPS}
         for name, cfg, st in [("16x8192", 3, 5), ("ragged256", 4, 5)]:
             b = synth.make_batch(cfg)
             tt, d, dms, dn, _, _ = time_workload(model, b, st, 2, sample=False)

@@ -3,6 +3,10 @@
     python -m encoder_transformer_amd.profiling stats <kernel_stats.csv> <out.md> --command "<cmd>"
     python -m encoder_transformer_amd.profiling traffic <fetch_counter.csv> <write_counter.csv> <out.md>
         --kernel layer_kernel --copy-mib 256 --command "<cmd>"
+    python -m encoder_transformer_amd.profiling call_traffic <fetch.csv> <write.csv> <out.md> --calls N
+        --copy-mib 256 --command "<cmd>"
+    python -m encoder_transformer_amd.profiling counters <counter.csv> <out.md> --kernels a,b --title T
+        --command "<cmd>"
 
 `stats` turns rocprofv3's --stats kernel table into markdown.  `traffic`
 turns two --pmc passes (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) into
@@ -11,6 +15,12 @@ for a plain device copy of known size in the same run (bench.py
 --calibration-copy-mib), because FETCH_SIZE and WRITE_SIZE do not count
 bytes one-to-one on every chip.  The summary carries a digest of the kernel
 sources; bench.py reports the figure only while the digest still matches.
+`call_traffic` does the same for every dispatch of a run of whole calls
+(bench.py --latency-only) and reports HBM bytes per call.  `counters`
+tabulates any --pmc pass per kernel (mean per dispatch) and, where the pass
+holds SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE, the matrix-core
+utilization as rocprofv3 defines it (MfmaUtil: the busy cycles summed over
+the SIMDs, over one XCD's GUI-active cycles times the SIMD count).
 """
 from __future__ import annotations
 
@@ -33,6 +43,10 @@ KERNELS = {
     "attn_local": ("attn_kernel", ["jl_kernels.hip", "jl_device.h", "jl_internal.h"]),
 }
 COPY_KERNEL = "copyBuffer"
+# sources of the per-GEMM schedule that a batch-1 call runs (kernels and launch plan)
+CALL_SOURCES = ["jl_kernels.hip", "jl_device.h", "jl_internal.h", "jl_api.cpp"]
+CALL_TRAFFIC_LINE = re.compile(r"^traffic_bytes_per_call:\s*([0-9.]+)\s+sources_sha256:\s*([0-9a-f]+)\s*$", re.M)
+SIMD_NUM = 1024  # 256 CUs x 4 SIMDs
 TRAFFIC_LINE = re.compile(r"^traffic_bytes_per_launch:\s*([0-9.]+)\s+sources_sha256:\s*([0-9a-f]+)\s*$", re.M)
 
 
@@ -123,6 +137,104 @@ def cmd_traffic(a):
     print(f"{a.out_md}: {(fb + wb) / 1e6:.2f} MB per launch")
 
 
+def read_call_traffic(profiles_dir: str):
+    """HBM bytes per 1 x 1,024 call from its committed summary, or None when
+    there is none or the sources changed since it was taken."""
+    path = os.path.join(profiles_dir, "traffic_call_1x1024_bf16.md")
+    if not os.path.exists(path):
+        return None
+    m = CALL_TRAFFIC_LINE.search(open(path).read())
+    if not m or m.group(2) != source_digest(CALL_SOURCES):
+        return None
+    return float(m.group(1))
+
+
+def cmd_call_traffic(a):
+    out = {}
+    for c, path in (("FETCH_SIZE", a.fetch_csv), ("WRITE_SIZE", a.write_csv)):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == c]
+        copies = [float(r["Counter_Value"]) for r in rows if COPY_KERNEL in r["Kernel_Name"]]
+        cal = max(copies)  # the calibration copy: the largest copy dispatch
+        scale = a.copy_mib * (1 << 20) / (cal * 1024.0)
+        # every dispatch of the calls: all but the calibration copies
+        total = sum(float(r["Counter_Value"]) for r in rows
+                    if not (COPY_KERNEL in r["Kernel_Name"] and float(r["Counter_Value"]) > 0.5 * cal))
+        out[c] = (len(rows), cal, scale, total * 1024.0 * scale / a.calls)
+    fb, wb = out["FETCH_SIZE"][3], out["WRITE_SIZE"][3]
+    digest = source_digest(CALL_SOURCES)
+    lines = [
+        "# HBM traffic of one 1 x 1,024 call (bf16, jl_forward + jl_probs)",
+        "",
+        "Command (two passes, one counter each, from the repository root):",
+        "",
+        "```",
+        a.command,
+        "```",
+        "",
+        f"Every dispatch of the {a.calls} calls of the run is summed (the three calibration copies of "
+        f"{a.copy_mib} MiB excluded) and divided by {a.calls}.  Calibration: the copy reads "
+        f"FETCH_SIZE = {out['FETCH_SIZE'][1]:.0f} KiB and WRITE_SIZE = {out['WRITE_SIZE'][1]:.0f} KiB per dispatch, "
+        f"so the counters are scaled by {out['FETCH_SIZE'][2]:.3f} (fetch) and {out['WRITE_SIZE'][2]:.3f} (write).",
+        "",
+        "| counter | dispatches in the run | scaled MB per call |",
+        "|---|---|---|",
+        f"| FETCH_SIZE | {out['FETCH_SIZE'][0]} | {fb / 1e6:.2f} |",
+        f"| WRITE_SIZE | {out['WRITE_SIZE'][0]} | {wb / 1e6:.2f} |",
+        f"| total | | {(fb + wb) / 1e6:.2f} |",
+        "",
+        f"traffic_bytes_per_call: {fb + wb:.0f} sources_sha256: {digest}",
+        "",
+    ]
+    if a.note:
+        lines += [a.note, ""]
+    with open(a.out_md, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"{a.out_md}: {(fb + wb) / 1e6:.2f} MB per call")
+
+
+def gpu_xcc(counter_csv: str) -> int:
+    """XCD count of the GPU agent, from the run_agent_info.csv beside a counter CSV."""
+    info = os.path.join(os.path.dirname(counter_csv), "run_agent_info.csv")
+    for r in csv.DictReader(open(info)):
+        if r.get("Agent_Type", "").upper() == "GPU" or int(r.get("Simd_Count", "0") or 0) > 0:
+            return int(r["Num_Xcc"])
+    raise SystemExit("no GPU agent in " + info)
+
+
+def cmd_counters(a):
+    rows = list(csv.DictReader(open(a.counter_csv)))
+    xcc = gpu_xcc(a.counter_csv)
+    names = sorted({r["Counter_Name"] for r in rows})
+    lines = [f"# Counters: {a.title}", "", "Command (from the repository root):", "", "```", a.command, "```", "",
+             "Mean per dispatch of each kernel (counters summed over the chip's units as rocprofv3 reports them; "
+             f"GRBM_GUI_ACTIVE is summed over the {xcc} XCDs, so one XCD's active cycles are it / {xcc}).",
+             ""]
+    have_util = "SQ_VALU_MFMA_BUSY_CYCLES" in names and "GRBM_GUI_ACTIVE" in names
+    head = ["kernel", "dispatches"] + names + (["MFMA util"] if have_util else [])
+    lines += ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    for part in a.kernels.split(";"):
+        sel = [r for r in rows if part in r["Kernel_Name"]]
+        if not sel:
+            continue
+        per = {}
+        for r in sel:
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        n = len(per[names[0]]) if names[0] in per else 0
+        vals = [statistics.mean(per[c]) if c in per else float("nan") for c in names]
+        cells = [f"`{part}`", str(n)] + [f"{v:.4g}" for v in vals]
+        if have_util:
+            util = statistics.mean(per["SQ_VALU_MFMA_BUSY_CYCLES"]) / (
+                statistics.mean(per["GRBM_GUI_ACTIVE"]) / xcc * SIMD_NUM)
+            cells.append(f"{100 * util:.1f}%")
+        lines.append("| " + " | ".join(cells) + " |")
+    lines.append("")
+    if a.note:
+        lines += [a.note, ""]
+    with open(a.out_md, "w") as fh:
+        fh.write("\n".join(lines))
+    print(a.out_md)
+
+
 def cmd_stats(a):
     rows = []
     with open(a.stats_csv) as fh:
@@ -176,8 +288,23 @@ def main():
     t.add_argument("--copy-mib", type=int, default=256)
     t.add_argument("--command", required=True)
     t.add_argument("--note", default="")
+    c = sub.add_parser("call_traffic")
+    c.add_argument("fetch_csv")
+    c.add_argument("write_csv")
+    c.add_argument("out_md")
+    c.add_argument("--calls", type=int, required=True)
+    c.add_argument("--copy-mib", type=int, default=256)
+    c.add_argument("--command", required=True)
+    c.add_argument("--note", default="")
+    k = sub.add_parser("counters")
+    k.add_argument("counter_csv")
+    k.add_argument("out_md")
+    k.add_argument("--kernels", required=True, help="parts of kernel names, separated by ;")
+    k.add_argument("--title", required=True)
+    k.add_argument("--command", required=True)
+    k.add_argument("--note", default="")
     a = ap.parse_args()
-    cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "call_traffic": cmd_call_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
