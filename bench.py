@@ -140,11 +140,14 @@ def time_workload(model, batch, steps, warmup, profile_class=None, sample=True):
 def serve_timing(model, batch, handles=2, budget=32768, reps=5):
     """The ragged mix as independent host-side requests through jl_serve:
     length-sorted micro-batches of at most `budget` tokens on `handles`
-    weight-sharing handles, one stream each; host in, host out (ids uploaded
-    and results downloaded inside the timed region)."""
+    weight-sharing handles, one stream each, each micro-batch padded to a
+    shape bucket and replayed from that bucket's captured graph; host in,
+    host out (ids uploaded and results downloaded inside the timed region)."""
     from encoder_transformer_amd import lib
     req = lib.Requests([batch.sequence(b) for b in range(batch.n_seqs)])
     hs = [model.share(budget, 4096) for _ in range(handles)]
+    for h in hs:  # micro-batches padded to shape buckets replay one graph per bucket
+        h.set_graph_cache(16)
     try:
         lib.serve(hs, req, budget)  # first use: streams, buffers, code paths
         gc.collect()
@@ -156,12 +159,15 @@ def serve_timing(model, batch, handles=2, budget=32768, reps=5):
             t = (time.perf_counter() - t0) / reps
         finally:
             gc.enable()
+        infos = [h.info() for h in hs]
     finally:
         for h in hs:
             h.close()
     return {"ms_per_queue": round(1e3 * t, 3), "requests_per_s": round(req.n / t, 1),
             "tokens_per_s": round(int(req.id_offsets[-1]) / t, 1), "micro_batches": res.n_batches,
-            "handles": handles, "max_batch_tokens": budget, "host_to_host": True}
+            "handles": handles, "max_batch_tokens": budget, "host_to_host": True,
+            "graph_captures": sum(i["graph_captures"] for i in infos),
+            "graph_replays": sum(i["graph_replays"] for i in infos)}
 
 
 def call_distribution(model, batch, calls=200):
@@ -280,12 +286,14 @@ def main():
 
     if args.only:
         b = synth.make_batch({"16x8192": 3, "ragged256": 4}[args.only])
-        tt, d, *_ = time_workload(model, b, args.steps, args.warmup, sample=False)
+        tt, d, _, _, per_class, _ = time_workload(model, b, args.steps, args.warmup, sample=False)
         fl = sum(class_flops(b, row_block=b.n_tokens >= ROW_BLOCK_MIN_TOKENS).values())
         model.close()
         print(json.dumps({"metric": f"decisions/s at {args.only}", "value": round(b.n_seqs * args.steps / tt, 2),
                           "unit": "decisions/s", "ms_per_step": round(1e3 * tt / args.steps, 3),
                           "step_mfma_frac": round(fl / (tt / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "device_ms_per_step_by_class": {k: round(v[0] / max(1, args.warmup), 4)
+                                                          for k, v in per_class.items()},
                           "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic"}))
         return
 

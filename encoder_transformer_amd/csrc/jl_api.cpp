@@ -143,7 +143,16 @@ struct Workspace {
 // offsets, marker counts, types and positions, and work lists of 8-int items
 // (attention items plus at most half as many empty ones, and 8 more).
 constexpr size_t meta_ints_for(size_t T, size_t Mm, size_t Bm) {
-  return 2 * (Bm + 1) + Bm + Mm + 12 * (T / 64 + Bm + 8) + 12 * (T / 128 + Bm + 8) + 8 * Bm + 64;
+  return 2 * (Bm + 1) + Bm + Mm + 12 * (T / 64 + Bm + 16) + 12 * (T / 128 + Bm + 16) + 8 * Bm + 64;
+}
+
+// Attention work items any batch of T tokens and B sequences can need with
+// `tile`-query items: at most T / tile + B items, laid out per XCD with at
+// most half again as many empty ones (and 8 more), rounded up to 8.  A
+// bucketed call pads its lists to this count, so that its launch shape
+// depends on (T, B) only.
+constexpr int work_capacity(int64_t T, int64_t B, int tile) {
+  return (int)(((T / tile + B) * 3 / 2 + 8 + 1 + 7) / 8 * 8);
 }
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -235,6 +244,7 @@ struct jl_model {
   std::vector<GraphEntry> graphs;
   int graph_cap = 0;
   uint64_t graph_clock = 0;
+  int64_t graph_captures = 0, graph_replays = 0;
   int *host_meta[kMetaSlots] = {};
   hipEvent_t slot_done[kMetaSlots] = {};
   bool slot_pending[kMetaSlots] = {};
@@ -799,9 +809,9 @@ extern "C" int jl_set_row_block_min_tokens(jl_model *m, int64_t min_tokens) {
 
 extern "C" int jl_model_info(const jl_model *m, int64_t *info, int n) {
   if (!m || !info) return fail(JL_ERR_ARG, "NULL argument");
-  const int64_t v[6] = {m->precision, m->max_tokens, m->max_markers, m->device, (int64_t)m->wbytes,
-                        (int64_t)m->wsbytes};
-  for (int i = 0; i < n && i < 6; ++i) info[i] = v[i];
+  const int64_t v[8] = {m->precision, m->max_tokens, m->max_markers, m->device, (int64_t)m->wbytes,
+                        (int64_t)m->wsbytes, m->graph_captures, m->graph_replays};
+  for (int i = 0; i < n && i < 8; ++i) info[i] = v[i];
   return JL_OK;
 }
 
@@ -823,8 +833,11 @@ struct Plan {
 // `dmeta_override`: device block to upload to instead of the handle's own
 // (the allocation-free entry point's, in its static scratch).  Allocates
 // nothing: the host-side vectors are the handle's, reserved at load.
+// `pad64` / `pad128` > 0: pad the 64- and 128-query attention lists with empty
+// items to exactly that many (a bucketed call; see work_capacity).
 int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, int32_t M, const int32_t *qt,
-                hipStream_t s, Plan &pl, bool to_graph_buffer = false, int *dmeta_override = nullptr) {
+                hipStream_t s, Plan &pl, bool to_graph_buffer = false, int *dmeta_override = nullptr, int pad64 = 0,
+                int pad128 = 0) {
   pl.B = B;
   pl.M = M;
   pl.T = so[B];
@@ -846,8 +859,9 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
       items64 += (len + 63) / 64;
       items128 += (len + 127) / 128;
     }
-    const size_t need = (((size_t)(B + 1) * 2 + B + M + 7) & ~size_t(7)) + 8 * (items64 + items64 / 2 + 8) +
-                        8 * (items128 + items128 / 2 + 8) + 8 * (size_t)B;
+    const size_t need = (((size_t)(B + 1) * 2 + B + M + 7) & ~size_t(7)) +
+                        8 * std::max(items64 + items64 / 2 + 8, (size_t)pad64) +
+                        8 * std::max(items128 + items128 / 2 + 8, (size_t)pad128) + 8 * (size_t)B;
     if (need > m->meta_ints) return fail(JL_ERR_CAPACITY, "batch metadata exceeds the staging buffer");
   }
   int *h = m->host_meta[slot];
@@ -944,9 +958,18 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
   };
   const size_t o_aw = o;
   int nw = 0, nw_wide = 0;
+  auto pad_to = [&](int &count, int target) -> int {
+    if (target <= 0) return JL_OK;
+    if (count > target) return fail(JL_ERR_CAPACITY, "attention work list longer than its bucket's capacity");
+    const AttnWork empty{0, 0, 0, 0, 0, 0, 0, 0};
+    for (; count < target; ++count, o += 8) std::memcpy(h + o, &empty, sizeof(empty));
+    return JL_OK;
+  };
   work_list(64, false, nw);
+  if (int rc = pad_to(nw, pad64)) return rc;
   const size_t o_aw_wide = o;
   work_list(128, true, nw_wide);
+  if (int rc = pad_to(nw_wide, pad128)) return rc;
   const size_t o_mw = o;
   for (int b = 0; b < B; ++b) {
     const int first = h[o_mo + b], cnt = h[o_mo + b + 1] - first;
@@ -1299,6 +1322,9 @@ int forward_graph(jl_model *m, const int32_t *ids, const Plan &pl, float *out, h
     }
     m->graphs.push_back({pl.T, pl.B, pl.M, pl.n_work, pl.n_work_wide, row_block, ids, out, g, ge, 0});
     hit = &m->graphs.back();
+    ++m->graph_captures;
+  } else {
+    ++m->graph_replays;
   }
   hit->last_use = ++m->graph_clock;
   JL_HIP(hipGraphLaunch(hit->exec, s));
@@ -1371,6 +1397,25 @@ extern "C" int jl_forward_static(jl_model *m, const int32_t *ids_dev, const int3
   m->prof_suspended = false;
   return finish_plan(m, pl, s, rc);
 }
+
+int jl::forward_bucketed(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
+                         const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, float *logits_dev,
+                         hipStream_t s) {
+  if (m->graph_cap <= 0 || s == nullptr || m->prof)
+    return jl_forward(m, ids_dev, seq_offsets, n_seqs, mask_positions, n_markers, qtype, logits_dev, s);
+  if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, m->max_tokens, m->max_markers))
+    return rc;
+  if (n_seqs == 0) return JL_OK;
+  DeviceGuard dg(m->device);
+  const int64_t T = seq_offsets[n_seqs];
+  Plan pl;
+  if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl, true, nullptr,
+                           work_capacity(T, n_seqs, 64), work_capacity(T, n_seqs, 128)))
+    return rc;
+  return finish_plan(m, pl, s, forward_graph(m, ids_dev, pl, logits_dev, s));
+}
+
+int jl::model_graph_cap(const jl_model *m) { return m->graph_cap; }
 
 extern "C" int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
                                const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, int32_t stage,

@@ -202,6 +202,15 @@ struct HandleBuffers {
   int64_t max_tokens, max_markers;
 };
 int handle_buffers(jl_model *m, HandleBuffers *out);
+// jl_forward for a batch already padded to its bucket's exact shape (jl_serve
+// adds filler sequences): the attention work lists are padded with empty
+// items to the capacity of (tokens, sequences), so that every batch of the
+// bucket replays one captured graph.  Falls back to jl_forward when the
+// handle's graph cache is off, on the NULL stream, or with the timer on.
+int forward_bucketed(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
+                     const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, float *logits_dev,
+                     hipStream_t s);
+int model_graph_cap(const jl_model *m);
 int model_device(const jl_model *m);
 int64_t model_max_tokens(const jl_model *m);
 int64_t model_max_markers(const jl_model *m);

@@ -99,6 +99,31 @@ ServeState *serve_state(jl_model *m, int *rc) {
   return s;
 }
 
+// Pad a micro-batch (ids in `h_ids`, offsets `so`, marker positions `mp`,
+// types `qt`) to its shape bucket with filler questions: B sequences to
+// B_b = ceil((B + 2) / 8) * 8 (F = B_b - B fillers, 2..9), M markers to
+// M_b = ceil((M + 2F) / 32) * 32 (each filler 2..20 of them), T tokens to
+// T_b = ceil((T + 21F) / 2048) * 2048 (each filler at least one token more
+// than its markers).  Filler tokens are id 0, its markers its first
+// positions after the first, its type choice.
+void bucket_pad(int32_t *h_ids, std::vector<int32_t> &so, std::vector<int32_t> &mp, std::vector<int32_t> &qt) {
+  const int64_t B = (int64_t)qt.size(), M = (int64_t)mp.size(), T = so.back();
+  const int64_t Bb = (B + 2 + 7) / 8 * 8, F = Bb - B;
+  const int64_t Mb = (M + 2 * F + 31) / 32 * 32, Tb = (T + 21 * F + 2047) / 2048 * 2048;
+  const int64_t E = Mb - M, R = Tb - T;
+  for (int64_t f = 0; f < F; ++f) {
+    // markers: 2 each, the rest dealt one by one (E - 2F <= 31 <= 18 F)
+    const int64_t extra = E - 2 * F;
+    const int64_t k = 2 + extra / F + (f < extra % F ? 1 : 0);
+    const int64_t len = R / F + (f < R % F ? 1 : 0);  // >= 21 > k
+    const int32_t start = so.back();
+    for (int64_t i = 0; i < len; ++i) h_ids[start + i] = 0;
+    for (int64_t i = 0; i < k; ++i) mp.push_back(start + 1 + (int32_t)i);
+    qt.push_back(JL_CHOICE);
+    so.push_back(start + (int32_t)len);
+  }
+}
+
 }  // namespace
 
 int jl::handle_buffers(jl_model *m, HandleBuffers *out) {
@@ -183,9 +208,19 @@ static int jl_serve_impl(jl_model *const *models, int32_t n_models, int32_t n_re
     if (int rc = jl_validate(so, 1, mask_positions + mask_offsets[r], (int32_t)M, qtype + r, L, M > 1 ? M : 2))
       return serve_fail(rc, "request " + std::to_string(r) + ": " + jl_last_error());
   }
+  // Graph mode: micro-batches padded to shape buckets (bucket_pad below), so
+  // the plan leaves the padding's headroom: at most 9 fillers, 2,047 + 189
+  // tokens and 18 + 31 markers.
+  bool bucketed = true;
+  for (int32_t k = 0; k < n_models; ++k) bucketed = bucketed && model_graph_cap(models[k]) > 0;
+  constexpr int64_t kFill = 9, kPadTokens = 2047 + 21 * kFill, kPadMarkers = 2 * kFill + 31;
+  if (bucketed && (cap_t <= kPadTokens + kMaxSeq || cap_m <= kPadMarkers + 64 || cap_s <= kFill + 1))
+    bucketed = false;  // too small a handle to leave the headroom
+  const int64_t plan_t = bucketed ? cap_t - kPadTokens : cap_t, plan_m = bucketed ? cap_m - kPadMarkers : cap_m;
+  const int64_t plan_s = bucketed ? cap_s - kFill : cap_s;
   std::vector<int32_t> order(n_requests), batch_of(n_requests);
   int32_t nb = 0;
-  if (int rc = jl_serve_plan(n_requests, id_offsets, mask_offsets, cap_t, cap_m, cap_s, order.data(),
+  if (int rc = jl_serve_plan(n_requests, id_offsets, mask_offsets, plan_t, plan_m, plan_s, order.data(),
                              batch_of.data(), &nb))
     return rc;
   std::vector<ServeState *> st(n_models);
@@ -239,14 +274,27 @@ static int jl_serve_impl(jl_model *const *models, int32_t n_models, int32_t n_re
       s->reqs.push_back(r);
     }
     const int32_t B = (int32_t)qt.size(), M = (int32_t)mp.size(), T = so.back();
+    if (bucketed) bucket_pad(s->h_ids, so, mp, qt);  // fillers after the requests
+    const int32_t Tp = so.back();
     if (hipSetDevice(s->device) != hipSuccess ||
-        hipMemcpyAsync(s->d_ids, s->h_ids, (size_t)T * 4, hipMemcpyHostToDevice, s->stream) != hipSuccess) {
+        hipMemcpyAsync(s->d_ids, s->h_ids, (size_t)Tp * 4, hipMemcpyHostToDevice, s->stream) != hipSuccess) {
       rc = serve_fail(JL_ERR_DEVICE, "id upload failed");
       break;
     }
     float *d_logits = s->d_out, *d_probs = s->d_out + s->max_markers;
     float *d_answer = s->d_out + 2 * s->max_markers, *d_maxp = d_answer + s->max_seqs;
-    if ((rc = jl_forward(m, s->d_ids, so.data(), B, mp.data(), M, qt.data(), d_logits, s->stream)) != JL_OK) break;
+    if (bucketed) {
+      rc = forward_bucketed(m, s->d_ids, so.data(), (int32_t)qt.size(), mp.data(), (int32_t)mp.size(), qt.data(),
+                            d_logits, s->stream);
+      // the read-offs of the requests only (the fillers come after them)
+      so.resize(B + 1);
+      mp.resize(M);
+      qt.resize(B);
+    } else {
+      rc = jl_forward(m, s->d_ids, so.data(), B, mp.data(), M, qt.data(), d_logits, s->stream);
+    }
+    (void)T;
+    if (rc != JL_OK) break;
     if ((rc = jl_probs(m, d_logits, so.data(), B, mp.data(), M, qt.data(), d_probs, d_answer, s->d_argmax, d_maxp,
                        s->stream)) != JL_OK)
       break;

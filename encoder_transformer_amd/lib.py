@@ -289,9 +289,10 @@ class Model:
             pass
 
     def info(self) -> dict:
-        buf = (ctypes.c_int64 * 6)()
-        _check(self._lib.jl_model_info(self._h, buf, 6))
-        keys = ["precision", "max_tokens", "max_markers", "device", "weight_bytes", "workspace_bytes"]
+        buf = (ctypes.c_int64 * 8)()
+        _check(self._lib.jl_model_info(self._h, buf, 8))
+        keys = ["precision", "max_tokens", "max_markers", "device", "weight_bytes", "workspace_bytes",
+                "graph_captures", "graph_replays"]
         return dict(zip(keys, list(buf)))
 
     # -- entry points --------------------------------------------------------

@@ -307,6 +307,14 @@ int jl_serve_plan(int32_t n_requests, const int64_t *id_offsets, const int64_t *
  * would a batch of that one request before any work starts, so a rejected
  * call leaves the outputs untouched.  Blocks until every result is in the
  * output arrays.  Calls that share a handle must not overlap.
+ * With the graph cache on (jl_set_graph_cache on every handle), each
+ * micro-batch is padded to a shape bucket and replays one captured graph per
+ * bucket: B sequences become B_b = ceil((B + 2) / 8) * 8 by F = B_b - B filler
+ * questions (choice type, token id 0, 2-20 markers each), M markers become
+ * M_b = ceil((M + 2F) / 32) * 32 and T tokens T_b = ceil((T + 21F) / 2048) *
+ * 2048; the fillers' results are discarded, and the micro-batch budget is
+ * lowered by that headroom.  A request's results then depend on the bucket
+ * (the schedule follows T_b), within the bf16 bounds of the two schedules.
  */
 int jl_serve(jl_model *const *models, int32_t n_models, int32_t n_requests, const int32_t *ids,
              const int64_t *id_offsets, const int32_t *mask_positions, const int64_t *mask_offsets,
@@ -344,8 +352,9 @@ int jl_profile(jl_model *m, int enable, uint32_t class_mask);
  * Synchronizes on the recorded events. */
 int jl_profile_read(jl_model *m, int kernel_class, double *total_ms, int64_t *launches);
 
-/* info[0..n): precision, max_tokens, max_markers, device, device bytes of
- * weights, device bytes of workspace. */
+/* info[0..n), n <= 8: precision, max_tokens, max_markers, device, device
+ * bytes of weights, device bytes of workspace, graphs captured and graph
+ * replays so far (jl_set_graph_cache). */
 int jl_model_info(const jl_model *m, int64_t *info, int n);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -147,3 +147,45 @@ def test_serve_against_the_oracle(name):
     print(name, "serve vs oracle", worst, "micro-batches", res.n_batches)
     assert worst["logit"] <= bound
     assert worst["prob"] <= BF16_PROB_BOUND
+
+
+def test_serve_graph_buckets_against_the_oracle():
+    """With the graph cache on, jl_serve pads each micro-batch to a shape
+    bucket with filler questions and replays one graph per bucket: a second
+    pass over the same queue replays every micro-batch and gives the same
+    results bitwise; both against the oracle (wide weights, all 256
+    requests of the ragged mix)."""
+    from encoder_transformer_amd import lib
+    from gpu_common import BF16_PROB_BOUND, LOGIT_TOL, golden_for, weight_file
+    from oracle import julia_oracle as jo
+    batch, seqs, ref_logits = golden_for(4, wide=True)
+    items = [batch.sequence(b) for b in seqs]
+    req = lib.Requests(items)
+    m = lib.Model(weight_file("wide"), lib.BF16, 32768, 4096)
+    h2 = m.share()
+    try:
+        for h in (m, h2):
+            h.set_graph_cache(16)
+        first = lib.serve([m, h2], req, max_batch_tokens=32768)
+        info1 = [h.info() for h in (m, h2)]
+        second = lib.serve([m, h2], req, max_batch_tokens=32768)
+        info2 = [h.info() for h in (m, h2)]
+    finally:
+        h2.close()
+        m.close()
+    caps1 = sum(i["graph_captures"] for i in info1)
+    caps2 = sum(i["graph_captures"] for i in info2)
+    reps2 = sum(i["graph_replays"] for i in info2) - sum(i["graph_replays"] for i in info1)
+    print("micro-batches", first.n_batches, "captured", caps1, "then", caps2, "replays in the second pass", reps2)
+    assert caps1 >= 1 and caps2 == caps1 and reps2 == second.n_batches
+    assert np.array_equal(first.logits, second.logits) and np.array_equal(first.probs, second.probs)
+    bound = LOGIT_TOL[("wide", "bf16")]
+    worst = {"logit": 0.0, "prob": 0.0}
+    for r, (ids, marks, qt) in enumerate(items):
+        ref = np.asarray(ref_logits[r])
+        worst["logit"] = max(worst["logit"], float(np.max(np.abs(first.request_logits(r) - ref))))
+        ro = jo.read_offs(ref, np.array([0, len(ids)]), np.asarray(marks), np.array([qt]))
+        dp = float(np.max(np.abs(first.probs[req.mask_offsets[r]:req.mask_offsets[r + 1]] - ro["probs"])))
+        worst["prob"] = max(worst["prob"], dp)
+    print("bucketed serve vs oracle", worst)
+    assert worst["logit"] <= bound and worst["prob"] <= BF16_PROB_BOUND
