@@ -366,12 +366,14 @@ def main():
             extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2),
                            "fp32_peak_frac": round(fl / (tt / st) / 1e12 / PEAK_FP32_TFLOPS, 4)}
         m32.close()
-        # FP8 mode (e4m3 QKV and W_i products, per-GEMM schedule), for context
+        # FP8 mode (e4m3 QKV and W_i products: the row-block schedule at
+        # 16 x 1,024, the per-GEMM one at 1 x 1,024), for context
         m8 = lib.Model(path, lib.FP8, max_tokens=20_000, max_markers=1024, device=0)
         m8.set_graph_cache(2)
         for name, b, st in [("16x1024_fp8", b2, 10), ("1x1024_fp8", b1, 20)]:
-            tt, *_ = time_workload(m8, b, st, 2, sample=False)
-            extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2)}
+            tt, _, _, _, pc, _ = time_workload(m8, b, st, 2, sample=False)
+            extra[name] = {"ms_per_step": round(1e3 * tt / st, 3), "decisions_per_s": round(b.n_seqs * st / tt, 2),
+                           "device_ms_per_step_by_class": {k: round(v[0] / 2, 4) for k, v in pc.items() if v[1]}}
         m8.close()
         result["extra"] = extra
     result["ms_per_call_1x1024"] = result.get("extra", {}).get("1x1024_ms_per_call")

@@ -101,6 +101,21 @@ void pack_fragments(const float *W, int N, int K, const std::vector<int> *row_of
     }
 }
 
+// e4m3 codes [N, 384] (row-major) in the row-block kernel's fp8 fragment
+// order: block (gn, s) of 16 rows x 128 k is 2 KB, half h of it 1 KB in which
+// lane l holds row 16 gn + l % 16, k = 128 s + 32 (l / 16) + 16 h + e at byte
+// 16 l + e; blocks gn-major, so a wave's fragment is two contiguous 1 KB loads.
+void pack_fragments8(const uint8_t *codes, int N, int K, uint8_t *out) {
+  const int ks = K / 128;
+  for (int gn = 0; gn < N / 16; ++gn)
+    for (int s = 0; s < ks; ++s)
+      for (int h = 0; h < 2; ++h) {
+        uint8_t *blk = out + (((size_t)gn * ks + s) * 2 + h) * 1024;
+        for (int l = 0; l < 64; ++l)
+          std::memcpy(blk + 16 * l, codes + (size_t)(16 * gn + (l & 15)) * K + 128 * s + 32 * (l >> 4) + 16 * h, 16);
+      }
+}
+
 struct LayerW {
   const float *attn_norm = nullptr;
   const void *Wqkv = nullptr, *Wo = nullptr, *Wi = nullptr, *Wout = nullptr;
@@ -110,6 +125,8 @@ struct LayerW {
   // JL_FP8: e4m3 codes [N, 384] of the QKV (layers 1-21) and W_i rows and each row's scale
   const void *Wqkv8 = nullptr, *Wi8 = nullptr;
   const float *sqkv = nullptr, *si = nullptr;
+  // the same codes in fp8 fragment order for the row-block layer kernel
+  const void *pWqkv8 = nullptr, *pWi8 = nullptr;
 };
 struct HeadW {
   const void *in_w = nullptr, *out_w = nullptr, *l1_w = nullptr, *l2_w = nullptr;
@@ -549,8 +566,8 @@ static int jl_load_weights_impl(const char *path, int precision, int64_t max_tok
   // e4m3 codes of a matrix [rows, cols] (rows through `row_of`): each row
   // times 448 / max |row| (in FP32), and the row scales max |row| / 448
   auto put_e4m3 = [&](const float *src, size_t rows, size_t cols, const void **dst, const float **scale,
-                      const std::vector<int> *row_of) {
-    const size_t off = ar.add(rows * cols), soff = ar.add(rows * 4);
+                      const std::vector<int> *row_of, const void **packed) {
+    const size_t off = ar.add(rows * cols), soff = ar.add(rows * 4), poff = ar.add(rows * cols);
     uint8_t *d = (uint8_t *)(ar.buf.data() + off);
     float *sc = (float *)(ar.buf.data() + soff);
     for (size_t r = 0; r < rows; ++r) {
@@ -561,8 +578,10 @@ static int jl_load_weights_impl(const char *path, int precision, int64_t max_tok
       sc[r] = amax > 0.f ? amax / 448.0f : 1.0f;
       for (size_t c = 0; c < cols; ++c) d[r * cols + c] = f32_to_e4m3(sr[c] * rc);
     }
+    pack_fragments8(d, (int)rows, (int)cols, (uint8_t *)(ar.buf.data() + poff));
     pend.push_back({dst, off});
     pend.push_back({(const void **)scale, soff});
+    pend.push_back({packed, poff});
   };
   auto put_packed = [&](const float *src, int rows, int cols, const void **dst, const std::vector<int> *row_of,
                         const std::vector<float> *row_scale = nullptr) {
@@ -624,7 +643,7 @@ static int jl_load_weights_impl(const char *path, int precision, int64_t max_tok
     t = scale_q_rows(t, 3 * D, D);
     put_elem(t, 3 * D, D, &m->L[l].Wqkv, nullptr);
     if (bf) put_packed(t, 3 * D, D, &m->L[l].pWqkv, nullptr);
-    if (f8 && l != 0) put_e4m3(t, 3 * D, D, &m->L[l].Wqkv8, &m->L[l].sqkv, nullptr);
+    if (f8 && l != 0) put_e4m3(t, 3 * D, D, &m->L[l].Wqkv8, &m->L[l].sqkv, nullptr, &m->L[l].pWqkv8);
     GET(p + "attn.Wo.weight", D, D);
     put_elem(t, D, D, &m->L[l].Wo, nullptr);
     if (bf) put_packed(t, D, D, &m->L[l].pWo, nullptr);
@@ -632,7 +651,7 @@ static int jl_load_weights_impl(const char *path, int precision, int64_t max_tok
     put_f32(t, D, &m->L[l].mlp_norm);
     GET(p + "mlp.Wi.weight", 2 * kGeglu, D);
     put_elem(t, 2 * kGeglu, D, &m->L[l].Wi, &geglu_rows);
-    if (f8) put_e4m3(t, 2 * kGeglu, D, &m->L[l].Wi8, &m->L[l].si, &geglu_rows);
+    if (f8) put_e4m3(t, 2 * kGeglu, D, &m->L[l].Wi8, &m->L[l].si, &geglu_rows, &m->L[l].pWi8);
     if (bf) put_packed(t, 2 * kGeglu, D, &m->L[l].pWi, &geglu_rows, &gate_half);
     GET(p + "mlp.Wo.weight", D, kGeglu);
     put_elem(t, D, kGeglu, &m->L[l].Wout, nullptr);
@@ -1092,7 +1111,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
     JL_HIP(hipMemcpyAsync(out, src, rows * D * 4, hipMemcpyDeviceToDevice, s));
     return JL_OK;
   };
-  const bool row_block = m->precision == JL_BF16 && T >= m->row_block_min_tokens;
+  const bool row_block = m->precision != JL_FP32 && T >= m->row_block_min_tokens;
   if (row_block) {  // the embedding kernel also computes the first layer's QKV
     EmbedArgs ea{};
     ea.ids = ids;
@@ -1140,10 +1159,16 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
       la.pos = w.pos;
       la.qkv_out = (__bf16 *)w.qkv;
       la.T = T;
+      if (W.pWi8) {  // JL_FP8: e4m3 W_i and next QKV
+        la.Wi8 = (const uint8_t *)W.pWi8;
+        la.si = W.si;
+      }
       if (l + 1 < kLayers && stop != l + 1) {
         const LayerW &N = m->L[l + 1];
         la.attn_norm_next = N.attn_norm;
         la.Wqkv_next = (const __bf16 *)N.pWqkv;
+        la.Wqkv8_next = (const uint8_t *)N.pWqkv8;
+        la.sqkv_next = N.sqkv;
         la.rope_cos_next = m->rope_cos[layer_is_global(l + 1)];
         la.rope_sin_next = m->rope_sin[layer_is_global(l + 1)];
       } else if (l + 1 == kLayers && stop != kLayers) {
@@ -1288,7 +1313,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
 
 // Replay (capturing on first use) the forward pass of this batch shape.
 int forward_graph(jl_model *m, const int32_t *ids, const Plan &pl, float *out, hipStream_t s) {
-  const bool row_block = m->precision == JL_BF16 && pl.T >= m->row_block_min_tokens;
+  const bool row_block = m->precision != JL_FP32 && pl.T >= m->row_block_min_tokens;
   jl_model::GraphEntry *hit = nullptr;
   for (auto &g : m->graphs)
     if (g.T == pl.T && g.B == pl.B && g.M == pl.M && g.n_work == pl.n_work && g.n_work_wide == pl.n_work_wide &&

@@ -101,6 +101,14 @@ struct LayerArgs {
   const float *type_rows;       //   type table [3, 384],
   const int *qtype;             //   question type per sequence,
   const int *tok_seq;           //   sequence of each token
+  // e4m3 products (JL_FP8), or nullptr for bf16: W_i and the next encoder
+  // layer's QKV as e4m3 codes in the 128-k fragment order of the fp8
+  // matrix-core product, with one scale per (packed) weight row; the
+  // LayerNorm rows that feed them are scaled and coded per row in the kernel
+  const uint8_t *Wi8;           // [2304 x 384] codes, GEGLU rows interleaved by 16
+  const float *si;              // [2304] row scales, same order
+  const uint8_t *Wqkv8_next;    // [1152 x 384] codes of the next encoder layer
+  const float *sqkv_next;       // [1152]
   int T;
 };
 

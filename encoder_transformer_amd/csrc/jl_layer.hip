@@ -30,6 +30,21 @@ DI void start_wi(WPipe<NTI, PD> &w, const LayerArgs &a, int c, int lane, int wav
   for (int j = 0; j < NTI; ++j) ng[j] = 32 * c + NTI * wave + j;
   wp_start(w, a.Wi, KSD, ng, 0, lane);
 }
+// e4m3 W_i (JL_FP8) in halves of a chunk: half q of chunk c (NTI groups per
+// wave) is wave w's GELU/gate group pair 32 c + NTI w + 2 q, + 1.
+DI void start_wi8h(Pipe28 &w, const LayerArgs &a, int c, int q, int nti, int lane, int wave) {
+  const int ng[2] = {32 * c + nti * wave + 2 * q, 32 * c + nti * wave + 2 * q + 1};
+  wp8_start(w, a.Wi8, ng, lane);
+}
+// Scales of such a half's sums: row and column scales, the gate column halved
+// as the bf16 packing halves the gate rows.
+DI void scale_wi8h(f32x4 (&H)[4][4], const LayerArgs &a, int c, int q, int nti, const float (&srow)[4], int lane,
+                   int wave) {
+  const int ng[2] = {32 * c + nti * wave + 2 * q, 32 * c + nti * wave + 2 * q + 1};
+  scale8<2>(H, ng, a.si, srow, lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) H[i][1] *= 0.5f;
+}
 // W_out k-steps of chunk c for wave w's 48 output columns.
 DI void start_wout(PipeO &w, const LayerArgs &a, int c, int lane, int wave) {
   const int ng[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
@@ -53,6 +68,19 @@ DI float geglu_half_gate(float z, float gh) {
   return (z + u) * gh;
 }
 
+// GEGLU of the pair (H[.][0], H[.][1]) as pair p of a chunk of NTI groups per
+// wave, into the chunk buffer sHb.
+template <int NTI>
+DI void geglu_pair(const f32x4 (&H)[4][4], bf16 *sHb, int p, int lane, int wave) {
+  constexpr int KS = 2 * NTI;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int col = 8 * NTI * wave + 16 * p + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    put4(sHb, 16 * i + r16, col, KS, geglu_half_gate(H[i][0][0], H[i][1][0]), geglu_half_gate(H[i][0][1], H[i][1][1]),
+         geglu_half_gate(H[i][0][2], H[i][1][2]), geglu_half_gate(H[i][0][3], H[i][1][3]));
+}
+
 // GEGLU of H[.][0, NTI) into the chunk buffer sHb (fragment order, 64 x 64 NTI).
 template <int NTI>
 DI void geglu(const f32x4 (&H)[4][4], bf16 *sHb, int lane, int wave) {
@@ -71,9 +99,14 @@ DI void geglu(const f32x4 (&H)[4][4], bf16 *sHb, int lane, int wave) {
 
 // kHeadNext: after the last layer, continue into the first head layer's
 // LayerNorm (with shift) and biased in-projection, without RoPE.
-template <bool kHeadNext>
+// kF8: W_i and the next encoder layer's QKV take e4m3 operands (their
+// LayerNorm tiles coded per row into sA); the head's in-projection, the
+// out-projection and W_out stay bf16.
+template <bool kHeadNext, bool kF8>
 __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sA[RB * kWidth];  // 48 KB: o, then u, then u'
+  __shared__ float sAmax[kF8 ? NW : 1][RB];                       // e4m3: partial row maxima
+  uint8_t *sA8 = reinterpret_cast<uint8_t *>(sA);                 // e4m3: the coded u, then u'
   __shared__ __attribute__((aligned(16))) bf16 sH0[RB * 256];    // 32 KB: GEGLU chunk buffers,
   __shared__ __attribute__((aligned(16))) bf16 sH1[RB * 256];    // 32 KB: double-buffered
   __shared__ __attribute__((aligned(16))) float sCos[RB * 32];   // 8 KB: RoPE rows of this block
@@ -92,6 +125,8 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   PipeO po;
   PipeI pi;
   Pipe2 p2;
+  Pipe28 pa8, pb8;  // e4m3 W_i halves
+  float srow[4];    // e4m3: scales of this lane's rows of the coded tile in sA8
   {
     const int ngo[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
     wp_start(po, a.Wo, KSD, ngo, 0, lane);  // needs nothing: first
@@ -120,7 +155,8 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   // 2. X = x + o . W_o^T   (wave w: columns 48w .. 48w+47, 3 groups of 16)
   f32x4 X[4][3];
   zero(X);
-  wp_run<KSD>(X, po, sA, lane, [&] { start_wi(pi, a, 0, lane, wave); });
+  if constexpr (kF8) wp_run<KSD>(X, po, sA, lane, [&] { start_wi8h(pa8, a, 0, 0, 4, lane, wave); });
+  else wp_run<KSD>(X, po, sA, lane, [&] { start_wi(pi, a, 0, lane, wave); });
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = min(row0 + 16 * i + r16, T - 1);
@@ -132,7 +168,8 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   // 3. u = LayerNorm_mlp(X) -> sA (the syncs in row_stats also retire every read of o)
   float mean[4], rstd[4];
   row_stats(X, sRed, lane, wave, mean, rstd);
-  write_ln<false>(X, a.mlp_norm, nullptr, mean, rstd, sA, lane, wave);
+  if constexpr (kF8) write_ln8<false>(X, a.mlp_norm, nullptr, mean, rstd, sAmax, sA8, srow, lane, wave);
+  else write_ln<false>(X, a.mlp_norm, nullptr, mean, rstd, sA, lane, wave);
   __syncthreads();
 
   // 4. MLP: the 1,152 intermediate columns in 4 chunks of 256 and one of 128,
@@ -143,7 +180,35 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   //    SIMD one wave's GEGLU arithmetic then overlaps its partner's
   //    matrix-core work.  X receives the chunks in order.
   f32x4 H[4][4];
-  if (lead) {
+  if constexpr (kF8) {
+    // e4m3: every wave in one order, W_i in halves (one GELU/gate pair per
+    // wave) each followed by its GEGLU, so a half's accumulators are all
+    // that the product keeps live; step c runs chunk c - 1's W_out first
+    auto run_half = [&](Pipe28 &p, int c, int q, int nti, auto nxt) {
+      zero_cols<2>(H);
+      wp8_run(H, p, sA8, lane, nxt);
+      scale_wi8h(H, a, c, q, nti, srow, lane, wave);
+    };
+    run_half(pa8, 0, 0, 4, [&] { start_wi8h(pb8, a, 0, 1, 4, lane, wave); });
+    geglu_pair<4>(H, sH0, 0, lane, wave);
+    run_half(pb8, 0, 1, 4, [&] { start_wout(po, a, 0, lane, wave); });
+    geglu_pair<4>(H, sH0, 1, lane, wave);
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 1; c < 4; ++c) {
+      bf16 *prev = (c & 1) ? sH0 : sH1, *cur = (c & 1) ? sH1 : sH0;
+      wp_run<8>(X, po, prev, lane, [&] { start_wi8h(pa8, a, c, 0, 4, lane, wave); });
+      run_half(pa8, c, 0, 4, [&] { start_wi8h(pb8, a, c, 1, 4, lane, wave); });
+      geglu_pair<4>(H, cur, 0, lane, wave);
+      run_half(pb8, c, 1, 4, [&] { start_wout(po, a, c, lane, wave); });
+      geglu_pair<4>(H, cur, 1, lane, wave);
+      __syncthreads();
+    }
+    wp_run<8>(X, po, sH1, lane, [&] { start_wi8h(pa8, a, 4, 0, 2, lane, wave); });
+    run_half(pa8, 4, 0, 2, [&] { start_wout(po, a, 4, lane, wave); });
+    geglu_pair<2>(H, sH0, 0, lane, wave);
+    __syncthreads();
+  } else if (lead) {
     zero_cols<4>(H);
     wp_run<KSD>(H, pi, sA, lane, NoNext());
     start_wout(po, a, 0, lane, wave);
@@ -267,20 +332,36 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   // 6. next layer: u' = LayerNorm_attn(next)(X) -> sA; its QKV (encoder
   //    layers rotate q and k; the head's first layer adds the bias)
   row_stats(X, sRed, lane, wave, mean, rstd);
-  write_ln<kHeadNext>(X, a.attn_norm_next, a.attn_shift_next, mean, rstd, sA, lane, wave);
-  __syncthreads();
-  qkv_phase<kHeadNext>(a.Wqkv_next, a.qkv_bias_next, a.qkv_out, sCos, sSin, sA, po, pi, p2, H, X, lane, wave, row0,
-                       T);
+  if constexpr (kF8 && !kHeadNext) {
+    PipeO8 po8;
+    write_ln8<false>(X, a.attn_norm_next, nullptr, mean, rstd, sAmax, sA8, srow, lane, wave);
+    __syncthreads();
+    qkv_phase8(a.Wqkv8_next, a.sqkv_next, a.qkv_out, sCos, sSin, sA8, srow, po8, pa8, pb8, H, X, lane, wave, row0,
+               T);
+  } else {
+    write_ln<kHeadNext>(X, a.attn_norm_next, a.attn_shift_next, mean, rstd, sA, lane, wave);
+    __syncthreads();
+    qkv_phase<kHeadNext>(a.Wqkv_next, a.qkv_bias_next, a.qkv_out, sCos, sSin, sA, po, pi, p2, H, X, lane, wave,
+                         row0, T);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_layer(const LayerArgs &a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  if (a.qkv_bias_next != nullptr)
-    layer_kernel<true><<<(a.T + RB - 1) / RB, 512, 0, s>>>(a);
-  else
-    layer_kernel<false><<<(a.T + RB - 1) / RB, 512, 0, s>>>(a);
+  const dim3 grid((a.T + RB - 1) / RB);
+  const bool f8 = a.Wi8 != nullptr;
+  if (f8 && (a.si == nullptr || (a.Wqkv_next != nullptr && a.qkv_bias_next == nullptr &&
+                                 (a.Wqkv8_next == nullptr || a.sqkv_next == nullptr))))
+    return hipErrorInvalidValue;  // e4m3 codes without their scales, or a next layer without codes
+  if (a.qkv_bias_next != nullptr) {
+    if (f8) layer_kernel<true, true><<<grid, 512, 0, s>>>(a);
+    else layer_kernel<true, false><<<grid, 512, 0, s>>>(a);
+  } else {
+    if (f8) layer_kernel<false, true><<<grid, 512, 0, s>>>(a);
+    else layer_kernel<false, false><<<grid, 512, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -399,6 +399,230 @@ DI void qkv_phase(const bf16 *Wqkv, const float *bias, bf16 *qkv_out, const floa
   }
 }
 
+// ---------------------------------------------------------------------------
+// e4m3 products (JL_FP8): v_mfma_scale_f32_16x16x128_f8f6f4 with unit block
+// scales, 128 k per product.  A fragment block (16 rows x 128 k) is 2 KB:
+// half h (k 16 h .. 16 h + 15 of each lane's 32) is 1 KB, lane l holding row
+// l % 16, k = 32 (l / 16) + 16 h + e.  Weights are packed in this order
+// (blocks gn-major, then k-step), and the LayerNorm output tile in LDS uses
+// it too (row group i, k-step s at block 3 i + s), so every load is one
+// contiguous 1 KB wave access.
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int KS8 = kWidth / 128;  // 3 k-steps of 128 over the model width
+
+DI i32x8 cat8(i32x4 lo, i32x4 hi) { return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
+DI __amdgpu_buffer_rsrc_t codes_rsrc(const uint8_t *W) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(W), (short)0, 0x7fffffff, 0x00020000);
+}
+DI i32x8 ldw8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return cat8(__builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0)),
+              __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 1024, 0)));
+}
+DI i32x8 lds_frag8(const uint8_t *p) {
+  return cat8(*reinterpret_cast<const i32x4 *>(p), *reinterpret_cast<const i32x4 *>(p + 1024));
+}
+
+// An e4m3 weight pipe: PD of the 3 k-steps of a wave's NT fragment columns in flight.
+template <int NT, int PD>
+struct WPipe8 {
+  const uint8_t *W;
+  int vo[NT];
+  i32x8 fb[PD][NT];
+};
+
+template <int NT, int PD>
+DI void wp8_start(WPipe8<NT, PD> &w, const uint8_t *Wp, const int (&ng)[NT], int lane) {
+  static_assert(PD <= KS8, "prefetch depth");
+  w.W = Wp;
+  const __amdgpu_buffer_rsrc_t rw = codes_rsrc(Wp);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) w.vo[j] = ng[j] * (KS8 * 2048) + lane * 16;
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) w.fb[p][j] = ldw8(rw, w.vo[j], p * 2048);
+}
+
+// acc[i][j] += (codes(A) . codes(W)^T)^T over the 384-wide e4m3 tile sA8 for a
+// started pipe (the unscaled sums of code products).  A weight fragment is
+// reloaded right after the products that read it (with PD = 1 the next
+// column's products then cover its latency); the activation fragments of the
+// next k-step are read once every column is done.  `next()` runs once every
+// load of this product is issued.
+template <int NT, int PD, int NTA, class Next>
+DI void wp8_run(f32x4 (&acc)[4][NTA], WPipe8<NT, PD> &w, const uint8_t *sA8, int lane, Next next) {
+  static_assert(NT <= NTA, "accumulator columns");
+  // the tile is read afresh by every product: kept from one product to the
+  // next, all its fragments (96 registers) would stay live
+  asm volatile("" ::: "memory");
+  const __amdgpu_buffer_rsrc_t rw = codes_rsrc(w.W);
+  const uint8_t *ap = sA8 + lane * 16;
+  i32x8 fa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = lds_frag8(ap + (i * KS8) * 2048);
+#pragma unroll
+  for (int s = 0; s < KS8; ++s) {
+    const int p = s % PD;
+    if (s == KS8 - PD) next();
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.fb[p][j], fa[i], acc[i][j], 0, 0, 0, 127, 0,
+                                                                     127);
+      if (s + PD < KS8) w.fb[p][j] = ldw8(rw, w.vo[j], (s + PD) * 2048);
+    }
+    if (s + 1 < KS8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = lds_frag8(ap + (i * KS8 + s + 1) * 2048);
+    }
+    // a k-step's loads stay in it: no load of a later step moves up (that
+    // would keep all three steps' fragments live at once)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The e4m3 LayerNorm tile: y = gain * (X - mean) * rstd (+ shift) in FP32 as
+// in write_ln, each row's largest magnitude over all 384 columns (reduced
+// over the 4 lane groups and the 8 waves through sAmax, one barrier), codes
+// of y * fl(448 / amax) into sA8, and the row scale fl(amax / 448) (1 for an
+// all-zero row) returned per row group of this lane.
+template <bool kShift>
+DI void write_ln8(const f32x4 (&X)[4][3], const float *__restrict__ gain, const float *__restrict__ shift,
+                  const float (&mean)[4], const float (&rstd)[4], float (*sAmax)[RB], uint8_t *sA8,
+                  float (&srow)[4], int lane, int wave) {
+  const int r16 = lane & 15, g = lane >> 4;
+  f32x4 y[4][3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int col = 48 * wave + 16 * j + 4 * g;
+    const f32x4 gm = *reinterpret_cast<const f32x4 *>(gain + col);
+    f32x4 sh = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kShift) sh = *reinterpret_cast<const f32x4 *>(shift + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        y[i][j][r] = (X[i][j][r] - mean[i]) * rstd[i] * gm[r];
+        if constexpr (kShift) y[i][j][r] = y[i][j][r] + sh[r];
+      }
+  }
+  float am[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a = fmaxf(a, fabsf(y[i][j][r]));
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    a = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    am[i] = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sAmax[wave][16 * i + r16] = am[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) a = fmaxf(a, sAmax[w][16 * i + r16]);
+    const float rc = a > 0.f ? 448.0f / a : 1.0f;
+    srow[i] = a > 0.f ? a / 448.0f : 1.0f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      // columns k .. k+3 of row 16 i + r16: k-step k / 128, lane group
+      // (k % 128) / 32, half (k % 32) / 16, byte k % 16
+      const int k = 48 * wave + 16 * j + 4 * g, kk = k & 127;
+      int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[i][j][0] * rc, y[i][j][1] * rc, 0, false);
+      c = __builtin_amdgcn_cvt_pk_fp8_f32(y[i][j][2] * rc, y[i][j][3] * rc, c, true);
+      *reinterpret_cast<int *>(sA8 + ((i * KS8 + (k >> 7)) * 2 + ((kk >> 4) & 1)) * 1024 +
+                               (r16 + 16 * (kk >> 5)) * 16 + (kk & 15)) = c;
+    }
+  }
+}
+
+// H[i][j] *= srow[i] * scale(column): the e4m3 products' scales, column scales
+// of fragment group ng[j] (16 columns) from `cs`.
+template <int NT, int NTA>
+DI void scale8(f32x4 (&H)[4][NTA], const int (&ng)[NT], const float *cs, const float (&srow)[4], int lane) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const f32x4 c = *reinterpret_cast<const f32x4 *>(cs + 16 * ng[j] + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) H[i][j][r] = H[i][j][r] * (srow[i] * c[r]);
+  }
+}
+
+// An empty instruction that reads accumulators: the products that produce
+// them are complete here, not sunk into the epilogue's per-row branches
+// (which would keep every fragment they read live until then).  Emits no
+// code.
+template <int NT, int NTA>
+DI void pin_acc(const f32x4 (&H)[4][NTA]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) asm volatile("" ::"v"(H[i][j]));
+}
+
+using PipeO8 = WPipe8<3, 1>;
+using Pipe28 = WPipe8<2, 1>;
+
+// The QKV projection with e4m3 operands (the codes of the LayerNorm tile sA8,
+// row scales srow), in qkv_phase's order, each q/k head taken as its two
+// rotation halves (column groups d, d + 32), so that one product keeps 32
+// accumulators live; then RoPE on q and k and the stores.
+DI void qkv_phase8(const uint8_t *Wqkv8, const float *sqkv, bf16 *qkv_out, const float *sCos, const float *sSin,
+                   const uint8_t *sA8, const float (&srow)[4], PipeO8 &po, Pipe28 &pa, Pipe28 &pb, f32x4 (&H)[4][4],
+                   f32x4 (&X)[4][3], int lane, int wave, int row0, int T) {
+  const int half_col = 512 + 64 * (wave >> 1), half = wave & 1;
+  const int ngw0[2] = {4 * wave, 4 * wave + 2}, ngw1[2] = {4 * wave + 1, 4 * wave + 3};
+  int ngh[2], ngv[3];
+  ng_qk_half(ngh, wave);
+  ng_v(ngv, wave);
+  // the next product's pipe starts once this one's products are issued, its
+  // loads in flight during the epilogue
+  auto qk_half = [&](Pipe28 &p, const int (&ng)[2], int col, int hf, auto nxt) {
+    zero_cols<2>(H);
+    wp8_run(H, p, sA8, lane, NoNext());
+    scale8<2>(H, ng, sqkv, srow, lane);
+    pin_acc<2>(H);
+    nxt();
+    rope_store<2>(H, sCos, sSin, qkv_out, col, hf, lane, row0, T);
+  };
+  auto v_part = [&](auto nxt) {
+    zero(X);
+    wp8_run(X, po, sA8, lane, NoNext());
+    scale8<3>(X, ngv, sqkv, srow, lane);
+    pin_acc<3>(X);
+    nxt();
+    v_store(X, qkv_out, lane, wave, row0, T);
+  };
+  if (wave < NW / 2) {
+    wp8_start(pa, Wqkv8, ngw0, lane);
+    qk_half(pa, ngw0, 64 * wave, 0, [&] { wp8_start(pb, Wqkv8, ngw1, lane); });
+    qk_half(pb, ngw1, 64 * wave, 1, [&] { wp8_start(pa, Wqkv8, ngh, lane); });
+    qk_half(pa, ngh, half_col, half, [&] { wp8_start(po, Wqkv8, ngv, lane); });
+    v_part(NoNext());
+  } else {
+    wp8_start(pa, Wqkv8, ngh, lane);
+    qk_half(pa, ngh, half_col, half, [&] { wp8_start(po, Wqkv8, ngv, lane); });
+    v_part([&] { wp8_start(pb, Wqkv8, ngw0, lane); });
+    qk_half(pb, ngw0, 64 * wave, 0, [&] { wp8_start(pa, Wqkv8, ngw1, lane); });
+    qk_half(pa, ngw1, 64 * wave, 1, NoNext());
+  }
+}
+
 // Stage the RoPE table rows of this block's positions (one per row, from
 // pos_of(r)) in LDS: 64 rows x 32 angles of each table.
 template <class PosOf>

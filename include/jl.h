@@ -48,8 +48,8 @@ enum jl_precision {
                /* activations per token row inside the product, FP32            */
                /* accumulation, both scales applied to the FP32 result; the     */
                /* reduced-precision projection mode of "Julia-1 MLX",           */
-               /* Performance (precision), on gfx950's fp8 matrix cores.        */
-               /* Always the per-GEMM schedule                                  */
+               /* Performance (precision), on gfx950's fp8 matrix cores, in     */
+               /* both schedules                                                */
 };
 
 enum jl_status {
@@ -181,13 +181,13 @@ int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offs
                     const int32_t *qtype, int32_t stage, float *out_dev, void *stream);
 
 /*
- * Tuning: bf16 batches of at least `min_tokens` packed tokens run each encoder
- * layer as one attention launch plus one row-block layer launch (64 token rows
- * per work-group: out-projection, LayerNorm, GEGLU MLP and the next layer's
- * QKV with the rows resident in LDS, weights streamed from L2); smaller
- * batches, and the FP32 mode, run one launch per GEMM.  Default 8,192; 0
+ * Tuning: bf16 and FP8 batches of at least `min_tokens` packed tokens run
+ * each encoder layer as one attention launch plus one row-block layer launch
+ * (64 token rows per work-group: out-projection, LayerNorm, GEGLU MLP and the
+ * next layer's QKV with the rows resident in LDS, weights streamed from L2);
+ * smaller batches, and the FP32 mode, run one launch per GEMM.  Default 8,192; 0
  * forces the row-block path, INT64_MAX the per-GEMM path.  Both compute the
- * same function; their bf16 roundings differ in summation order only.
+ * same function; their roundings differ in summation order only.
  */
 int jl_set_row_block_min_tokens(jl_model *m, int64_t min_tokens);
 
