@@ -148,10 +148,12 @@ struct ProfRec {
 //   x [T, 384] FP32 residual stream (the head's h from the final LayerNorm on);
 //   qkv [T, 1152] (head layer 2: keys|values [T, 768]); o [T, 384] attention
 //   output, also the normalized GEMM operand u; act [T, 1536] GEGLU output /
-//   head FFN hidden; pos, tok_seq [T] int32; marker rows z, sh, zu [M, 384]
-//   FP32, qm, om [M, 384], actm [M, 1536] (element type).
+//   head FFN hidden; pos, tok_seq [T] int32; marker rows z [M, 384] FP32,
+//   qm, om [M, 384], actm [M, 1536] (element type); the scorer's partial
+//   sums score_part [M, 6] FP32 and counters score_cnt [M / 16] int32.
 struct Workspace {
-  float *x = nullptr, *z = nullptr, *zu = nullptr, *sh = nullptr;
+  float *x = nullptr, *z = nullptr, *score_part = nullptr;
+  int *score_cnt = nullptr;
   char *qkv = nullptr, *o = nullptr, *act = nullptr, *qm = nullptr, *om = nullptr, *actm = nullptr;
   int *pos = nullptr, *tok_seq = nullptr;
 };
@@ -177,8 +179,9 @@ constexpr size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // Bytes of layout_workspace's layout (same pieces, same order).
 constexpr size_t workspace_bytes(size_t T, size_t Mm, size_t es, size_t meta_ints, int n_meta) {
   const size_t D = kWidth;
-  const size_t parts[12] = {T * D * 4,  T * 3 * D * es, T * D * es,  T * kHeadFfn * es,  T * 4,      T * 4,
-                            Mm * D * 4, Mm * D * es,    Mm * D * es, Mm * kHeadFfn * es, Mm * D * 4, Mm * D * 4};
+  const size_t parts[12] = {T * D * 4,  T * 3 * D * es, T * D * es,  T * kHeadFfn * es,  T * 4,
+                            T * 4,      Mm * D * 4,     Mm * D * es, Mm * D * es,         Mm * kHeadFfn * es,
+                            Mm * (kWidth / 64) * 4,     (Mm + 15) / 16 * 4};
   size_t off = 0;
   for (size_t p : parts) off = align256(off) + p;
   for (int k = 0; k < n_meta; ++k) off = align256(off) + meta_ints * 4;
@@ -208,8 +211,8 @@ size_t layout_workspace(char *base, size_t T, size_t Mm, size_t es, size_t meta_
   w->qm = take(Mm * D * es);
   w->om = take(Mm * D * es);
   w->actm = take(Mm * kHeadFfn * es);
-  w->sh = (float *)take(Mm * D * 4);
-  w->zu = (float *)take(Mm * D * 4);
+  w->score_part = (float *)take(Mm * (kWidth / 64) * 4);
+  w->score_cnt = (int *)take((Mm + 15) / 16 * 4);
   for (int k = 0; k < n_meta; ++k) meta[k] = (int *)take(meta_ints * 4);
   return align256(off);  // == workspace_bytes(T, Mm, es, meta_ints, n_meta)
 }
@@ -1276,7 +1279,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
                                        w.x, H.n1_w, H.n1_b),
                                s));
     }
-    JL_LAUNCH(JL_K_MISC, launch_gather_rows(w.x, pl.d_mp, M, w.z, s));
+    JL_LAUNCH(JL_K_MISC, launch_gather_rows(w.x, pl.d_mp, M, w.z, w.score_cnt, s));
     char *um = w.om;  // normalized marker rows, then the marker attention output
     JL_LAUNCH(JL_K_HEAD_GEMM,
               launch_ln_gemm(bf, E_STORE, with_ln(gemm(um, D, H.in_w, D, H.in_b, w.qm, D, M, D, D), w.z, H.n1_w, H.n1_b),
@@ -1304,10 +1307,9 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
   }
   if (stop == 25) return copy_out(w.z, M);
 
-  // scorer (FP32 in both modes)
-  JL_LAUNCH(JL_K_MISC, launch_ln_rows(false, w.z, m->sc_nw, m->sc_nb, M, w.zu, s));
-  JL_LAUNCH(JL_K_MISC, launch_gemm(bf, E_GELU_F32, gemm(w.zu, D, m->sc_w1, D, m->sc_b1, w.sh, D, M, D, D), s));
-  JL_LAUNCH(JL_K_MISC, launch_score_dot(w.sh, m->sc_w2, m->sc_b2, M, out, s));
+  // scorer (FP32 in every mode), one launch
+  JL_LAUNCH(JL_K_MISC, launch_score(w.z, m->sc_nw, m->sc_nb, m->sc_w1, m->sc_b1, m->sc_w2, m->sc_b2, M, w.score_part,
+                                    w.score_cnt, out, s));
   return JL_OK;
 }
 

@@ -31,7 +31,7 @@ constexpr float kQScale = (float)(1.4426950408889634 / 8.0);
 // A layer is global when its index is a multiple of 3 (layers 0, 3, ..., 21).
 inline bool layer_is_global(int l) { return l % 3 == 0; }
 
-enum EMode { E_STORE = 0, E_RESID = 1, E_GEGLU = 2, E_RELU = 3, E_GELU_F32 = 4 };
+enum EMode { E_STORE = 0, E_RESID = 1, E_GEGLU = 2, E_RELU = 3 };
 
 // C[M, N] = A[M, K] . W[N, K]^T with a fused epilogue.
 struct GemmArgs {
@@ -40,7 +40,7 @@ struct GemmArgs {
   const void *W;        // element matrix [N, ldw] (GEGLU: rows interleaved by 16)
   int ldw;
   const float *bias;    // [N] or nullptr
-  void *C;              // output (element type, or FP32 for E_RESID / E_GELU_F32)
+  void *C;              // output (element type, or FP32 for E_RESID)
   int ldc;
   int M, N, K;
   const float *rope_cos;// E_STORE: [8192, 32] table or nullptr (no RoPE)
@@ -170,9 +170,17 @@ hipError_t launch_embed_qkv(const EmbedArgs &a, hipStream_t s);
 hipError_t launch_final_ln_type(const float *x, const float *gain, const float *type_rows,
                                 const int *qtype, const int *tok_seq, int T, float *h,
                                 hipStream_t s);
-hipError_t launch_gather_rows(const float *src, const int *rows, int n, float *dst, hipStream_t s);
-hipError_t launch_score_dot(const float *hid, const float *w2, const float *b2, int n,
-                            float *logits, hipStream_t s);
+// Row groups of the scorer (16 marker rows each).
+constexpr int score_groups(int n) { return (n + 15) / 16; }
+// dst = src rows `rows` (the marker rows); also clears the scorer's
+// score_groups(n) counters for this pass.
+hipError_t launch_gather_rows(const float *src, const int *rows, int n, float *dst, int *score_cnt, hipStream_t s);
+// logits = w2 . GELU(W1 . LayerNorm(z; g, b) + b1) + b2 for the n rows of z
+// (FP32, one launch): part [n, 6] holds partial sums, cnt the row groups'
+// counters (cleared by the gather of the same pass, left cleared).
+hipError_t launch_score(const float *z, const float *g, const float *b, const float *W1, const float *b1,
+                        const float *w2, const float *b2, int n, float *part, int *cnt, float *logits,
+                        hipStream_t s);
 hipError_t launch_probs(const float *logits, const int *marker_offsets, const int *qtype,
                         int n_seqs, float *probs, float *answer, int *argmax, float *maxprob,
                         hipStream_t s);

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
   constexpr int A_BLKS = (BM / 16) * KS, B_BLKS = (BN / 16) * KS;
   constexpr int A_PER_WAVE = A_BLKS / 4, B_PER_WAVE = B_BLKS / 4;
   static_assert(A_BLKS % 4 == 0 && B_BLKS % 4 == 0, "tile must split over 4 waves");
-  static_assert(NT % 4 == 0 || EM == E_RESID || EM == E_RELU || EM == E_GELU_F32,
+  static_assert(NT % 4 == 0 || EM == E_RESID || EM == E_RELU,
                 "GEGLU and RoPE epilogues pair columns within 64-column groups");
   // bf16: an NSTAGE-stage pipeline whose loads go straight from memory into
   // LDS (16 bytes per lane, lane i at block offset 16 i: the fragment order),
@@ -726,10 +726,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
         T *C = (T *)g.C + (size_t)row * g.ldc + col0;
 #pragma unroll
         for (int j = 0; j < NT; ++j) C[j * 16] = to_elem<T>(fmaxf(v[j], 0.f));
-      } else if (EM == E_GELU_F32) {
-        float *C = (float *)g.C + (size_t)row * g.ldc + col0;
-#pragma unroll
-        for (int j = 0; j < NT; ++j) C[j * 16] = gelu_erf(v[j]);
       }
     }
   }
@@ -1163,9 +1159,14 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(const float *__restrict__ 
     for (int e = 0; e < 4; ++e) o[64 * c + e] = to_elem<T>(y[c][e]);
 }
 
+// dst[m] = src[rows[m]] (the marker rows); block 0 also clears the scorer's
+// counters of this pass (cnt[0, n_cnt)), which score_kernel leaves cleared.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const float *__restrict__ src,
                                                           const int *__restrict__ rows, int n,
-                                                          float *__restrict__ dst) {
+                                                          float *__restrict__ dst, int *__restrict__ cnt,
+                                                          int n_cnt) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_cnt; i += 256) cnt[i] = 0;
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= n) return;
@@ -1175,19 +1176,87 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const float *__restric
   for (int i = 0; i < 6; ++i) d[lane + 64 * i] = s[lane + 64 * i];
 }
 
-__global__ __launch_bounds__(256) void score_dot_kernel(const float *__restrict__ hid,
-                                                        const float *__restrict__ w2,
-                                                        const float *__restrict__ b2, int n,
-                                                        float *__restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= n) return;
-  const float *r = hid + (size_t)m * kWidth;
+// The scorer on the marker rows, FP32 in every mode: logit = w2 . GELU(W1 .
+// LayerNorm(z; g, b) + b1) + b2, one launch.  Block (rb, cb) takes rows
+// 16 rb .. 16 rb + 15 and hidden columns 64 cb .. 64 cb + 63: the rows are
+// normalized into LDS (the LayerNorm kernel's thread mapping and arithmetic),
+// wave w forms 16 hidden columns on the FP32 matrix cores (A = W1 rows, B =
+// the normalized rows; lane l feeds k = 4 (l / 16) + q of each 16-k block to
+// product q), adds b1, applies GELU and its part of the dot product; the
+// block's share of each row's logit goes to part[row][cb].  The last of the
+// kScoreBlocks blocks of a row group to finish (counted in cnt[rb]) adds the
+// shares in order of cb, plus b2, and clears cnt[rb] again.
+constexpr int kScoreBlocks = kWidth / 64;
+__global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ z, const float *__restrict__ g,
+                                                    const float *__restrict__ b, const float *__restrict__ W1,
+                                                    const float *__restrict__ b1, const float *__restrict__ w2,
+                                                    const float *__restrict__ b2, int M, float *part, int *cnt,
+                                                    float *__restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) float sU[16][kWidth + 4];  // 4 spare: conflict-free operand reads
+  __shared__ float sP[4][16];
+  __shared__ int sLast;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = blockIdx.x, cb = blockIdx.y;
+  {
+    const int lj = tid & 15, rl = tid >> 4;
+    const float *xr = z + (size_t)min(16 * rb + rl, M - 1) * kWidth + 4 * lj;
+    f32x4 y[6];
+#pragma unroll
+    for (int c = 0; c < 6; ++c) y[c] = *reinterpret_cast<const f32x4 *>(xr + 64 * c);
+    float mean, rstd;
+    ln_row16(y, mean, rstd);
+#pragma unroll
+    for (int c = 0; c < 6; ++c) {
+      const f32x4 gm = *reinterpret_cast<const f32x4 *>(g + 64 * c + 4 * lj);
+      const f32x4 sh = *reinterpret_cast<const f32x4 *>(b + 64 * c + 4 * lj);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[c][e] = (y[c][e] - mean) * rstd * gm[e] + sh[e];
+      *reinterpret_cast<f32x4 *>(&sU[rl][64 * c + 4 * lj]) = y[c];
+    }
+  }
+  __syncthreads();
+  const int lj = lane & 15, lr = lane >> 4;
+  const float *wr = W1 + (size_t)(64 * cb + 16 * wave + lj) * kWidth + 4 * lr;
+  const float *ur = &sU[lj][4 * lr];
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k0 = 0; k0 < kWidth; k0 += 16) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(wr + k0);
+    const f32x4 u = *reinterpret_cast<const f32x4 *>(ur + k0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], u[q], acc, 0, 0, 0);
+  }
+  // lane l holds hidden columns 64 cb + 16 w + 4 lr + r of row lj
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 6; ++i) s += r[lane + 64 * i] * w2[lane + 64 * i];
-  s = wave_sum(s);
-  if (lane == 0) logits[m] = s + b2[0];
+  for (int r = 0; r < 4; ++r) {
+    const int hc = 64 * cb + 16 * wave + 4 * lr + r;
+    s += gelu_erf(acc[r] + b1[hc]) * w2[hc];
+  }
+  {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  }
+  if (lr == 0) sP[wave][lj] = s;
+  __syncthreads();
+  const int row = 16 * rb + tid;
+  if (tid < 16 && row < M) part[(size_t)row * kScoreBlocks + cb] = ((sP[0][tid] + sP[1][tid]) + sP[2][tid]) + sP[3][tid];
+  __threadfence();  // this block's shares, visible device-wide before its count
+  __syncthreads();
+  if (tid == 0) sLast = atomicAdd(&cnt[rb], 1) == kScoreBlocks - 1;
+  __syncthreads();
+  if (!sLast) return;
+  __threadfence();  // every other block's shares, after their counts
+  if (tid < 16 && row < M) {
+    const float *pr = part + (size_t)row * kScoreBlocks;
+    float t = pr[0];
+#pragma unroll
+    for (int c = 1; c < kScoreBlocks; ++c) t += pr[c];
+    logits[row] = t + b2[0];
+  }
+  if (tid == 0) cnt[rb] = 0;
 }
 
 // One wave per question: softmax over its options and the three read-offs.
@@ -1256,10 +1325,6 @@ static hipError_t gemm_dispatch(int emode, const GemmArgs &a, hipStream_t s) {
       if constexpr (LNA || RF || F8) return hipErrorInvalidValue;
       else gemm_kernel<T, BM, BN, E_RESID, NS, false, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
       break;
-    case E_GELU_F32:
-      if constexpr (LNA || RF || F8) return hipErrorInvalidValue;
-      else gemm_kernel<T, BM, BN, E_GELU_F32, NS, false, KFIX><<<n_tiles, 256, 0, s>>>(a, tiles_n, n_tiles);
-      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1271,7 +1336,7 @@ hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t
   if (a.M <= 0) return hipSuccess;
   if (a.N % 128 != 0 || a.K % 64 != 0) return hipErrorInvalidValue;
   const long nt = a.N / 128;
-  if (bf16_mode && emode != E_GELU_F32) {
+  if (bf16_mode) {
     if (((a.M + 255) / 256) * nt >= 256) return gemm_dispatch<bf16, 256, 128, 2>(emode, a, s);
     if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<bf16, 128, 128, 2>(emode, a, s);
     if (((a.M + 63) / 64) * nt > 256) return gemm_dispatch<bf16, 64, 128, 2>(emode, a, s);
@@ -1306,12 +1371,6 @@ hipError_t launch_gemm(bool bf16_mode, int emode, const GemmArgs &a, hipStream_t
     }
   }
   if (((a.M + 127) / 128) * nt >= 256) return gemm_dispatch<float, 128, 128, 2>(emode, a, s);
-  // the FP32 scorer on the marker rows: narrower tiles, twice the work-groups
-  // One round of work-groups with the model's K: 4 K-steps in flight, the K
-  // loop unrolled completely.
-  if (emode == E_GELU_F32 && ((a.M + 63) / 64) * (a.N / 64) <= 256)
-    return a.K == kWidth ? gemm_dispatch<float, 64, 64, 5, false, kWidth>(emode, a, s)
-                         : gemm_dispatch<float, 64, 64, 2>(emode, a, s);
   if (((a.M + 63) / 64) * nt <= 256) {
     switch (a.K) {
       case kWidth: return gemm_dispatch<float, 64, 128, 5, false, kWidth>(emode, a, s);
@@ -1397,16 +1456,17 @@ hipError_t launch_final_ln_type(const float *x, const float *gain, const float *
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const float *src, const int *rows, int n, float *dst, hipStream_t s) {
+hipError_t launch_gather_rows(const float *src, const int *rows, int n, float *dst, int *score_cnt, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  gather_rows_kernel<<<(n + 3) / 4, 256, 0, s>>>(src, rows, n, dst);
+  gather_rows_kernel<<<(n + 3) / 4, 256, 0, s>>>(src, rows, n, dst, score_cnt, score_groups(n));
   return hipGetLastError();
 }
 
-hipError_t launch_score_dot(const float *hid, const float *w2, const float *b2, int n, float *logits,
-                            hipStream_t s) {
+hipError_t launch_score(const float *z, const float *g, const float *b, const float *W1, const float *b1,
+                        const float *w2, const float *b2, int n, float *part, int *cnt, float *logits,
+                        hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  score_dot_kernel<<<(n + 3) / 4, 256, 0, s>>>(hid, w2, b2, n, logits);
+  score_kernel<<<dim3(score_groups(n), kScoreBlocks), 256, 0, s>>>(z, g, b, W1, b1, w2, b2, n, part, cnt, logits);
   return hipGetLastError();
 }
 
