@@ -1197,9 +1197,19 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ z,
   __shared__ int sLast;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rb = blockIdx.x, cb = blockIdx.y;
+  const int lj = lane & 15, lr = lane >> 4;
+  // this lane's W1 operands (row 64 cb + 16 w + lj, k = 16 i + 4 lr .. + 3)
+  // and epilogue columns, all in flight during the LayerNorm
+  constexpr int KB = kWidth / 16;
+  f32x4 wa[KB];
+  const float *wr = W1 + (size_t)(64 * cb + 16 * wave + lj) * kWidth + 4 * lr;
+#pragma unroll
+  for (int i = 0; i < KB; ++i) wa[i] = *reinterpret_cast<const f32x4 *>(wr + 16 * i);
+  const int hc0 = 64 * cb + 16 * wave + 4 * lr;
+  const f32x4 bias1 = *reinterpret_cast<const f32x4 *>(b1 + hc0), wout = *reinterpret_cast<const f32x4 *>(w2 + hc0);
   {
-    const int lj = tid & 15, rl = tid >> 4;
-    const float *xr = z + (size_t)min(16 * rb + rl, M - 1) * kWidth + 4 * lj;
+    const int lr16 = tid & 15, rl = tid >> 4;
+    const float *xr = z + (size_t)min(16 * rb + rl, M - 1) * kWidth + 4 * lr16;
     f32x4 y[6];
 #pragma unroll
     for (int c = 0; c < 6; ++c) y[c] = *reinterpret_cast<const f32x4 *>(xr + 64 * c);
@@ -1207,32 +1217,26 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ z,
     ln_row16(y, mean, rstd);
 #pragma unroll
     for (int c = 0; c < 6; ++c) {
-      const f32x4 gm = *reinterpret_cast<const f32x4 *>(g + 64 * c + 4 * lj);
-      const f32x4 sh = *reinterpret_cast<const f32x4 *>(b + 64 * c + 4 * lj);
+      const f32x4 gm = *reinterpret_cast<const f32x4 *>(g + 64 * c + 4 * lr16);
+      const f32x4 sh = *reinterpret_cast<const f32x4 *>(b + 64 * c + 4 * lr16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[c][e] = (y[c][e] - mean) * rstd * gm[e] + sh[e];
-      *reinterpret_cast<f32x4 *>(&sU[rl][64 * c + 4 * lj]) = y[c];
+      *reinterpret_cast<f32x4 *>(&sU[rl][64 * c + 4 * lr16]) = y[c];
     }
   }
   __syncthreads();
-  const int lj = lane & 15, lr = lane >> 4;
-  const float *wr = W1 + (size_t)(64 * cb + 16 * wave + lj) * kWidth + 4 * lr;
   const float *ur = &sU[lj][4 * lr];
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k0 = 0; k0 < kWidth; k0 += 16) {
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(wr + k0);
-    const f32x4 u = *reinterpret_cast<const f32x4 *>(ur + k0);
+  for (int i = 0; i < KB; ++i) {
+    const f32x4 u = *reinterpret_cast<const f32x4 *>(ur + 16 * i);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], u[q], acc, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[i][q], u[q], acc, 0, 0, 0);
   }
   // lane l holds hidden columns 64 cb + 16 w + 4 lr + r of row lj
   float s = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int hc = 64 * cb + 16 * wave + 4 * lr + r;
-    s += gelu_erf(acc[r] + b1[hc]) * w2[hc];
-  }
+  for (int r = 0; r < 4; ++r) s += gelu_erf(acc[r] + bias1[r]) * wout[r];
   {
     const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
     s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
