@@ -30,20 +30,23 @@ DI void start_wi(WPipe<NTI, PD> &w, const LayerArgs &a, int c, int lane, int wav
   for (int j = 0; j < NTI; ++j) ng[j] = 32 * c + NTI * wave + j;
   wp_start(w, a.Wi, KSD, ng, 0, lane);
 }
-// e4m3 W_i (JL_FP8) in halves of a chunk: half q of chunk c (NTI groups per
-// wave) is wave w's GELU/gate group pair 32 c + NTI w + 2 q, + 1.
-DI void start_wi8h(Pipe28 &w, const LayerArgs &a, int c, int q, int nti, int lane, int wave) {
-  const int ng[2] = {32 * c + nti * wave + 2 * q, 32 * c + nti * wave + 2 * q + 1};
+// e4m3 W_i in units of 128 intermediate columns: unit u, wave w is the
+// GELU/gate group pair 16 u + 2 w, + 1 (intermediate columns 128 u + 16 w ..
+// + 15), so a unit's GEGLU output is 128 contiguous columns.
+DI void start_wi8u(Pipe28 &w, const LayerArgs &a, int u, int lane, int wave) {
+  const int ng[2] = {16 * u + 2 * wave, 16 * u + 2 * wave + 1};
   wp8_start(w, a.Wi8, ng, lane);
 }
-// Scales of such a half's sums: row and column scales, the gate column halved
-// as the bf16 packing halves the gate rows.
-DI void scale_wi8h(f32x4 (&H)[4][4], const LayerArgs &a, int c, int q, int nti, const float (&srow)[4], int lane,
-                   int wave) {
-  const int ng[2] = {32 * c + nti * wave + 2 * q, 32 * c + nti * wave + 2 * q + 1};
+DI void scale_wi8u(f32x4 (&H)[4][4], const LayerArgs &a, int u, const float (&srow)[4], int lane, int wave) {
+  const int ng[2] = {16 * u + 2 * wave, 16 * u + 2 * wave + 1};
   scale8<2>(H, ng, a.si, srow, lane);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) H[i][1] *= 0.5f;
+  for (int i = 0; i < 4; ++i) H[i][1] *= 0.5f;  // the gate, halved as in the bf16 packing
+}
+// W_out k-steps of unit u (4 of them) for wave w's 48 output columns.
+DI void start_wout_u(PipeO &w, const LayerArgs &a, int u, int lane, int wave) {
+  const int ng[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
+  wp_start(w, a.Wout, kGeglu / 32, ng, 4 * u, lane);
 }
 // W_out k-steps of chunk c for wave w's 48 output columns.
 DI void start_wout(PipeO &w, const LayerArgs &a, int c, int lane, int wave) {
@@ -68,16 +71,14 @@ DI float geglu_half_gate(float z, float gh) {
   return (z + u) * gh;
 }
 
-// GEGLU of the pair (H[.][0], H[.][1]) as pair p of a chunk of NTI groups per
-// wave, into the chunk buffer sHb.
-template <int NTI>
-DI void geglu_pair(const f32x4 (&H)[4][4], bf16 *sHb, int p, int lane, int wave) {
-  constexpr int KS = 2 * NTI;
+// GEGLU of the pair (H[.][0], H[.][1]) into a unit buffer (fragment order,
+// 64 x 128): wave w's columns 16 w .. 16 w + 15.
+DI void geglu_unit(const f32x4 (&H)[4][4], bf16 *sHb, int lane, int wave) {
   const int r16 = lane & 15, g = lane >> 4;
-  const int col = 8 * NTI * wave + 16 * p + 4 * g;
+  const int col = 16 * wave + 4 * g;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    put4(sHb, 16 * i + r16, col, KS, geglu_half_gate(H[i][0][0], H[i][1][0]), geglu_half_gate(H[i][0][1], H[i][1][1]),
+    put4(sHb, 16 * i + r16, col, 4, geglu_half_gate(H[i][0][0], H[i][1][0]), geglu_half_gate(H[i][0][1], H[i][1][1]),
          geglu_half_gate(H[i][0][2], H[i][1][2]), geglu_half_gate(H[i][0][3], H[i][1][3]));
 }
 
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   PipeO po;
   PipeI pi;
   Pipe2 p2;
-  Pipe28 pa8, pb8;  // e4m3 W_i halves
+  Pipe28 pa8, pb8;  // e4m3 products (W_i units, QKV rotation halves)
   float srow[4];    // e4m3: scales of this lane's rows of the coded tile in sA8
   {
     const int ngo[3] = {3 * wave, 3 * wave + 1, 3 * wave + 2};
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   // 2. X = x + o . W_o^T   (wave w: columns 48w .. 48w+47, 3 groups of 16)
   f32x4 X[4][3];
   zero(X);
-  if constexpr (kF8) wp_run<KSD>(X, po, sA, lane, [&] { start_wi8h(pa8, a, 0, 0, 4, lane, wave); });
+  if constexpr (kF8) wp_run<KSD>(X, po, sA, lane, [&] { start_wi8u(pa8, a, 0, lane, wave); });
   else wp_run<KSD>(X, po, sA, lane, [&] { start_wi(pi, a, 0, lane, wave); });
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -181,33 +182,54 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   //    matrix-core work.  X receives the chunks in order.
   f32x4 H[4][4];
   if constexpr (kF8) {
-    // e4m3: every wave in one order, W_i in halves (one GELU/gate pair per
-    // wave) each followed by its GEGLU, so a half's accumulators are all
-    // that the product keeps live; step c runs chunk c - 1's W_out first
-    auto run_half = [&](Pipe28 &p, int c, int q, int nti, auto nxt) {
+    // e4m3: the 1,152 intermediate columns in 9 units of 128, unit u's GEGLU
+    // output in buffer u % 2 (fragment order, 4 k-steps).  Waves 0-3 run
+    // step u as [W_out(u-1), W_i(u), GEGLU(u)], waves 4-7 as [GEGLU(u),
+    // W_out(u-1), W_i(u+1)], keeping the W_i accumulators across the
+    // barrier, so that on every SIMD one wave's GEGLU overlaps its partner's
+    // products; a unit's product keeps 32 accumulators live.
+    constexpr int NU = kGeglu / 128;
+    auto run_in = [&](int u) {
       zero_cols<2>(H);
-      wp8_run(H, p, sA8, lane, nxt);
-      scale_wi8h(H, a, c, q, nti, srow, lane, wave);
+      wp8_run(H, pa8, sA8, lane, NoNext());
+      scale_wi8u(H, a, u, srow, lane, wave);
+      pin_acc<2>(H);  // the products complete here, not sunk past the barrier into the GEGLU
     };
-    run_half(pa8, 0, 0, 4, [&] { start_wi8h(pb8, a, 0, 1, 4, lane, wave); });
-    geglu_pair<4>(H, sH0, 0, lane, wave);
-    run_half(pb8, 0, 1, 4, [&] { start_wout(po, a, 0, lane, wave); });
-    geglu_pair<4>(H, sH0, 1, lane, wave);
-    __syncthreads();
+    if (lead) {
+      run_in(0);  // its pipe started during the out-projection
+      start_wout_u(po, a, 0, lane, wave);
+      geglu_unit(H, sH0, lane, wave);
+      __syncthreads();
 #pragma unroll 1
-    for (int c = 1; c < 4; ++c) {
-      bf16 *prev = (c & 1) ? sH0 : sH1, *cur = (c & 1) ? sH1 : sH0;
-      wp_run<8>(X, po, prev, lane, [&] { start_wi8h(pa8, a, c, 0, 4, lane, wave); });
-      run_half(pa8, c, 0, 4, [&] { start_wi8h(pb8, a, c, 1, 4, lane, wave); });
-      geglu_pair<4>(H, cur, 0, lane, wave);
-      run_half(pb8, c, 1, 4, [&] { start_wout(po, a, c, lane, wave); });
-      geglu_pair<4>(H, cur, 1, lane, wave);
+      for (int u = 1; u < NU; ++u) {
+        bf16 *prev = (u & 1) ? sH0 : sH1, *cur = (u & 1) ? sH1 : sH0;
+        wp_run<4>(X, po, prev, lane, [&] { start_wi8u(pa8, a, u, lane, wave); });
+        run_in(u);
+        start_wout_u(po, a, u, lane, wave);
+        geglu_unit(H, cur, lane, wave);
+        __syncthreads();
+      }
+    } else {
+      run_in(0);
+      start_wi8u(pa8, a, 1, lane, wave);
+      geglu_unit(H, sH0, lane, wave);
+      run_in(1);
+      start_wout_u(po, a, 0, lane, wave);
+      __syncthreads();
+#pragma unroll 1
+      for (int u = 1; u < NU - 1; ++u) {
+        bf16 *prev = (u & 1) ? sH0 : sH1, *cur = (u & 1) ? sH1 : sH0;
+        geglu_unit(H, cur, lane, wave);
+        wp_run<4>(X, po, prev, lane, [&] { start_wi8u(pa8, a, u + 1, lane, wave); });
+        run_in(u + 1);
+        start_wout_u(po, a, u, lane, wave);
+        __syncthreads();
+      }
+      geglu_unit(H, sH0, lane, wave);  // unit 8 into buffer 0, W_out(7) from buffer 1
+      wp_run<4>(X, po, sH1, lane, NoNext());
+      start_wout_u(po, a, NU - 1, lane, wave);
       __syncthreads();
     }
-    wp_run<8>(X, po, sH1, lane, [&] { start_wi8h(pa8, a, 4, 0, 2, lane, wave); });
-    run_half(pa8, 4, 0, 2, [&] { start_wout(po, a, 4, lane, wave); });
-    geglu_pair<2>(H, sH0, 0, lane, wave);
-    __syncthreads();
   } else if (lead) {
     zero_cols<4>(H);
     wp_run<KSD>(H, pi, sA, lane, NoNext());
