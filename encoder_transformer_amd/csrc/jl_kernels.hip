@@ -737,6 +737,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 // max / sum and its output column on the same query (lane % 16).
 // ---------------------------------------------------------------------------
 
+// A fragment (8 elements per lane) through a buffer resource at byte offset voff.
+template <typename T> __device__ inline Frag<T> ldb_frag(__amdgpu_buffer_rsrc_t r, int voff);
+template <> __device__ inline Frag<bf16> ldb_frag<bf16>(__amdgpu_buffer_rsrc_t r, int voff) {
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+  return f;
+}
+template <> __device__ inline Frag<float> ldb_frag<float>(__amdgpu_buffer_rsrc_t r, int voff) {
+  Frag<float> f;
+  f.lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+  f.hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0));
+  return f;
+}
+
 // Slot of key k (0..63) in the transposed V tile: the 8 keys that lane group
 // g feeds to one 32-key step, {4g..4g+3, 16+4g..16+4g+3}, become contiguous.
 __device__ inline int vt_slot(int k) {
@@ -869,44 +883,33 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // this wave's query positions (wave-uniform)
   const int wq0 = w.q_pos0 + __builtin_amdgcn_readfirstlane(wave) * QW, wq_last = wq0 + QW - 1;
 
-  const T *kbase = (const T *)a.k + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
-  const T *vbase = (const T *)a.v + (size_t)w.kv_row0 * a.kv_stride + h * kHeadDim + (tid & 7) * 8;
-  const int last = w.kv_len - 1;
+  // K and V rows through buffer resources covering exactly this sequence's
+  // rows: a row past its end reads as zeros (a masked key), so no load
+  // clamps; the whole byte offset is per lane, where the range check sees it
+  const int row_bytes = a.kv_stride * (int)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>((const T *)a.k + (size_t)w.kv_row0 * a.kv_stride), (short)0, w.kv_len * row_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>((const T *)a.v + (size_t)w.kv_row0 * a.kv_stride), (short)0, w.kv_len * row_bytes, 0x00020000);
+  const int colb = (h * kHeadDim + (tid & 7) * 8) * (int)sizeof(T);
   // this thread's rows of tile 0 (keys lo + tid / 8 and + 32; values
-  // lo + 2 (tid / 8) and + 1); a full tile t is those rows + 64 t, a
-  // wave-uniform offset, so only the sequence's last tile clamps per row
-  const T *kp0 = kbase + (size_t)(lo + (tid >> 3)) * a.kv_stride;
-  const T *vp0 = vbase + (size_t)(lo + 2 * (tid >> 3)) * a.kv_stride;
-  const size_t r32 = (size_t)32 * a.kv_stride, r1 = (size_t)a.kv_stride;
+  // lo + 2 (tid / 8) and + 1); tile t is those rows + 64 t
+  const int koff = (lo + (tid >> 3)) * row_bytes + colb, voff = (lo + 2 * (tid >> 3)) * row_bytes + colb;
+
   // a tile's K and V rows of this thread, in register slot r: kPre3 keeps
   // all (at most 3) tiles of a window item in flight from the start, the
   // rolling path PF tiles (tile t in slot t % PF)
   constexpr int NR = kPre3 ? 3 : PF;
   Frag<T> rk0[NR], rk1[NR], rv0[NR], rv1[NR];
-  // Only the addresses depend on the branch, the loads take none: a load
-  // under a branch leaves its register to be merged at the join, and the
-  // compiler waits for the load there, not where the data is first used.
+  // No branch: a load under a branch leaves its register to be merged at
+  // the join, and the compiler waits for the load there, not where the data
+  // is first used.
   auto load_tile = [&](int t, int r) {
-    const int base = lo + t * 64;
-    const T *pk0, *pk1, *pv0, *pv1;
-    if (base + 64 <= w.kv_len) {
-      const size_t off = (size_t)(t * 64) * a.kv_stride;
-      pk0 = kp0 + off;
-      pk1 = kp0 + off + r32;
-      pv0 = vp0 + off;
-      pv1 = vp0 + off + r1;
-    } else {  // rows past the sequence end (or past the item's keys) read its last row
-      const int k0 = base + (tid >> 3);
-      const int v0 = base + 2 * (tid >> 3);
-      pk0 = kbase + (size_t)min(k0, last) * a.kv_stride;
-      pk1 = kbase + (size_t)min(k0 + 32, last) * a.kv_stride;
-      pv0 = vbase + (size_t)min(v0, last) * a.kv_stride;
-      pv1 = vbase + (size_t)min(v0 + 1, last) * a.kv_stride;
-    }
-    rk0[r] = load_frag(pk0);
-    rk1[r] = load_frag(pk1);
-    rv0[r] = load_frag(pv0);
-    rv1[r] = load_frag(pv1);
+    const int to = t * 64 * row_bytes;
+    rk0[r] = ldb_frag<T>(rsk, koff + to);
+    rk1[r] = ldb_frag<T>(rsk, koff + to + 32 * row_bytes);
+    rv0[r] = ldb_frag<T>(rsv, voff + to);
+    rv1[r] = ldb_frag<T>(rsv, voff + to + row_bytes);
   };
   auto store_tile = [&](int buf, int r) {
     const int c = (tid & 7) * 8;
@@ -951,12 +954,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // load (the q fragments), so no wait for them is left inside the loop,
   // where it would also stall on the next tile's prefetch
   load_tile(0, 0);
-  if constexpr (kPre3) {  // a window item meets at most 3 tiles; beyond n_tiles the loads are clamped and unused
+  if constexpr (kPre3) {  // a window item meets at most 3 tiles; tiles beyond n_tiles are loaded and unused
     load_tile(1, 1);
     load_tile(2, 2);
   } else {
 #pragma unroll
-    for (int r = 1; r < PF; ++r) load_tile(r, r);  // likewise clamped past the last tile
+    for (int r = 1; r < PF; ++r) load_tile(r, r);  // likewise past the last tile
   }
   store_tile(0, 0);
   // the q fragments must have arrived before the loop: otherwise the
@@ -1066,7 +1069,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   } else {
     // slot t % PF: tile t reached LDS at the end of step t - 1 (or before the
     // loop), so step t refills the slot with tile t + PF (past the last tile:
-    // clamped rows, never stored)
+    // loaded, never stored)
     for (int t0 = 0; t0 < n_tiles; t0 += PF) {
 #pragma unroll
       for (int r = 0; r < PF; ++r) {
