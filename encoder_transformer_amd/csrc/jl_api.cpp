@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -35,6 +36,22 @@ thread_local std::string g_err;
 int fail(int code, const std::string &msg) {
   g_err = msg;
   return code;
+}
+
+// HIP errors after which the device context is unusable (later HIP calls in
+// the process fail with the same error): memory faults, kernel exceptions,
+// aborts and timeouts, uncorrectable ECC errors.
+bool is_fault(hipError_t e) {
+  switch (e) {
+    case hipErrorIllegalAddress:
+    case hipErrorLaunchFailure:
+    case hipErrorLaunchTimeOut:
+    case hipErrorAssert:
+    case hipErrorECCNotCorrectable:
+      return true;
+    default:
+      return false;
+  }
 }
 
 #define JL_HIP(expr)                                                                      \
@@ -176,29 +193,43 @@ constexpr int work_capacity(int64_t T, int64_t B, int tile) {
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Every workspace piece is followed by a guard band of kGuardBytes bytes of
+// kGuardByte, written at load and never by a kernel; jl_check_guards reads
+// them back (a write past the end of a piece lands there first).
+constexpr size_t kGuardBytes = 256;
+constexpr uint8_t kGuardByte = 0xA5;
+constexpr int kWorkspacePieces = 12;
+const char *const kPieceNames[kWorkspacePieces] = {"x",  "qkv", "o",     "act",  "pos",        "tok_seq",
+                                                   "z",  "qm",  "om",    "actm", "score_part", "score_cnt"};
+
 // Bytes of layout_workspace's layout (same pieces, same order).
 constexpr size_t workspace_bytes(size_t T, size_t Mm, size_t es, size_t meta_ints, int n_meta) {
   const size_t D = kWidth;
-  const size_t parts[12] = {T * D * 4,  T * 3 * D * es, T * D * es,  T * kHeadFfn * es,  T * 4,
-                            T * 4,      Mm * D * 4,     Mm * D * es, Mm * D * es,         Mm * kHeadFfn * es,
-                            Mm * (kWidth / 64) * 4,     (Mm + 15) / 16 * 4};
+  const size_t parts[kWorkspacePieces] = {T * D * 4,  T * 3 * D * es, T * D * es,  T * kHeadFfn * es,  T * 4,
+                                          T * 4,      Mm * D * 4,     Mm * D * es, Mm * D * es,
+                                          Mm * kHeadFfn * es,         Mm * (kWidth / 64) * 4,
+                                          (Mm + 15) / 16 * 4};
   size_t off = 0;
-  for (size_t p : parts) off = align256(off) + p;
-  for (int k = 0; k < n_meta; ++k) off = align256(off) + meta_ints * 4;
+  for (size_t p : parts) off = align256(off) + p + kGuardBytes;
+  for (int k = 0; k < n_meta; ++k) off = align256(off) + meta_ints * 4 + kGuardBytes;
   return align256(off);
 }
 
 // Carve a workspace for T tokens and Mm markers (element size es) and n_meta
-// metadata blocks of meta_ints ints out of `base` (256-byte aligned pieces);
-// with base == nullptr only the size is computed.  Returns the bytes used.
+// metadata blocks of meta_ints ints out of `base` (256-byte aligned pieces,
+// each followed by its guard band); with base == nullptr only the size is
+// computed.  `guards` (or nullptr) receives each band's byte offset, pieces
+// first, then the metadata blocks.  Returns the bytes used.
 size_t layout_workspace(char *base, size_t T, size_t Mm, size_t es, size_t meta_ints, Workspace *w, int **meta,
-                        int n_meta) {
+                        int n_meta, std::vector<size_t> *guards = nullptr) {
   const size_t D = kWidth;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     off = (off + 255) & ~size_t(255);
     char *p = base ? base + off : nullptr;
     off += bytes;
+    if (guards) guards->push_back(off);
+    off += kGuardBytes;
     return p;
   };
   w->x = (float *)take(T * D * 4);
@@ -265,6 +296,13 @@ struct jl_model {
   int graph_cap = 0;
   uint64_t graph_clock = 0;
   int64_t graph_captures = 0, graph_replays = 0;
+
+  // debugging (jl_set_debug; JL_DEBUG_SYNC=1 in the environment at load sets
+  // JL_DEBUG_SYNC) and the poisoned state after a device fault
+  uint32_t debug = 0;
+  bool poisoned = false;
+  std::string poison_msg;
+  std::vector<size_t> guards;  // workspace guard band offsets (layout_workspace)
   int *host_meta[kMetaSlots] = {};
   hipEvent_t slot_done[kMetaSlots] = {};
   bool slot_pending[kMetaSlots] = {};
@@ -377,6 +415,40 @@ struct Arena {
 
 }  // namespace
 
+int jl::device_error(jl_model *m, hipError_t e, const char *what) {
+  std::string msg = std::string(what) + ": " + hipGetErrorString(e);
+  if (is_fault(e) && m && !m->poisoned) {
+    m->poisoned = true;
+    m->poison_msg = msg;
+  }
+  return fail(JL_ERR_DEVICE, msg);
+}
+
+namespace {
+
+// A HIP call on the handle `m`'s work: errors through device_error.
+#define JL_HIPM(expr)                                                   \
+  do {                                                                  \
+    hipError_t e_ = (expr);                                             \
+    if (e_ != hipSuccess) return ::jl::device_error(m, e_, #expr);     \
+  } while (0)
+
+// Entry check of every call that enqueues work on, or waits for, a handle.
+int usable(const jl_model *m) {
+  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (m->poisoned)
+    return fail(JL_ERR_DEVICE, "the handle is poisoned by an earlier device fault (" + m->poison_msg +
+                                   "); free it with jl_free");
+  return JL_OK;
+}
+
+uint32_t debug_from_env() {
+  const char *v = std::getenv("JL_DEBUG_SYNC");
+  return v && v[0] && std::strcmp(v, "0") != 0 ? (uint32_t)JL_DEBUG_SYNC : 0u;
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
@@ -457,7 +529,13 @@ int alloc_workspace(jl_model *m) {
   int *meta[jl_model::kMetaSlots + 1];
   m->wsbytes = layout_workspace(nullptr, T, Mm, m->esize, m->meta_ints, &m->w, meta, jl_model::kMetaSlots + 1);
   if (hipMalloc((void **)&m->ws, m->wsbytes) != hipSuccess) return fail(JL_ERR_OOM, "cannot allocate the device workspace");
-  layout_workspace(m->ws, T, Mm, m->esize, m->meta_ints, &m->w, meta, jl_model::kMetaSlots + 1);
+  m->guards.clear();
+  layout_workspace(m->ws, T, Mm, m->esize, m->meta_ints, &m->w, meta, jl_model::kMetaSlots + 1, &m->guards);
+  for (size_t g : m->guards)
+    if (hipMemset(m->ws + g, kGuardByte, kGuardBytes) != hipSuccess)
+      return fail(JL_ERR_DEVICE, "cannot write the workspace guard bands");
+  if (hipDeviceSynchronize() != hipSuccess) return fail(JL_ERR_DEVICE, "cannot write the workspace guard bands");
+  m->debug = debug_from_env();
   for (int k = 0; k < jl_model::kMetaSlots; ++k) m->meta[k] = meta[k];
   m->gmeta = meta[jl_model::kMetaSlots];
   m->plan_order.reserve(Bm);
@@ -818,6 +896,7 @@ extern "C" int jl_share(const jl_model *src, int64_t max_tokens, int64_t max_mar
 }
 
 ServeState *&jl::model_serve_state(jl_model *m) { return m->serve; }
+int jl::model_check(const jl_model *m) { return usable(m); }
 int jl::model_device(const jl_model *m) { return m->device; }
 int64_t jl::model_max_tokens(const jl_model *m) { return m->max_tokens; }
 int64_t jl::model_max_markers(const jl_model *m) { return m->max_markers; }
@@ -831,9 +910,35 @@ extern "C" int jl_set_row_block_min_tokens(jl_model *m, int64_t min_tokens) {
 
 extern "C" int jl_model_info(const jl_model *m, int64_t *info, int n) {
   if (!m || !info) return fail(JL_ERR_ARG, "NULL argument");
-  const int64_t v[8] = {m->precision, m->max_tokens, m->max_markers, m->device, (int64_t)m->wbytes,
-                        (int64_t)m->wsbytes, m->graph_captures, m->graph_replays};
-  for (int i = 0; i < n && i < 8; ++i) info[i] = v[i];
+  const int64_t v[10] = {m->precision, m->max_tokens,     m->max_markers,  m->device, (int64_t)m->wbytes,
+                         (int64_t)m->wsbytes, m->graph_captures, m->graph_replays, m->poisoned ? 1 : 0,
+                         (int64_t)m->debug};
+  for (int i = 0; i < n && i < 10; ++i) info[i] = v[i];
+  return JL_OK;
+}
+
+extern "C" int jl_set_debug(jl_model *m, uint32_t flags) {
+  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (flags & ~(uint32_t)(JL_DEBUG_SYNC | JL_DEBUG_REVERSE_BLOCKS | JL_DEBUG_SIMULATE_FAULT))
+    return fail(JL_ERR_ARG, "unknown debug flag");
+  m->debug = flags;
+  return JL_OK;
+}
+
+extern "C" int jl_check_guards(jl_model *m) {
+  if (int rc = usable(m)) return rc;
+  DeviceGuard dg(m->device);
+  JL_HIPM(hipDeviceSynchronize());
+  uint8_t band[kGuardBytes];
+  for (size_t i = 0; i < m->guards.size(); ++i) {
+    JL_HIPM(hipMemcpy(band, m->ws + m->guards[i], kGuardBytes, hipMemcpyDeviceToHost));
+    for (size_t k = 0; k < kGuardBytes; ++k)
+      if (band[k] != kGuardByte) {
+        const std::string piece = i < (size_t)kWorkspacePieces ? std::string("workspace buffer ") + kPieceNames[i]
+                                                               : "metadata block " + std::to_string(i - kWorkspacePieces);
+        return fail(JL_ERR_GUARD, "guard band after " + piece + " overwritten at byte " + std::to_string(k));
+      }
+  }
   return JL_OK;
 }
 
@@ -866,7 +971,7 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
   const int slot = m->next_slot;
   m->next_slot = (slot + 1) % jl_model::kMetaSlots;
   if (m->slot_pending[slot]) {
-    JL_HIP(hipEventSynchronize(m->slot_done[slot]));
+    JL_HIPM(hipEventSynchronize(m->slot_done[slot]));
     m->slot_pending[slot] = false;
   }
   pl.slot = slot;
@@ -999,7 +1104,7 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
     std::memcpy(h + o, &w, sizeof(w));
     o += 8;
   }
-  JL_HIP(hipMemcpyAsync(dmeta, h, o * 4, hipMemcpyHostToDevice, s));
+  JL_HIPM(hipMemcpyAsync(dmeta, h, o * 4, hipMemcpyHostToDevice, s));
   pl.n_work = nw;
   pl.n_work_wide = nw_wide;
   pl.d_aw_wide = (const AttnWork *)(dmeta + o_aw_wide);
@@ -1014,11 +1119,19 @@ int upload_plan(jl_model *m, const int32_t *so, int32_t B, const int32_t *mp, in
 
 // After the last launch that reads the slot's metadata (always, even after an
 // error, so that the slot is never left without a completion marker).
+// JL_DEBUG_SIMULATE_FAULT: the call reports a memory fault here, as if the
+// device had raised one (the enqueued work itself runs normally).
 int finish_plan(jl_model *m, const Plan &pl, hipStream_t s, int rc) {
-  if (hipEventRecord(m->slot_done[pl.slot], s) == hipSuccess) {
+  const hipError_t e = hipEventRecord(m->slot_done[pl.slot], s);
+  if (e == hipSuccess) {
     m->slot_pending[pl.slot] = true;
   } else if (rc == JL_OK) {
-    JL_HIP(hipStreamSynchronize(s));
+    rc = ::jl::device_error(m, e, "hipEventRecord(slot_done)");
+    if (hipStreamSynchronize(s) != hipSuccess) return rc;
+  }
+  if (rc == JL_OK && (m->debug & JL_DEBUG_SIMULATE_FAULT)) {
+    m->debug &= ~(uint32_t)JL_DEBUG_SIMULATE_FAULT;
+    return ::jl::device_error(m, hipErrorIllegalAddress, "simulated device fault (JL_DEBUG_SIMULATE_FAULT)");
   }
   return rc;
 }
@@ -1054,12 +1167,27 @@ struct Launch {
   }
 };
 
+// One launch of kernel class `cls`.  JL_DEBUG_SYNC: wait for it and check
+// the stream, so that an error is reported by the launch that caused it.
+int after_launch(jl_model *m, hipStream_t s, int cls, hipError_t e) {
+  static const char *const names[JL_K_NCLASS] = {"embed",   "qkv",       "attn_global", "attn_local", "outproj",
+                                                 "mlp_in",  "mlp_out",   "head_gemm",   "head_attn",  "misc",
+                                                 "ln",      "layer",     "head_layer"};
+  if (e == hipSuccess && (m->debug & JL_DEBUG_SYNC)) {
+    e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e == hipSuccess) return JL_OK;
+  const std::string what = std::string("kernel class ") + names[cls];
+  return ::jl::device_error(m, e, what.c_str());
+}
+
 #define JL_LAUNCH(cls, call)                                                          \
   do {                                                                                \
     Launch L_(m, s, cls);                                                             \
     hipError_t e_ = (call);                                                           \
     L_.done();                                                                        \
-    if (e_ != hipSuccess) return fail(JL_ERR_DEVICE, std::string("kernel launch failed: ") + hipGetErrorString(e_)); \
+    if (int rc_ = after_launch(m, s, cls, e_)) return rc_;                            \
   } while (0)
 
 // Sequence-wide attention takes 128-query work items (two 16-query sub-tiles
@@ -1110,8 +1238,19 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
   const size_t es = m->esize;
   const int T = pl.T, M = pl.M, D = kWidth;
   char *u = w.o;
+  // JL_DEBUG_REVERSE_BLOCKS: every kernel whose work-groups own tiles, row
+  // blocks or work items takes them in reversed order
+  const int rev = (m->debug & JL_DEBUG_REVERSE_BLOCKS) ? 1 : 0;
+  auto launch_gemm_r = [rev](bool b, int e, GemmArgs a, hipStream_t st) {
+    a.rev = rev;
+    return launch_gemm(b, e, a, st);
+  };
+  auto launch_ln_gemm_r = [rev](bool b, int e, GemmArgs a, hipStream_t st) {
+    a.rev = rev;
+    return launch_ln_gemm(b, e, a, st);
+  };
   auto copy_out = [&](const float *src, size_t rows) -> int {
-    JL_HIP(hipMemcpyAsync(out, src, rows * D * 4, hipMemcpyDeviceToDevice, s));
+    JL_HIPM(hipMemcpyAsync(out, src, rows * D * 4, hipMemcpyDeviceToDevice, s));
     return JL_OK;
   };
   const bool row_block = m->precision != JL_FP32 && T >= m->row_block_min_tokens;
@@ -1130,6 +1269,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
     ea.rope_sin = m->rope_sin[layer_is_global(0)];
     ea.qkv_out = (__bf16 *)w.qkv;
     ea.T = T;
+    ea.rev = rev;
     JL_LAUNCH(JL_K_EMBED, launch_embed_qkv(ea, s));
   } else {
     JL_LAUNCH(JL_K_EMBED, launch_embed(ids, m->emb, m->emb_norm, T, pl.d_so, pl.B, w.x, w.pos, w.tok_seq, s));
@@ -1145,6 +1285,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
   at.o = w.o;
   at.o_stride = D;
   at.work = pl.d_aw;
+  at.rev = rev;
   if (row_block) {
     // Row-block path: one attention launch and one layer launch per layer.
     for (int l = 0; l < kLayers; ++l) {
@@ -1162,6 +1303,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
       la.pos = w.pos;
       la.qkv_out = (__bf16 *)w.qkv;
       la.T = T;
+      la.rev = rev;
       if (W.pWi8) {  // JL_FP8: e4m3 W_i and next QKV
         la.Wi8 = (const uint8_t *)W.pWi8;
         la.si = W.si;
@@ -1201,16 +1343,16 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
     q.rope_sin = m->rope_sin[glob];
     q.pos = w.pos;
     q.rope_cols = 2 * D;
-    JL_LAUNCH(JL_K_QKV, launch_ln_gemm(bf, E_STORE, q, s));
+    JL_LAUNCH(JL_K_QKV, launch_ln_gemm_r(bf, E_STORE, q, s));
     at.half_window = glob ? -1 : kHalfWindow;
     JL_LAUNCH(glob ? JL_K_ATTN_GLOBAL : JL_K_ATTN_LOCAL, attention(bf, at, pl, glob, s));
-    JL_LAUNCH(JL_K_OUTPROJ, launch_gemm(bf, E_RESID, gemm(w.o, D, W.Wo, D, nullptr, w.x, D, T, D, D), s));
+    JL_LAUNCH(JL_K_OUTPROJ, launch_gemm_r(bf, E_RESID, gemm(w.o, D, W.Wo, D, nullptr, w.x, D, T, D, D), s));
     GemmArgs wi = with_ln(gemm(u, D, W.Wi8 ? W.Wi8 : W.Wi, D, nullptr, w.act, kGeglu, T, 2 * kGeglu, D), w.x,
                           W.mlp_norm, nullptr);
     wi.w_scale = W.si;
-    JL_LAUNCH(JL_K_MLP_IN, launch_ln_gemm(bf, E_GEGLU, wi, s));
+    JL_LAUNCH(JL_K_MLP_IN, launch_ln_gemm_r(bf, E_GEGLU, wi, s));
     JL_LAUNCH(JL_K_MLP_OUT,
-              launch_gemm(bf, E_RESID, gemm(w.act, kGeglu, W.Wout, kGeglu, nullptr, w.x, D, T, D, kGeglu), s));
+              launch_gemm_r(bf, E_RESID, gemm(w.act, kGeglu, W.Wout, kGeglu, nullptr, w.x, D, T, D, kGeglu), s));
     if (stop == l + 1) return copy_out(w.x, T);
   }
   // head input: final LayerNorm + type row (in place)
@@ -1226,7 +1368,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
     const HeadW &H = m->H[0];
     if (!row_block) {
       JL_LAUNCH(JL_K_HEAD_GEMM,
-                launch_ln_gemm(bf, E_STORE,
+                launch_ln_gemm_r(bf, E_STORE,
                                with_ln(gemm(u, D, H.in_w, D, H.in_b, w.qkv, 3 * D, T, 3 * D, D), w.x, H.n1_w, H.n1_b),
                                s));
     }
@@ -1253,15 +1395,16 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
         ha.kv_out = (__bf16 *)kv;
       }
       ha.T = T;
+      ha.rev = rev;
       JL_LAUNCH(JL_K_HEAD_LAYER, launch_head_layer(ha, s));
     } else {
-      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(w.o, D, H.out_w, D, H.out_b, w.x, D, T, D, D), s));
+      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm_r(bf, E_RESID, gemm(w.o, D, H.out_w, D, H.out_b, w.x, D, T, D, D), s));
       JL_LAUNCH(JL_K_HEAD_GEMM,
-                launch_ln_gemm(bf, E_RELU,
+                launch_ln_gemm_r(bf, E_RELU,
                                with_ln(gemm(u, D, H.l1_w, D, H.l1_b, w.act, kHeadFfn, T, kHeadFfn, D), w.x, H.n2_w,
                                        H.n2_b),
                                s));
-      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID,
+      JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm_r(bf, E_RESID,
                                             gemm(w.act, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, w.x, D, T, D, kHeadFfn),
                                             s));
     }
@@ -1273,7 +1416,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
     const HeadW &H = m->H[1];
     if (!row_block) {
       JL_LAUNCH(JL_K_HEAD_GEMM,
-                launch_ln_gemm(bf, E_STORE,
+                launch_ln_gemm_r(bf, E_STORE,
                                with_ln(gemm(u, D, (const char *)H.in_w + (size_t)D * D * es, D, H.in_b + D, kv, 2 * D,
                                             T, 2 * D, D),
                                        w.x, H.n1_w, H.n1_b),
@@ -1282,7 +1425,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
     JL_LAUNCH(JL_K_MISC, launch_gather_rows(w.x, pl.d_mp, M, w.z, w.score_cnt, s));
     char *um = w.om;  // normalized marker rows, then the marker attention output
     JL_LAUNCH(JL_K_HEAD_GEMM,
-              launch_ln_gemm(bf, E_STORE, with_ln(gemm(um, D, H.in_w, D, H.in_b, w.qm, D, M, D, D), w.z, H.n1_w, H.n1_b),
+              launch_ln_gemm_r(bf, E_STORE, with_ln(gemm(um, D, H.in_w, D, H.in_b, w.qm, D, M, D, D), w.z, H.n1_w, H.n1_b),
                              s));
     AttnArgs mk{};
     mk.q = w.qm;
@@ -1294,14 +1437,15 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
     mk.o_stride = D;
     mk.work = pl.d_mw;
     mk.half_window = -1;
+    mk.rev = rev;
     JL_LAUNCH(JL_K_HEAD_ATTN, launch_attention(bf, mk, pl.B, 64, s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID, gemm(w.om, D, H.out_w, D, H.out_b, w.z, D, M, D, D), s));
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm_r(bf, E_RESID, gemm(w.om, D, H.out_w, D, H.out_b, w.z, D, M, D, D), s));
     JL_LAUNCH(JL_K_HEAD_GEMM,
-              launch_ln_gemm(bf, E_RELU,
+              launch_ln_gemm_r(bf, E_RELU,
                              with_ln(gemm(um, D, H.l1_w, D, H.l1_b, w.actm, kHeadFfn, M, kHeadFfn, D), w.z, H.n2_w,
                                      H.n2_b),
                              s));
-    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm(bf, E_RESID,
+    JL_LAUNCH(JL_K_HEAD_GEMM, launch_gemm_r(bf, E_RESID,
                                           gemm(w.actm, kHeadFfn, H.l2_w, kHeadFfn, H.l2_b, w.z, D, M, D, kHeadFfn),
                                           s));
   }
@@ -1309,7 +1453,7 @@ int run_forward(jl_model *m, const Workspace &w, const int32_t *ids, const Plan 
 
   // scorer (FP32 in every mode), one launch
   JL_LAUNCH(JL_K_MISC, launch_score(w.z, m->sc_nw, m->sc_nb, m->sc_w1, m->sc_b1, m->sc_w2, m->sc_b2, M, w.score_part,
-                                    w.score_cnt, out, s));
+                                    w.score_cnt, out, rev, s));
   return JL_OK;
 }
 
@@ -1332,7 +1476,7 @@ int forward_graph(jl_model *m, const int32_t *ids, const Plan &pl, float *out, h
       (void)hipGraphDestroy(m->graphs[lru].graph);
       m->graphs.erase(m->graphs.begin() + lru);
     }
-    JL_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    JL_HIPM(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
     const int rc = run_forward(m, m->w, ids, pl, 26, out, s);
     hipGraph_t g = nullptr;
     const hipError_t e = hipStreamEndCapture(s, &g);
@@ -1340,12 +1484,12 @@ int forward_graph(jl_model *m, const int32_t *ids, const Plan &pl, float *out, h
       if (g) (void)hipGraphDestroy(g);
       return rc;
     }
-    if (e != hipSuccess) return fail(JL_ERR_DEVICE, std::string("graph capture failed: ") + hipGetErrorString(e));
+    if (e != hipSuccess) return ::jl::device_error(m, e, "graph capture");
     hipGraphExec_t ge = nullptr;
     const hipError_t ei = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
     if (ei != hipSuccess) {
       (void)hipGraphDestroy(g);
-      return fail(JL_ERR_DEVICE, std::string("graph instantiation failed: ") + hipGetErrorString(ei));
+      return ::jl::device_error(m, ei, "graph instantiation");
     }
     m->graphs.push_back({pl.T, pl.B, pl.M, pl.n_work, pl.n_work_wide, row_block, ids, out, g, ge, 0});
     hit = &m->graphs.back();
@@ -1354,7 +1498,7 @@ int forward_graph(jl_model *m, const int32_t *ids, const Plan &pl, float *out, h
     ++m->graph_replays;
   }
   hit->last_use = ++m->graph_clock;
-  JL_HIP(hipGraphLaunch(hit->exec, s));
+  JL_HIPM(hipGraphLaunch(hit->exec, s));
   return JL_OK;
 }
 
@@ -1378,7 +1522,7 @@ extern "C" int jl_set_graph_cache(jl_model *m, int max_graphs) {
 extern "C" int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
                           const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, float *logits_dev,
                           void *stream) {
-  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (int rc = usable(m)) return rc;
   if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, m->max_tokens, m->max_markers))
     return rc;
   if (n_seqs == 0) return JL_OK;
@@ -1386,8 +1530,9 @@ extern "C" int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *se
   DeviceGuard dg(m->device);
   hipStream_t s = (hipStream_t)stream;
   Plan pl;
-  // graphs need a capturable stream and no per-launch timer events
-  const bool use_graph = m->graph_cap > 0 && s != nullptr && !m->prof;
+  // graphs need a capturable stream, no per-launch timer events and no
+  // debugging switches (per-launch synchronization cannot be captured)
+  const bool use_graph = m->graph_cap > 0 && s != nullptr && !m->prof && !m->debug;
   if (int rc = upload_plan(m, seq_offsets, n_seqs, mask_positions, n_markers, qtype, s, pl, use_graph)) return rc;
   if (!use_graph) return finish_plan(m, pl, s, run_forward(m, m->w, ids_dev, pl, 26, logits_dev, s));
   return finish_plan(m, pl, s, forward_graph(m, ids_dev, pl, logits_dev, s));
@@ -1400,7 +1545,7 @@ extern "C" int jl_forward(jl_model *m, const int32_t *ids_dev, const int32_t *se
 extern "C" int jl_forward_static(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
                                  const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype,
                                  float *logits_dev, void *stream) {
-  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (int rc = usable(m)) return rc;
   const int64_t max_t = std::min(m->max_tokens, kStaticMaxTokens), max_m = std::min(m->max_markers, kStaticMaxMarkers);
   if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, max_t, max_m)) {
     if (rc == JL_ERR_CAPACITY)
@@ -1428,7 +1573,7 @@ extern "C" int jl_forward_static(jl_model *m, const int32_t *ids_dev, const int3
 int jl::forward_bucketed(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
                          const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, float *logits_dev,
                          hipStream_t s) {
-  if (m->graph_cap <= 0 || s == nullptr || m->prof)
+  if (m->graph_cap <= 0 || s == nullptr || m->prof || m->debug || m->poisoned)
     return jl_forward(m, ids_dev, seq_offsets, n_seqs, mask_positions, n_markers, qtype, logits_dev, s);
   if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, m->max_tokens, m->max_markers))
     return rc;
@@ -1447,7 +1592,7 @@ int jl::model_graph_cap(const jl_model *m) { return m->graph_cap; }
 extern "C" int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_t *seq_offsets, int32_t n_seqs,
                                const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, int32_t stage,
                                float *out_dev, void *stream) {
-  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (int rc = usable(m)) return rc;
   if (stage < 0 || stage > 25) return fail(JL_ERR_ARG, "stage must be in 0..25");
   if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, m->max_tokens, m->max_markers))
     return rc;
@@ -1463,7 +1608,7 @@ extern "C" int jl_debug_hidden(jl_model *m, const int32_t *ids_dev, const int32_
 extern "C" int jl_probs(jl_model *m, const float *logits_dev, const int32_t *seq_offsets, int32_t n_seqs,
                         const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, float *probs_dev,
                         float *answer_dev, int32_t *argmax_dev, float *maxprob_dev, void *stream) {
-  if (!m) return fail(JL_ERR_ARG, "model handle is NULL");
+  if (int rc = usable(m)) return rc;
   if (int rc = jl_validate(seq_offsets, n_seqs, mask_positions, n_markers, qtype, m->max_tokens, m->max_markers))
     return rc;
   if (n_seqs == 0) return JL_OK;
@@ -1493,16 +1638,17 @@ extern "C" int jl_profile(jl_model *m, int enable, uint32_t class_mask) {
 }
 
 extern "C" int jl_profile_read(jl_model *m, int kernel_class, double *total_ms, int64_t *launches) {
-  if (!m || !total_ms || !launches) return fail(JL_ERR_ARG, "NULL argument");
+  if (int rc = usable(m)) return rc;
+  if (!total_ms || !launches) return fail(JL_ERR_ARG, "NULL argument");
   if (kernel_class < 0 || kernel_class >= JL_K_NCLASS) return fail(JL_ERR_ARG, "bad kernel class");
   DeviceGuard dg(m->device);
   double tot = 0.0;
   int64_t n = 0;
   for (const ProfRec &r : m->prof_rec) {
     if (r.cls != kernel_class) continue;
-    JL_HIP(hipEventSynchronize(r.b));
+    JL_HIPM(hipEventSynchronize(r.b));
     float ms = 0.f;
-    JL_HIP(hipEventElapsedTime(&ms, r.a, r.b));
+    JL_HIPM(hipEventElapsedTime(&ms, r.a, r.b));
     tot += ms;
     ++n;
   }

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(512, 1) void embed_qkv_kernel(EmbedArgs a) {
   __shared__ int sPos[RB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.x * RB;
+  const int row0 = (a.rev ? gridDim.x - 1 - blockIdx.x : blockIdx.x) * RB;
   const int T = a.T;
 
   // 1. sequence and position of each row (rows past T repeat row T - 1)

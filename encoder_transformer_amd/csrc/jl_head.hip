@@ -52,7 +52,7 @@ __global__ __launch_bounds__(512, 1) void head_kernel(HeadArgs a) {
   __shared__ float sRed[2][NW][RB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.x * RB;
+  const int row0 = (a.rev ? gridDim.x - 1 - blockIdx.x : blockIdx.x) * RB;
   const int T = a.T;
 
   PipeO po;

@@ -54,6 +54,7 @@ struct GemmArgs {
   // e4m3 products (launch_ln_gemm only): W holds e4m3 codes [N, ldw] and
   // w_scale[N] each row's scale; nullptr: W is bf16/FP32
   const float *w_scale;
+  int rev;              // nonzero: work-groups take their tiles in reversed order
 };
 
 // One attention work item: up to 64 or 128 queries (the launch's tile size) of
@@ -73,6 +74,7 @@ struct AttnArgs {
   void *o; int o_stride;
   const AttnWork *work;
   int half_window;                  // < 0: attend to the whole sequence
+  int rev;                          // nonzero: work items and heads in reversed order
 };
 
 // Row-block layer kernel (bf16 only): out-projection + residual, LayerNorm,
@@ -110,6 +112,7 @@ struct LayerArgs {
   const uint8_t *Wqkv8_next;    // [1152 x 384] codes of the next encoder layer
   const float *sqkv_next;       // [1152]
   int T;
+  int rev;                      // nonzero: row blocks in reversed order
 };
 
 // Row-block head-layer kernel (bf16 only): everything of one head layer
@@ -132,6 +135,7 @@ struct HeadArgs {
   const float *bkv;             // [768]
   __bf16 *kv_out;               // [T, 768]: keys, then values
   int T;
+  int rev;                      // nonzero: row blocks in reversed order
 };
 
 // Row-block embedding kernel (bf16 only): token embedding gather + its
@@ -150,6 +154,7 @@ struct EmbedArgs {
   const float *rope_cos, *rope_sin;  // the first layer's RoPE table [8192, 32]
   __bf16 *qkv_out;              // [T, 1152]
   int T;
+  int rev;                      // nonzero: row blocks in reversed order
 };
 
 // Launchers (jl_kernels.hip, jl_layer.hip, jl_head.hip, jl_embed.hip).  `bf16` selects the bf16 instantiation, else FP32.
@@ -177,9 +182,10 @@ constexpr int score_groups(int n) { return (n + 15) / 16; }
 hipError_t launch_gather_rows(const float *src, const int *rows, int n, float *dst, int *score_cnt, hipStream_t s);
 // logits = w2 . GELU(W1 . LayerNorm(z; g, b) + b1) + b2 for the n rows of z
 // (FP32, one launch): part [n, 6] holds partial sums, cnt the row groups'
-// counters (cleared by the gather of the same pass, left cleared).
+// counters (cleared by the gather of the same pass, left cleared).  `rev`:
+// work-groups in reversed order (the result is the same bit for bit).
 hipError_t launch_score(const float *z, const float *g, const float *b, const float *W1, const float *b1,
-                        const float *w2, const float *b2, int n, float *part, int *cnt, float *logits,
+                        const float *w2, const float *b2, int n, float *part, int *cnt, float *logits, int rev,
                         hipStream_t s);
 hipError_t launch_probs(const float *logits, const int *marker_offsets, const int *qtype,
                         int n_seqs, float *probs, float *answer, int *argmax, float *maxprob,
@@ -227,6 +233,14 @@ int forward_bucketed(jl_model *m, const int32_t *ids_dev, const int32_t *seq_off
                      const int32_t *mask_positions, int32_t n_markers, const int32_t *qtype, float *logits_dev,
                      hipStream_t s);
 int model_graph_cap(const jl_model *m);
+// A HIP error seen on the handle's work: sets jl_last_error() to `what` and
+// the HIP string and returns JL_ERR_DEVICE; an error that leaves the device
+// context unusable (a memory fault, a kernel abort or timeout, an
+// uncorrectable ECC error) also marks the handle poisoned, after which every
+// call on it fails with JL_ERR_DEVICE until jl_free.
+int device_error(jl_model *m, hipError_t e, const char *what);
+// JL_OK, or the error (with its message) of a NULL or poisoned handle.
+int model_check(const jl_model *m);
 int model_device(const jl_model *m);
 int64_t model_max_tokens(const jl_model *m);
 int64_t model_max_markers(const jl_model *m);

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int tiles_n, int 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int t = xcd_tile(blockIdx.x, n_tiles);
+  const int t = xcd_tile(g.rev ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x, n_tiles);
   const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
   const int M = g.M;
   const int lr = lane & 15, lc = (lane >> 4) * 8;           // lane's row / k offset inside a block
@@ -854,9 +854,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int QW = 16 * NSUB;
   __shared__ __attribute__((aligned(16))) T sK[2][64 * KS];
   __shared__ __attribute__((aligned(16))) T sV[2][64 * KS];  // [d][slot]
-  const AttnWork w = a.work[blockIdx.x];
+  const AttnWork w = a.work[a.rev ? gridDim.x - 1 - blockIdx.x : blockIdx.x];
   if (w.n_q <= 0) return;  // padding item of the XCD layout
-  const int h = blockIdx.y;
+  const int h = a.rev ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 15, g = lane >> 4;
   const bool local = a.half_window >= 0;
@@ -1194,12 +1194,12 @@ __global__ __launch_bounds__(256) void score_kernel(const float *__restrict__ z,
                                                     const float *__restrict__ b, const float *__restrict__ W1,
                                                     const float *__restrict__ b1, const float *__restrict__ w2,
                                                     const float *__restrict__ b2, int M, float *part, int *cnt,
-                                                    float *__restrict__ logits) {
+                                                    float *__restrict__ logits, int rev) {
   __shared__ __attribute__((aligned(16))) float sU[16][kWidth + 4];  // 4 spare: conflict-free operand reads
   __shared__ float sP[4][16];
   __shared__ int sLast;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rb = blockIdx.x, cb = blockIdx.y;
+  const int rb = rev ? gridDim.x - 1 - blockIdx.x : blockIdx.x, cb = rev ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
   const int lj = lane & 15, lr = lane >> 4;
   // this lane's W1 operands (row 64 cb + 16 w + lj, k = 16 i + 4 lr .. + 3)
   // and epilogue columns, all in flight during the LayerNorm
@@ -1470,10 +1470,11 @@ hipError_t launch_gather_rows(const float *src, const int *rows, int n, float *d
 }
 
 hipError_t launch_score(const float *z, const float *g, const float *b, const float *W1, const float *b1,
-                        const float *w2, const float *b2, int n, float *part, int *cnt, float *logits,
+                        const float *w2, const float *b2, int n, float *part, int *cnt, float *logits, int rev,
                         hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  score_kernel<<<dim3(score_groups(n), kScoreBlocks), 256, 0, s>>>(z, g, b, W1, b1, w2, b2, n, part, cnt, logits);
+  score_kernel<<<dim3(score_groups(n), kScoreBlocks), 256, 0, s>>>(z, g, b, W1, b1, w2, b2, n, part, cnt, logits,
+                                                                    rev);
   return hipGetLastError();
 }
 

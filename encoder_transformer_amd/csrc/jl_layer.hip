@@ -115,7 +115,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   __shared__ float sRed[2][NW][RB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.x * RB;
+  const int row0 = (a.rev ? gridDim.x - 1 - blockIdx.x : blockIdx.x) * RB;
   const int T = a.T;
   const bool lead = wave < NW / 2;
   const bool next_layer = a.Wqkv_next != nullptr;

@@ -220,14 +220,14 @@ struct ModelScorer {
     std::vector<int32_t> qt(n_seqs, JL_CHOICE);
     float *logits_dev = hb.d_out, *probs_dev = hb.d_out + hb.max_markers;
     std::memcpy(hb.h_ids, ids, T * sizeof(int32_t));
-    if (hipMemcpyAsync(hb.d_ids, hb.h_ids, T * sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess)
-      return jl::set_error(JL_ERR_DEVICE, "router ids upload");
+    if (hipError_t e = hipMemcpyAsync(hb.d_ids, hb.h_ids, T * sizeof(int32_t), hipMemcpyHostToDevice, s))
+      return jl::device_error(m, e, "router ids upload");
     if (int rc = jl_forward(m, hb.d_ids, so, n_seqs, mp, M, qt.data(), logits_dev, s)) return rc;
     if (int rc = jl_probs(m, logits_dev, so, n_seqs, mp, M, qt.data(), probs_dev, nullptr, nullptr, nullptr, s))
       return rc;
-    if (hipMemcpyAsync(hb.h_out, probs_dev, M * sizeof(float), hipMemcpyDeviceToHost, s) != hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess)
-      return jl::set_error(JL_ERR_DEVICE, "router probabilities download");
+    hipError_t e = hipMemcpyAsync(hb.h_out, probs_dev, M * sizeof(float), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return jl::device_error(m, e, "router probabilities download");
     std::memcpy(probs, hb.h_out, M * sizeof(float));
     return JL_OK;
   }
@@ -267,7 +267,7 @@ static int jl_route_impl(jl_model *m, int32_t n_questions, const int32_t *prefix
                         const int64_t *option_offsets, const int32_t *question_options, int32_t mask_id,
                         int32_t *pick, float *pick_prob, int32_t *n_final, int32_t *final_idx, float *final_prob,
                         int32_t *calls, int32_t *rounds, void *stream) {
-  if (!m) return jl::set_error(JL_ERR_ARG, "model handle is NULL");
+  if (int rc = jl::model_check(m)) return rc;
   int64_t info[4];
   if (int rc = jl_model_info(m, info, 4)) return rc;
   ModelScorer ms{m, (hipStream_t)stream, (int)info[3], {}};

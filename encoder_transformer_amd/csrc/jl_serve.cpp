@@ -28,6 +28,7 @@ namespace jl {
 
 // One handle's serving resources, made on the first jl_serve that uses it.
 struct ServeState {
+  jl_model *model = nullptr;     // the handle this state belongs to
   int device = 0;
   hipStream_t stream = nullptr;
   hipEvent_t done = nullptr;
@@ -73,6 +74,7 @@ ServeState *serve_state(jl_model *m, int *rc) {
   ServeState *&st = model_serve_state(m);
   if (st) return st;
   ServeState *s = new ServeState();
+  s->model = m;
   s->device = model_device(m);
   s->max_tokens = model_max_tokens(m);
   s->max_markers = model_max_markers(m);
@@ -183,7 +185,7 @@ static int jl_serve_impl(jl_model *const *models, int32_t n_models, int32_t n_re
                         int32_t *argmax, float *maxprob, int32_t *n_batches) {
   if (!models || n_models < 1 || n_models > 16) return serve_fail(JL_ERR_ARG, "need 1..16 model handles");
   for (int32_t k = 0; k < n_models; ++k)
-    if (!models[k]) return serve_fail(JL_ERR_ARG, "model handle is NULL");
+    if (int rc = model_check(models[k])) return rc;
   if (n_requests < 0) return serve_fail(JL_ERR_ARG, "negative request count");
   if (n_requests == 0) {
     if (n_batches) *n_batches = 0;
@@ -235,8 +237,9 @@ static int jl_serve_impl(jl_model *const *models, int32_t n_models, int32_t n_re
   auto retire = [&](ServeState *s) -> int {
     if (!s->busy) return JL_OK;
     s->busy = false;
-    if (hipSetDevice(s->device) != hipSuccess || hipEventSynchronize(s->done) != hipSuccess)
-      return serve_fail(JL_ERR_DEVICE, "serving stream failed");
+    hipError_t e = hipSetDevice(s->device);
+    if (e == hipSuccess) e = hipEventSynchronize(s->done);
+    if (e != hipSuccess) return device_error(s->model, e, "serving stream");
     const float *h_logits = s->h_out, *h_probs = s->h_out + s->max_markers;
     const float *h_answer = s->h_out + 2 * s->max_markers, *h_maxp = h_answer + s->max_seqs;
     int64_t k = 0;
@@ -276,10 +279,13 @@ static int jl_serve_impl(jl_model *const *models, int32_t n_models, int32_t n_re
     const int32_t B = (int32_t)qt.size(), M = (int32_t)mp.size(), T = so.back();
     if (bucketed) bucket_pad(s->h_ids, so, mp, qt);  // fillers after the requests
     const int32_t Tp = so.back();
-    if (hipSetDevice(s->device) != hipSuccess ||
-        hipMemcpyAsync(s->d_ids, s->h_ids, (size_t)Tp * 4, hipMemcpyHostToDevice, s->stream) != hipSuccess) {
-      rc = serve_fail(JL_ERR_DEVICE, "id upload failed");
-      break;
+    {
+      hipError_t e = hipSetDevice(s->device);
+      if (e == hipSuccess) e = hipMemcpyAsync(s->d_ids, s->h_ids, (size_t)Tp * 4, hipMemcpyHostToDevice, s->stream);
+      if (e != hipSuccess) {
+        rc = device_error(m, e, "id upload");
+        break;
+      }
     }
     float *d_logits = s->d_out, *d_probs = s->d_out + s->max_markers;
     float *d_answer = s->d_out + 2 * s->max_markers, *d_maxp = d_answer + s->max_seqs;
@@ -298,17 +304,22 @@ static int jl_serve_impl(jl_model *const *models, int32_t n_models, int32_t n_re
     if ((rc = jl_probs(m, d_logits, so.data(), B, mp.data(), M, qt.data(), d_probs, d_answer, s->d_argmax, d_maxp,
                        s->stream)) != JL_OK)
       break;
-    if (hipMemcpyAsync(s->h_out, s->d_out, (size_t)M * 4, hipMemcpyDeviceToHost, s->stream) != hipSuccess ||
-        hipMemcpyAsync(s->h_out + s->max_markers, d_probs, (size_t)M * 4, hipMemcpyDeviceToHost, s->stream) !=
-            hipSuccess ||
-        hipMemcpyAsync(s->h_out + 2 * s->max_markers, d_answer, (size_t)B * 4, hipMemcpyDeviceToHost, s->stream) !=
-            hipSuccess ||
-        hipMemcpyAsync(s->h_out + 2 * s->max_markers + s->max_seqs, d_maxp, (size_t)B * 4, hipMemcpyDeviceToHost,
-                       s->stream) != hipSuccess ||
-        hipMemcpyAsync(s->h_argmax, s->d_argmax, (size_t)B * 4, hipMemcpyDeviceToHost, s->stream) != hipSuccess ||
-        hipEventRecord(s->done, s->stream) != hipSuccess) {
-      rc = serve_fail(JL_ERR_DEVICE, "result download failed");
-      break;
+    {
+      hipError_t e = hipMemcpyAsync(s->h_out, s->d_out, (size_t)M * 4, hipMemcpyDeviceToHost, s->stream);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(s->h_out + s->max_markers, d_probs, (size_t)M * 4, hipMemcpyDeviceToHost, s->stream);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(s->h_out + 2 * s->max_markers, d_answer, (size_t)B * 4, hipMemcpyDeviceToHost, s->stream);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(s->h_out + 2 * s->max_markers + s->max_seqs, d_maxp, (size_t)B * 4, hipMemcpyDeviceToHost,
+                           s->stream);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(s->h_argmax, s->d_argmax, (size_t)B * 4, hipMemcpyDeviceToHost, s->stream);
+      if (e == hipSuccess) e = hipEventRecord(s->done, s->stream);
+      if (e != hipSuccess) {
+        rc = device_error(m, e, "result download");
+        break;
+      }
     }
     s->busy = true;
   }

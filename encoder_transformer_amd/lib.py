@@ -18,10 +18,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjl.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "jl.h")
 
 FP32, BF16, FP8 = 0, 1, 2  # jl_precision: FP32 products; bf16 operands; bf16 with e4m3 QKV and W_i products
-OK, ERR_ARG, ERR_OPTIONS, ERR_LENGTH, ERR_QTYPE, ERR_FILE, ERR_DEVICE, ERR_OOM, ERR_CAPACITY = (
-    0, -1, -2, -3, -4, -5, -6, -7, -8)
+OK, ERR_ARG, ERR_OPTIONS, ERR_LENGTH, ERR_QTYPE, ERR_FILE, ERR_DEVICE, ERR_OOM, ERR_CAPACITY, ERR_GUARD = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
 STATUS_NAMES = {0: "OK", -1: "ARG", -2: "OPTIONS", -3: "LENGTH", -4: "QTYPE", -5: "FILE",
-                -6: "DEVICE", -7: "OOM", -8: "CAPACITY"}
+                -6: "DEVICE", -7: "OOM", -8: "CAPACITY", -9: "GUARD"}
+DEBUG_SYNC, DEBUG_REVERSE_BLOCKS, DEBUG_SIMULATE_FAULT = 1, 2, 4  # jl_debug_flag
 (K_EMBED, K_QKV, K_ATTN_GLOBAL, K_ATTN_LOCAL, K_OUTPROJ, K_MLP_IN, K_MLP_OUT, K_HEAD_GEMM, K_HEAD_ATTN,
  K_MISC, K_LN, K_LAYER, K_HEAD_LAYER) = range(13)
 KERNEL_CLASS_NAMES = ["embed", "qkv", "attn_global", "attn_local", "outproj", "mlp_in", "mlp_out",
@@ -90,6 +91,10 @@ def load_library():
     L.jl_set_row_block_min_tokens.argtypes = [vp, i64]
     L.jl_model_info.restype = ctypes.c_int
     L.jl_model_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.c_int]
+    L.jl_set_debug.restype = ctypes.c_int
+    L.jl_set_debug.argtypes = [vp, ctypes.c_uint32]
+    L.jl_check_guards.restype = ctypes.c_int
+    L.jl_check_guards.argtypes = [vp]
     L.jl_share.restype = ctypes.c_int
     L.jl_share.argtypes = [vp, i64, i64, ctypes.POINTER(vp)]
     L.jl_serve_plan.restype = ctypes.c_int
@@ -289,11 +294,19 @@ class Model:
             pass
 
     def info(self) -> dict:
-        buf = (ctypes.c_int64 * 8)()
-        _check(self._lib.jl_model_info(self._h, buf, 8))
+        buf = (ctypes.c_int64 * 10)()
+        _check(self._lib.jl_model_info(self._h, buf, 10))
         keys = ["precision", "max_tokens", "max_markers", "device", "weight_bytes", "workspace_bytes",
-                "graph_captures", "graph_replays"]
+                "graph_captures", "graph_replays", "poisoned", "debug"]
         return dict(zip(keys, list(buf)))
+
+    def set_debug(self, flags: int):
+        """jl_set_debug: DEBUG_SYNC | DEBUG_REVERSE_BLOCKS | DEBUG_SIMULATE_FAULT (0: off)."""
+        _check(self._lib.jl_set_debug(self._h, int(flags)))
+
+    def check_guards(self):
+        """jl_check_guards: raise JLError (ERR_GUARD) if a workspace guard band was overwritten."""
+        _check(self._lib.jl_check_guards(self._h))
 
     # -- entry points --------------------------------------------------------
     def forward(self, ids, seq_offsets, mask_positions, qtype, out=None, stream=None):
@@ -314,25 +327,30 @@ class Model:
                                            len(mp), _p(qt), ctypes.c_void_p(out.data_ptr()), self._stream(stream)))
         return out
 
-    def probs(self, logits, seq_offsets, mask_positions, qtype, stream=None):
-        """(probs [M], answer [B], argmax [B] int32, maxprob [B]) as torch tensors on the device."""
+    def probs(self, logits, seq_offsets, mask_positions, qtype, stream=None, out=None):
+        """(probs [M], answer [B], argmax [B] int32, maxprob [B]) as torch tensors on the device
+        (written into `out`, such a 4-tuple, when given)."""
         import torch
         so, mp, qt = self._meta(seq_offsets, mask_positions, qtype)
         dev = f"cuda:{self.device}"
-        probs = torch.empty(len(mp), dtype=torch.float32, device=dev)
-        answer = torch.empty(len(qt), dtype=torch.float32, device=dev)
-        argmax = torch.empty(len(qt), dtype=torch.int32, device=dev)
-        maxprob = torch.empty(len(qt), dtype=torch.float32, device=dev)
+        if out is not None:
+            probs, answer, argmax, maxprob = out
+        else:
+            probs = torch.empty(len(mp), dtype=torch.float32, device=dev)
+            answer = torch.empty(len(qt), dtype=torch.float32, device=dev)
+            argmax = torch.empty(len(qt), dtype=torch.int32, device=dev)
+            maxprob = torch.empty(len(qt), dtype=torch.float32, device=dev)
         ptr = lambda t: ctypes.c_void_p(t.data_ptr())
         _check(self._lib.jl_probs(self._h, ptr(logits), _p(so), len(qt), _p(mp), len(mp), _p(qt), ptr(probs),
                                   ptr(answer), ptr(argmax), ptr(maxprob), self._stream(stream)))
         return probs, answer, argmax, maxprob
 
-    def debug_hidden(self, ids, seq_offsets, mask_positions, qtype, stage: int, stream=None):
+    def debug_hidden(self, ids, seq_offsets, mask_positions, qtype, stage: int, stream=None, out=None):
         import torch
         so, mp, qt = self._meta(seq_offsets, mask_positions, qtype)
         rows = len(mp) if stage == 25 else int(so[-1])
-        out = torch.empty((rows, 384), dtype=torch.float32, device=f"cuda:{self.device}")
+        if out is None:
+            out = torch.empty((rows, 384), dtype=torch.float32, device=f"cuda:{self.device}")
         _check(self._lib.jl_debug_hidden(self._h, ctypes.c_void_p(ids.data_ptr()), _p(so), len(qt), _p(mp),
                                          len(mp), _p(qt), stage, ctypes.c_void_p(out.data_ptr()),
                                          self._stream(stream)))

@@ -24,6 +24,15 @@
  *   - "_dev" pointers are device memory on the handle's device, caller-owned.
  *     All other pointers are host memory, caller-owned, read only during the
  *     call.
+ *   - Device faults: a HIP error that leaves the device unusable (memory
+ *     fault, kernel exception, abort or timeout, uncorrectable ECC error),
+ *     seen by any call on a handle -- at a launch, at the wait for an earlier
+ *     call's metadata slot, or at a synchronization -- returns JL_ERR_DEVICE
+ *     with the HIP error string and marks the handle poisoned: from then on
+ *     every call that enqueues or waits on it returns JL_ERR_DEVICE naming the
+ *     first fault, and only jl_free, jl_model_info and jl_set_debug accept it.
+ *     Faults surface asynchronously (at a later call or the caller's own
+ *     synchronization) unless JL_DEBUG_SYNC is on.
  */
 #ifndef JL_H
 #define JL_H
@@ -61,9 +70,11 @@ enum jl_status {
                         /* increasing from 0                                   */
   JL_ERR_QTYPE = -4,    /* a question type outside {0,1,2}                     */
   JL_ERR_FILE = -5,     /* weight file missing, truncated, bad magic/checksum  */
-  JL_ERR_DEVICE = -6,   /* a HIP runtime error (message holds its string)      */
+  JL_ERR_DEVICE = -6,   /* a HIP runtime error (message holds its string); a   */
+                        /* device fault also poisons the handle (see below)    */
   JL_ERR_OOM = -7,      /* device or pinned-host allocation failed at load     */
-  JL_ERR_CAPACITY = -8  /* more tokens or markers than the handle was sized for */
+  JL_ERR_CAPACITY = -8, /* more tokens or markers than the handle was sized for */
+  JL_ERR_GUARD = -9     /* jl_check_guards: a workspace guard band overwritten  */
 };
 
 enum jl_qtype { JL_CHOICE = 0, JL_SCORE = 1, JL_NOUL = 2 };
@@ -352,10 +363,47 @@ int jl_profile(jl_model *m, int enable, uint32_t class_mask);
  * Synchronizes on the recorded events. */
 int jl_profile_read(jl_model *m, int kernel_class, double *total_ms, int64_t *launches);
 
-/* info[0..n), n <= 8: precision, max_tokens, max_markers, device, device
+/* info[0..n), n <= 10: precision, max_tokens, max_markers, device, device
  * bytes of weights, device bytes of workspace, graphs captured and graph
- * replays so far (jl_set_graph_cache). */
+ * replays so far (jl_set_graph_cache), 1 if the handle is poisoned, the
+ * debugging flags (jl_set_debug). */
 int jl_model_info(const jl_model *m, int64_t *info, int n);
+
+/*
+ * Debugging switches of a handle (replacing its previous flags; 0 = off).
+ *   JL_DEBUG_SYNC            after every kernel launch, wait for the stream
+ *                            and check hipGetLastError, so that an error or a
+ *                            device fault is reported by the call and kernel
+ *                            class that caused it; graph replay is off.  Also
+ *                            set at load when the environment variable
+ *                            JL_DEBUG_SYNC is set and not "0".
+ *   JL_DEBUG_REVERSE_BLOCKS  every kernel whose work-groups own tiles, row
+ *                            blocks, attention items or heads (the GEMMs, the
+ *                            row-block kernels, attention, the scorer) takes
+ *                            them in reversed order.  Each work-group computes
+ *                            its outputs alone and the scorer adds its
+ *                            partial sums in a fixed order, so the results
+ *                            are the same bit for bit; a difference exposes a
+ *                            race between work-groups.  Graph replay is off.
+ *   JL_DEBUG_SIMULATE_FAULT  the next call that enqueues work reports a
+ *                            memory fault after its launches, as a real one
+ *                            would be reported (the work itself runs
+ *                            normally), poisoning the handle; cleared when
+ *                            used.  For testing callers' fault handling.
+ * Errors: JL_ERR_ARG (NULL handle, unknown flag).
+ */
+enum jl_debug_flag { JL_DEBUG_SYNC = 1, JL_DEBUG_REVERSE_BLOCKS = 2, JL_DEBUG_SIMULATE_FAULT = 4 };
+int jl_set_debug(jl_model *m, uint32_t flags);
+
+/*
+ * Workspace guard bands: every buffer of the handle's workspace (activations,
+ * marker rows, scorer partials and counters, metadata blocks) is followed by
+ * 256 bytes of 0xA5, written at load and never by a kernel.  Synchronizes the
+ * device, reads the bands back and returns JL_OK, or JL_ERR_GUARD naming the
+ * first buffer whose band was overwritten (a write past its end).  Errors:
+ * JL_ERR_ARG, JL_ERR_DEVICE.
+ */
+int jl_check_guards(jl_model *m);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *jl_last_error(void);

@@ -83,7 +83,30 @@ def test_null_and_negative_arguments(L):
     assert L.jl_forward(None, None, p(so), 1, p(mp), 2, p(qt), None, None) == lib.ERR_ARG
     assert L.jl_probs(None, None, p(so), 1, p(mp), 2, p(qt), None, None, None, None, None) == lib.ERR_ARG
     assert L.jl_debug_hidden(None, None, p(so), 1, p(mp), 2, p(qt), 0, None, None) == lib.ERR_ARG
+    assert L.jl_set_debug(None, lib.DEBUG_SYNC) == lib.ERR_ARG
+    assert L.jl_check_guards(None) == lib.ERR_ARG
     L.jl_free(None)
+
+
+def _header_enum(name):
+    """{member: value} of `enum name { ... }` in include/jl.h."""
+    import re
+    with open(lib.HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    body = re.search(r"enum\s+" + name + r"\s*\{(.*?)\}", text, re.S).group(1)
+    return {k: int(v) for k, v in re.findall(r"(JL_\w+)\s*=\s*(-?\d+)", body)}
+
+
+def test_binding_constants_match_the_header():
+    status = _header_enum("jl_status")
+    assert {k[len("JL_"):]: v for k, v in status.items()} == {
+        ("OK" if v == 0 else "ERR_" + lib.STATUS_NAMES[v]): v for v in lib.STATUS_NAMES}
+    for k, v in status.items():
+        assert getattr(lib, k[len("JL_"):]) == v, k
+    debug = _header_enum("jl_debug_flag")
+    assert debug == {"JL_DEBUG_SYNC": lib.DEBUG_SYNC, "JL_DEBUG_REVERSE_BLOCKS": lib.DEBUG_REVERSE_BLOCKS,
+                     "JL_DEBUG_SIMULATE_FAULT": lib.DEBUG_SIMULATE_FAULT}
+    assert _header_enum("jl_precision") == {"JL_FP32": lib.FP32, "JL_BF16": lib.BF16, "JL_FP8": lib.FP8}
 
 
 def load_code(L, path, precision=lib.BF16, max_tokens=1024, max_markers=64):
