@@ -75,8 +75,8 @@ def test_reversed_block_order_is_bitwise_identical(models, prec, sched):
     m = models[prec]
     _schedule(m, sched)
     # ragged tails (9, 1 and 63 rows past a 64-row tile) and the 16 x 1,024
-    # configuration (many tiles per launch, all four window/global forms)
-    for batch in (stage_batch(), synth.make_batch(1)):
+    # configuration (many tiles and work items per launch)
+    for batch in (stage_batch(), synth.make_batch(2)):
         m.set_debug(0)
         ref = _run(m, batch)
         m.set_debug(lib.DEBUG_REVERSE_BLOCKS)
