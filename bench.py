@@ -114,8 +114,10 @@ def time_workload(model, batch, steps, warmup, profile_class=None, sample=True):
     # 10th).
     # sample=False times plain graph replays only (the latency figures).
     model.profile(1, 0)  # clears the warm-up records
-    if not sample:
-        model.profile(0, 0)  # profiling off: every step replays its graph
+    model.profile(0, 0)
+    step()  # one more warm-up step with the timer off: captures this shape's graph
+    if sample:
+        model.profile(1, 0)
     torch.cuda.synchronize()
     # Python's cyclic garbage collector is paused in the timed region (as
     # timeit does): a full collection of this interpreter's heap stalls the
@@ -283,7 +285,7 @@ def main():
         calibration_copy(args.calibration_copy_mib)
         print(json.dumps({"metric": "ms per call at 1x1024", "value": round(1e3 * t1 / args.steps, 4), "unit": "ms",
                           "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
-                          "calls": 1 + max(1, args.warmup) + args.steps}))
+                          "calls": 2 + max(1, args.warmup) + args.steps}))
         return
 
     if args.only:
