@@ -352,7 +352,9 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
   }
 
   // 6. next layer: u' = LayerNorm_attn(next)(X) -> sA; its QKV (encoder
-  //    layers rotate q and k; the head's first layer adds the bias)
+  //    layers rotate q and k; the head's first layer adds the bias).  The
+  //    GEGLU buffers are free now: each wave stages its q/k/v stores through
+  //    8 KB of them.
   row_stats(X, sRed, lane, wave, mean, rstd);
   if constexpr (kF8 && !kHeadNext) {
     PipeO8 po8;
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
     write_ln<kHeadNext>(X, a.attn_norm_next, a.attn_shift_next, mean, rstd, sA, lane, wave);
     __syncthreads();
     qkv_phase<kHeadNext>(a.Wqkv_next, a.qkv_bias_next, a.qkv_out, sCos, sSin, sA, po, pi, p2, H, X, lane, wave,
-                         row0, T);
+                         row0, T, (wave < NW / 2 ? sH0 : sH1) + (wave & 3) * 4096);
   }
 }
 

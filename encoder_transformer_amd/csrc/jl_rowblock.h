@@ -310,6 +310,64 @@ DI void rope_store(const f32x4 (&H)[4][4], const float *sCos, const float *sSin,
   }
 }
 
+// rope_store<4> through a per-wave LDS tile (64 rows x 64 columns, 16-byte
+// chunks XOR-swizzled by row so that the 16-byte reads are free of bank
+// conflicts): each global store instruction then
+// writes 8 whole 128-byte rows of the head instead of 16 rows x 32 bytes.
+// The same values reach the same addresses; only the store pattern differs.
+DI void rope_store_staged(const f32x4 (&H)[4][4], const float *sCos, const float *sSin, bf16 *qkv_out, int head_col,
+                          bf16 *sStage, int lane, int row0, int T) {
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int jp = 0; jp < 2; ++jp) {
+    const int d0 = 16 * jp + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = 16 * i + r16, sw = rl & 7;
+      const f32x4 cs = *reinterpret_cast<const f32x4 *>(sCos + rl * 32 + d0);
+      const f32x4 sn = *reinterpret_cast<const f32x4 *>(sSin + rl * 32 + d0);
+      bf16x4 lo, hi;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x0 = H[i][jp][r], x1 = H[i][jp + 2][r];
+        lo[r] = (bf16)(x0 * cs[r] - x1 * sn[r]);
+        hi[r] = (bf16)(x1 * cs[r] + x0 * sn[r]);
+      }
+      *reinterpret_cast<bf16x4 *>(sStage + rl * 64 + (((d0 >> 3) ^ sw) << 3) + (d0 & 7)) = lo;
+      *reinterpret_cast<bf16x4 *>(sStage + rl * 64 + ((((d0 + 32) >> 3) ^ sw) << 3) + (d0 & 7)) = hi;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int rl = 8 * k + (lane >> 3), c = lane & 7, row = row0 + rl;
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(sStage + rl * 64 + ((c ^ (rl & 7)) << 3));
+    if (row < T) *reinterpret_cast<bf16x8 *>(qkv_out + (size_t)row * (3 * kWidth) + head_col + 8 * c) = v;
+  }
+}
+
+// v_store through a per-wave LDS tile (64 rows x 48 columns, rows 112 bytes
+// apart): each global store instruction then writes 96-byte row segments
+// instead of 32-byte ones.
+DI void v_store_staged(const f32x4 (&V)[4][3], bf16 *qkv_out, bf16 *sStage, int lane, int wave, int row0, int T) {
+  constexpr int S = 56;  // tile row stride (elements)
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      bf16x4 t;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] = (bf16)V[i][j][r];
+      *reinterpret_cast<bf16x4 *>(sStage + (16 * i + r16) * S + 16 * j + 4 * g) = t;
+    }
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const int q = 64 * k + lane, rl = q / 6, c = q - 6 * rl, row = row0 + rl;
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(sStage + rl * S + 8 * c);
+    if (row < T) *reinterpret_cast<bf16x8 *>(qkv_out + (size_t)row * (3 * kWidth) + 2 * kWidth + 48 * wave + 8 * c) = v;
+  }
+}
+
 // v accumulators (wave w: columns 48 w .. 48 w + 47) to bf16.
 DI void v_store(const f32x4 (&V)[4][3], bf16 *qkv_out, int lane, int wave, int row0, int T) {
   const int r16 = lane & 15, g = lane >> 4;
@@ -358,10 +416,12 @@ DI void bias_store(const f32x4 (&H)[4][NTA], const int (&ng)[NT], const float *b
 // partner's matrix-core work.  kBias: add the projection bias and store
 // (the head's in-projection); else rotate q and k (RoPE rows of this block in
 // sCos / sSin) and store.  Every pipe, H and X are free on entry.
+// sStage: this wave's 8 KB of free LDS, through which the encoder's whole-head
+// q/k and v stores are staged (nullptr: stored straight from registers).
 template <bool kBias>
 DI void qkv_phase(const bf16 *Wqkv, const float *bias, bf16 *qkv_out, const float *sCos, const float *sSin,
                   const bf16 *sA, PipeO &po, PipeI &pi, Pipe2 &p2, f32x4 (&H)[4][4], f32x4 (&X)[4][3], int lane,
-                  int wave, int row0, int T) {
+                  int wave, int row0, int T, bf16 *sStage = nullptr) {
   const int half_col = 512 + 64 * (wave >> 1), half = wave & 1;
   int ngw[4], ngh[2], ngv[3];
   ng_qk_whole(ngw, wave);
@@ -373,6 +433,7 @@ DI void qkv_phase(const bf16 *Wqkv, const float *bias, bf16 *qkv_out, const floa
     zero_cols<4>(H);
     wp_run<KSD>(H, pi, sA, lane, [&] { start_qk_half(p2, Wqkv, lane, wave); });
     if constexpr (kBias) bias_store<4>(H, ngw, bias, qkv_out, QS, lane, row0, T);
+    else if (sStage) rope_store_staged(H, sCos, sSin, qkv_out, 64 * wave, sStage, lane, row0, T);
     else rope_store<4>(H, sCos, sSin, qkv_out, 64 * wave, 0, lane, row0, T);
     zero_cols<2>(H);
     wp_run<KSD>(H, p2, sA, lane, [&] { start_v(po, Wqkv, lane, wave); });
@@ -381,6 +442,7 @@ DI void qkv_phase(const bf16 *Wqkv, const float *bias, bf16 *qkv_out, const floa
     zero(X);
     wp_run<KSD>(X, po, sA, lane, NoNext());
     if constexpr (kBias) bias_store<3>(X, ngv, bias, qkv_out, QS, lane, row0, T);
+    else if (sStage) v_store_staged(X, qkv_out, sStage, lane, wave, row0, T);
     else v_store(X, qkv_out, lane, wave, row0, T);
   } else {
     start_qk_half(p2, Wqkv, lane, wave);
@@ -391,10 +453,12 @@ DI void qkv_phase(const bf16 *Wqkv, const float *bias, bf16 *qkv_out, const floa
     zero(X);
     wp_run<KSD>(X, po, sA, lane, [&] { start_qk_whole(pi, Wqkv, lane, wave); });
     if constexpr (kBias) bias_store<3>(X, ngv, bias, qkv_out, QS, lane, row0, T);
+    else if (sStage) v_store_staged(X, qkv_out, sStage, lane, wave, row0, T);
     else v_store(X, qkv_out, lane, wave, row0, T);
     zero_cols<4>(H);
     wp_run<KSD>(H, pi, sA, lane, NoNext());
     if constexpr (kBias) bias_store<4>(H, ngw, bias, qkv_out, QS, lane, row0, T);
+    else if (sStage) rope_store_staged(H, sCos, sSin, qkv_out, 64 * wave, sStage, lane, row0, T);
     else rope_store<4>(H, sCos, sSin, qkv_out, 64 * wave, 0, lane, row0, T);
   }
 }
