@@ -1083,17 +1083,49 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
     }
   }
+  // Output rows o / l.  bf16: each wave's 16 NSUB x 64 outputs go through its
+  // own part of the K buffers (free after the last tile's barrier), 16-byte
+  // chunks XOR-swizzled by row so that the reads are free of bank conflicts,
+  // and leave as whole 128-byte rows of the head: 2 NSUB store instructions
+  // per wave instead of 4 NSUB of 16 rows x 32 bytes.  FP32: straight from
+  // the accumulators.
+  if constexpr (sizeof(T) == 2) {
+    T *st = &sK[0][0] + wave * (16 * NSUB * kHeadDim);
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const float lt = lsum[s][0];  // every row of the ones product holds the query's sum
-    const int qi = wave * QW + 16 * s + ql;
-    if (qi < w.n_q) {
+    for (int s = 0; s < NSUB; ++s) {
+      const float lt = lsum[s][0];  // every row of the ones product holds the query's sum
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-      T *op = (T *)a.o + (size_t)(w.q_row0 + qi) * a.o_stride + h * kHeadDim + 4 * g;
+      const int rl = 16 * s + ql, sw = ql & 7;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
+      for (int ds = 0; ds < 4; ++ds) {
+        typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) op[ds * 16 + r] = to_elem<T>(o[s][ds][r] * inv);
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)(o[s][ds][r] * inv);
+        const int d0 = ds * 16 + 4 * g;
+        *reinterpret_cast<bf16x4 *>(st + rl * kHeadDim + (((d0 >> 3) ^ sw) << 3) + (d0 & 7)) = v;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2 * NSUB; ++kk) {
+      const int rl = 8 * kk + (lane >> 3), c = lane & 7, qi = wave * QW + rl;
+      const bf16x8 v = *reinterpret_cast<const bf16x8 *>(st + rl * kHeadDim + ((c ^ (rl & 7)) << 3));
+      if (qi < w.n_q)
+        *reinterpret_cast<bf16x8 *>((T *)a.o + (size_t)(w.q_row0 + qi) * a.o_stride + h * kHeadDim + 8 * c) = v;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const float lt = lsum[s][0];
+      const int qi = wave * QW + 16 * s + ql;
+      if (qi < w.n_q) {
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        T *op = (T *)a.o + (size_t)(w.q_row0 + qi) * a.o_stride + h * kHeadDim + 4 * g;
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) op[ds * 16 + r] = to_elem<T>(o[s][ds][r] * inv);
+      }
     }
   }
 }
