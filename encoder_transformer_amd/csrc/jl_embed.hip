@@ -18,6 +18,7 @@ __global__ __launch_bounds__(512, 1) void embed_qkv_kernel(EmbedArgs a) {
   __shared__ __attribute__((aligned(16))) float sSin[RB * 32];   // 8 KB
   __shared__ float sRed[2][NW][RB];
   __shared__ int sPos[RB];
+  __shared__ __attribute__((aligned(16))) bf16 sStage[NW * 4096];  // 64 KB: 8 KB per wave for the q/k/v stores
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int row0 = (a.rev ? gridDim.x - 1 - blockIdx.x : blockIdx.x) * RB;
@@ -77,7 +78,8 @@ __global__ __launch_bounds__(512, 1) void embed_qkv_kernel(EmbedArgs a) {
   PipeI pi;
   Pipe2 p2;
   f32x4 H[4][4];
-  qkv_phase<false>(a.Wqkv, nullptr, a.qkv_out, sCos, sSin, sA, po, pi, p2, H, X, lane, wave, row0, T);
+  qkv_phase<false>(a.Wqkv, nullptr, a.qkv_out, sCos, sSin, sA, po, pi, p2, H, X, lane, wave, row0, T,
+                   sStage + wave * 4096);
 }
 
 }  // namespace
