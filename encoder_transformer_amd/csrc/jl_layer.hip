@@ -361,7 +361,7 @@ __global__ __launch_bounds__(512, 1) void layer_kernel(LayerArgs a) {
     write_ln8<false>(X, a.attn_norm_next, nullptr, mean, rstd, sAmax, sA8, srow, lane, wave);
     __syncthreads();
     qkv_phase8(a.Wqkv8_next, a.sqkv_next, a.qkv_out, sCos, sSin, sA8, srow, po8, pa8, pb8, H, X, lane, wave, row0,
-               T);
+               T, (wave < NW / 2 ? sH0 : sH1) + (wave & 3) * 4096);
   } else {
     write_ln<kHeadNext>(X, a.attn_norm_next, a.attn_shift_next, mean, rstd, sA, lane, wave);
     __syncthreads();

@@ -345,6 +345,38 @@ DI void rope_store_staged(const f32x4 (&H)[4][4], const float *sCos, const float
   }
 }
 
+// The e4m3 QKV phase computes a whole head in two rotation halves: each
+// half's rotated q/k values (columns 16 hf + (0..15) and + 32) go into the
+// wave's swizzled head tile as rope_store_staged lays it out, and
+// head_tile_store writes the tile after the second half.
+DI void rope_stage_half(const f32x4 (&H)[4][4], const float *sCos, const float *sSin, int hf, bf16 *sStage,
+                        int lane) {
+  const int r16 = lane & 15, g = lane >> 4, d0 = 16 * hf + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = 16 * i + r16, sw = rl & 7;
+    const f32x4 cs = *reinterpret_cast<const f32x4 *>(sCos + rl * 32 + d0);
+    const f32x4 sn = *reinterpret_cast<const f32x4 *>(sSin + rl * 32 + d0);
+    bf16x4 lo, hi;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = H[i][0][r], x1 = H[i][1][r];
+      lo[r] = (bf16)(x0 * cs[r] - x1 * sn[r]);
+      hi[r] = (bf16)(x1 * cs[r] + x0 * sn[r]);
+    }
+    *reinterpret_cast<bf16x4 *>(sStage + rl * 64 + (((d0 >> 3) ^ sw) << 3) + (d0 & 7)) = lo;
+    *reinterpret_cast<bf16x4 *>(sStage + rl * 64 + ((((d0 + 32) >> 3) ^ sw) << 3) + (d0 & 7)) = hi;
+  }
+}
+DI void head_tile_store(const bf16 *sStage, bf16 *qkv_out, int head_col, int lane, int row0, int T) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int rl = 8 * k + (lane >> 3), c = lane & 7, row = row0 + rl;
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(sStage + rl * 64 + ((c ^ (rl & 7)) << 3));
+    if (row < T) *reinterpret_cast<bf16x8 *>(qkv_out + (size_t)row * (3 * kWidth) + head_col + 8 * c) = v;
+  }
+}
+
 // v_store through a per-wave LDS tile (64 rows x 48 columns, rows 112 bytes
 // apart): each global store instruction then writes 96-byte row segments
 // instead of 32-byte ones.
@@ -648,7 +680,7 @@ using Pipe28 = WPipe8<2, 1>;
 // accumulators live; then RoPE on q and k and the stores.
 DI void qkv_phase8(const uint8_t *Wqkv8, const float *sqkv, bf16 *qkv_out, const float *sCos, const float *sSin,
                    const uint8_t *sA8, const float (&srow)[4], PipeO8 &po, Pipe28 &pa, Pipe28 &pb, f32x4 (&H)[4][4],
-                   f32x4 (&X)[4][3], int lane, int wave, int row0, int T) {
+                   f32x4 (&X)[4][3], int lane, int wave, int row0, int T, bf16 *sStage) {
   const int half_col = 512 + 64 * (wave >> 1), half = wave & 1;
   const int ngw0[2] = {4 * wave, 4 * wave + 2}, ngw1[2] = {4 * wave + 1, 4 * wave + 3};
   int ngh[2], ngv[3];
@@ -656,13 +688,20 @@ DI void qkv_phase8(const uint8_t *Wqkv8, const float *sqkv, bf16 *qkv_out, const
   ng_v(ngv, wave);
   // the next product's pipe starts once this one's products are issued, its
   // loads in flight during the epilogue
-  auto qk_half = [&](Pipe28 &p, const int (&ng)[2], int col, int hf, auto nxt) {
+  // whole: a rotation half of the wave's own head, staged (the second half
+  // then writes the head's rows); else half of a shared head, stored directly
+  auto qk_half = [&](Pipe28 &p, const int (&ng)[2], int col, int hf, bool whole, auto nxt) {
     zero_cols<2>(H);
     wp8_run(H, p, sA8, lane, NoNext());
     scale8<2>(H, ng, sqkv, srow, lane);
     pin_acc<2>(H);
     nxt();
-    rope_store<2>(H, sCos, sSin, qkv_out, col, hf, lane, row0, T);
+    if (whole) {
+      rope_stage_half(H, sCos, sSin, hf, sStage, lane);
+      if (hf == 1) head_tile_store(sStage, qkv_out, col, lane, row0, T);
+    } else {
+      rope_store<2>(H, sCos, sSin, qkv_out, col, hf, lane, row0, T);
+    }
   };
   auto v_part = [&](auto nxt) {
     zero(X);
@@ -670,20 +709,20 @@ DI void qkv_phase8(const uint8_t *Wqkv8, const float *sqkv, bf16 *qkv_out, const
     scale8<3>(X, ngv, sqkv, srow, lane);
     pin_acc<3>(X);
     nxt();
-    v_store(X, qkv_out, lane, wave, row0, T);
+    v_store_staged(X, qkv_out, sStage, lane, wave, row0, T);
   };
   if (wave < NW / 2) {
     wp8_start(pa, Wqkv8, ngw0, lane);
-    qk_half(pa, ngw0, 64 * wave, 0, [&] { wp8_start(pb, Wqkv8, ngw1, lane); });
-    qk_half(pb, ngw1, 64 * wave, 1, [&] { wp8_start(pa, Wqkv8, ngh, lane); });
-    qk_half(pa, ngh, half_col, half, [&] { wp8_start(po, Wqkv8, ngv, lane); });
+    qk_half(pa, ngw0, 64 * wave, 0, true, [&] { wp8_start(pb, Wqkv8, ngw1, lane); });
+    qk_half(pb, ngw1, 64 * wave, 1, true, [&] { wp8_start(pa, Wqkv8, ngh, lane); });
+    qk_half(pa, ngh, half_col, half, false, [&] { wp8_start(po, Wqkv8, ngv, lane); });
     v_part(NoNext());
   } else {
     wp8_start(pa, Wqkv8, ngh, lane);
-    qk_half(pa, ngh, half_col, half, [&] { wp8_start(po, Wqkv8, ngv, lane); });
+    qk_half(pa, ngh, half_col, half, false, [&] { wp8_start(po, Wqkv8, ngv, lane); });
     v_part([&] { wp8_start(pb, Wqkv8, ngw0, lane); });
-    qk_half(pb, ngw0, 64 * wave, 0, [&] { wp8_start(pa, Wqkv8, ngw1, lane); });
-    qk_half(pa, ngw1, 64 * wave, 1, NoNext());
+    qk_half(pb, ngw0, 64 * wave, 0, true, [&] { wp8_start(pa, Wqkv8, ngw1, lane); });
+    qk_half(pa, ngw1, 64 * wave, 1, true, NoNext());
   }
 }
 
