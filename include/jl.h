@@ -212,8 +212,11 @@ int jl_set_row_block_min_tokens(jl_model *m, int64_t min_tokens);
  * least recently used evicted.  Each call still uploads its own batch
  * metadata first (to one graph-owned device buffer, ordered on the stream),
  * so any batch of a cached shape is computed exactly as eagerly.  Calls on
- * the NULL stream, and calls while the per-kernel timer is on, run eagerly.
- * 0 (the default) turns graphs off and releases the cached graphs; at most 64.
+ * the NULL stream, calls while the per-kernel timer is on, and calls with a
+ * debugging flag set (jl_set_debug) run eagerly.  0 (the default) turns
+ * graphs off and releases the cached graphs; at most 64.  The launch count is
+ * the cost "julia1 - Rust runtime for Julia-1" (Why it is faster) names for
+ * its CUDA path: about 200 launches per forward with no interpreter between.
  */
 int jl_set_graph_cache(jl_model *m, int max_graphs);
 
@@ -279,7 +282,8 @@ int jl_route_with_scorer(jl_score_fn score, void *user, int64_t max_tokens, int6
  * A second handle over the weights of `src`, with a workspace of its own
  * (max_tokens, max_markers), metadata ring, graph cache and timer.  Handles
  * that share weights may run jl_forward / jl_probs concurrently on different
- * streams; the weights stay allocated until the last handle sharing them is
+ * streams, as the concurrent requests of "Julia-1 MLX" (Performance) each run
+ * on a stream of their own; the weights stay allocated until the last handle sharing them is
  * freed with jl_free.  Errors: JL_ERR_ARG (NULL or sizes out of range),
  * JL_ERR_OOM / JL_ERR_DEVICE.
  */
@@ -332,7 +336,9 @@ int jl_serve(jl_model *const *models, int32_t n_models, int32_t n_requests, cons
              const int32_t *qtype, int64_t max_batch_tokens, float *logits, float *probs, float *answer,
              int32_t *argmax, float *maxprob, int32_t *n_batches);
 
-/* Kernel classes reported by the per-kernel timer. */
+/* Kernel classes reported by the per-kernel timer: the per-operation timings
+ * that "julia1 - Rust runtime for Julia-1" prints with JULIA_PROFILE=1
+ * (Layout, after the list of what is not ported), taken on the device. */
 enum jl_kernel_class {
   JL_K_EMBED = 0,      /* embedding gather + LayerNorm (row-block path: also   */
                        /* the first layer's QKV)                                */
