@@ -177,7 +177,8 @@ def test_serve_graph_buckets_against_the_oracle():
     caps2 = sum(i["graph_captures"] for i in info2)
     reps2 = sum(i["graph_replays"] for i in info2) - sum(i["graph_replays"] for i in info1)
     print("micro-batches", first.n_batches, "captured", caps1, "then", caps2, "replays in the second pass", reps2)
-    assert caps1 >= 1 and caps2 == caps1 and reps2 == second.n_batches
+    if info1[0]["debug"] == 0:  # debugging switches (JL_DEBUG_SYNC at load) turn graph replay off
+        assert caps1 >= 1 and caps2 == caps1 and reps2 == second.n_batches
     assert np.array_equal(first.logits, second.logits) and np.array_equal(first.probs, second.probs)
     bound = LOGIT_TOL[("wide", "bf16")]
     worst = {"logit": 0.0, "prob": 0.0}
